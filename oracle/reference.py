@@ -1,0 +1,349 @@
+"""Float64 CPU oracle of causal sparse attention — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg
+may import this module.  It shares no code with the HIP library and imports nothing
+from it.
+
+Every function is the plain definition of what the method computes, written out in
+float64 numpy, with no blocking, fusion or reordering beyond that definition.  The
+attention functions evaluate *dense* causal attention over all earlier positions and
+then apply the explicit selected-key mask (unselected logits are set to -inf before an
+ordinary max-subtracted softmax), so selection and attention are checked separately.
+
+Sources (web pages; the text is Spanish, cited by title and section):
+
+* [IC] "IndexCache ... inferencia 82% más rápida" (larebelion.com, from VentureBeat),
+  body paragraphs 2-4: a lightweight indexer scores every earlier token and the query
+  attends only to the selected subset (DSA); F layers compute and cache the selected
+  indices, S layers reuse those of the nearest preceding F layer.
+* [HS2] "Xiaomi presenta HySparse2 ..." (diariobitcoin.com), sections "Dos niveles para
+  compartir la caché" and "Más precisión con menos memoria": token-level (not block)
+  selection, and the most recent tokens are forced into the selected set instead of a
+  separate sliding-window branch (128 recent + up to 1,024 global).
+* [SLM] "SpatialLM-Mini aceleró el entrenamiento con un contexto de 16K en 2,47 veces en
+  una RTX 3050" (news.hamidun.com), section "Cómo eligen los tokens a quién escuchar":
+  a fixed list of allowed positions — the token itself, near predecessors and positions
+  at distances 1, 2, 4, 8, ... — never future ones; weights grow as the distance between
+  learned 3-D query and key coordinates shrinks, adjusted by further learned parameters.
+* [NSA] "Native Sparse Attention: Revolucionando el Procesamiento de Contexto Extenso ..."
+  (ctol-es.com), sections "Puntos Clave" and "Análisis Profundo": coarse compression,
+  blockwise fine-grained selection, sliding window; GQA group-centric loading with a
+  shared KV fetch (one selection per KV head, shared by its query heads).
+* [STAR] "NVIDIA AI Research presenta Star Attention ..." (7minutos.es), third body
+  paragraph: partial attentions computed separately are combined with a distributed
+  softmax.  The oracle has no split; its result is what any such combination must equal.
+
+The pages give no formulas.  The concrete arithmetic of each workload (indexer score
+Σ_h w_h·ReLU(qi_h[t]·ki[s]), window sizes, the power-of-two offsets, the distance logit
+-τ‖c_q-c_k‖² + b_h, block size 64 and top-16 blocks) is the workload definition that
+these pages' methods are instantiated with; each reading of an open point is marked
+"Reading:" where it is used.
+
+Pins: every function is checked by the CPU tests against closed forms, library special
+cases, brute force on tiny inputs and hand-worked fixtures (tests/golden/); none of the
+functions here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------------------
+# Indexer  [IC] body paragraphs 2-3 (the DSA indexer scores every earlier token)
+# ----------------------------------------------------------------------------------------
+
+def indexer_scores_row(qi, ki, w, b: int, t: int) -> np.ndarray:
+    """Scores of query row ``t`` against keys s = 0..t (float64, length t+1).
+
+    score(t, s) = Σ_h w[h] · max(0, qi[b,t,h,:] · ki[b,s,:])
+
+    Reading: the indexer key ``ki`` is shared by the indexer heads, ``w`` is one
+    constant per head shared by all rows, and there is no scale factor.
+    """
+    q = _f64(qi[b, t])                      # [H_I, D_I]
+    k = _f64(ki[b, : t + 1])                # [t+1, D_I]
+    dots = np.matmul(q, k.T)                # [H_I, t+1]: one dot product per head and key
+    relu = np.maximum(dots, 0.0)
+    return np.matmul(_f64(w), relu)         # Σ_h w_h · ReLU(.)
+
+
+def indexer_scores(qi, ki, w, rows=None):
+    """All requested rows as a dict ``{(b, t): row}``; rows default to every (b, t)."""
+    B, T = qi.shape[0], qi.shape[1]
+    rows = range(T) if rows is None else rows
+    return {(b, t): indexer_scores_row(qi, ki, w, b, t) for b in range(B) for t in rows}
+
+
+# ----------------------------------------------------------------------------------------
+# Top-k selection  [IC] paragraph 2 (select a small subset), [HS2] "Más precisión con
+# menos memoria" (individual tokens, not blocks)
+# ----------------------------------------------------------------------------------------
+
+def topk_select_row(scores_row, k: int) -> np.ndarray:
+    """The min(k, n) positions with the largest scores, ties to the lower position.
+
+    Returned ascending and padded with -1 to length k (int32).  The order used is the
+    total order (score descending, position ascending); -0.0 equals +0.0.
+    Reading: every earlier position is a candidate, the window included (the window is
+    added afterwards as a set union).
+    """
+    s = _f64(scores_row)
+    n = s.shape[0]
+    out = np.full(k, -1, dtype=np.int32)
+    if k <= 0:
+        return out
+    if n <= k:
+        out[:n] = np.arange(n, dtype=np.int32)
+        return out
+    kth = np.partition(s, n - k)[n - k]                 # the k-th largest value
+    above = np.flatnonzero(s > kth)
+    need = k - above.shape[0]
+    ties = np.flatnonzero(s == kth)[:need]              # lowest positions among the ties
+    sel = np.sort(np.concatenate([above, ties]))
+    out[:] = sel.astype(np.int32)
+    return out
+
+
+def topk_select(scores: dict, k: int, B: int, T: int, rows=None) -> np.ndarray:
+    """``idx[B, T, k]`` int32 for the requested rows (others stay -1)."""
+    rows = range(T) if rows is None else rows
+    idx = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in rows:
+            idx[b, t] = topk_select_row(scores[(b, t)], k)
+    return idx
+
+
+def topk_boundary(scores_row, k: int):
+    """(a, b): the k-th and (k+1)-th largest scores of a row with more than k entries,
+    else None.  Used to decide which rows are within rounding distance of a tie."""
+    s = _f64(scores_row)
+    n = s.shape[0]
+    if n <= k:
+        return None
+    srt = np.sort(s)[::-1]
+    return float(srt[k - 1]), float(srt[k])
+
+
+# ----------------------------------------------------------------------------------------
+# Sparse attention over the selected set  [IC] paragraph 2, [HS2] "Dos niveles ..."
+# (recent tokens forced into the set), [NSA] "Análisis Profundo" (shared KV per group)
+# ----------------------------------------------------------------------------------------
+
+def selected_mask_row(t: int, idx_row, window: int) -> np.ndarray:
+    """Boolean mask over s = 0..t: s is attended iff s is a listed index in [0, t]
+    or s lies in the window {t-window+1, ..., t}.  Each key counts once (a set)."""
+    m = np.zeros(t + 1, dtype=bool)
+    ids = np.asarray(idx_row, dtype=np.int64)
+    ids = ids[(ids >= 0) & (ids <= t)]
+    m[ids] = True
+    if window > 0:
+        m[max(0, t - window + 1): t + 1] = True
+    return m
+
+
+def _masked_softmax_attend(logits, mask, vals):
+    """Dense logits [H, n] → masked softmax → (out [H, D], lse [H]).
+    An empty mask gives out = 0 and lse = -inf."""
+    H = logits.shape[0]
+    if not mask.any():
+        return np.zeros((H, vals.shape[-1])), np.full(H, NEG_INF)
+    lg = np.where(mask[None, :], logits, NEG_INF)
+    mx = lg.max(axis=1, keepdims=True)
+    p = np.exp(lg - mx)                                  # exp(-inf) = 0 off the mask
+    l = p.sum(axis=1, keepdims=True)
+    out = np.matmul(p, vals) / l if vals.ndim == 2 else np.einsum("hs,hsd->hd", p, vals) / l
+    lse = (mx + np.log(l))[:, 0]
+    return out, lse
+
+
+def sparse_attn(q, k, v, idx, window: int, scale: float, rows=None):
+    """O[b,t,h,:] = Σ_{s∈S_t} softmax_s(scale·q[b,t,h]·k[b,s,g]) · v[b,s,g], g = h // (Hq/Hkv).
+
+    S_t = {s ∈ idx[b,t] : 0 ≤ s ≤ t} ∪ {max(0, t-window+1), ..., t}.  Returns
+    (O [B,R,Hq,D], LSE [B,Hq,R]) for the R requested rows (natural-log LSE).
+    Reading: one selection per query row, shared by all heads of every KV group.
+    """
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    rows = list(range(T)) if rows is None else list(rows)
+    O = np.zeros((B, len(rows), Hq, D))
+    LSE = np.zeros((B, Hq, len(rows)))
+    for b in range(B):
+        kb, vb = _f64(k[b]), _f64(v[b])
+        for r, t in enumerate(rows):
+            mask = selected_mask_row(t, idx[b, t], window)
+            for g in range(Hkv):
+                qh = _f64(q[b, t, g * G:(g + 1) * G])                 # [G, D]
+                logits = scale * np.matmul(qh, kb[: t + 1, g].T)      # dense causal [G, t+1]
+                o, lse = _masked_softmax_attend(logits, mask, vb[: t + 1, g])
+                O[b, r, g * G:(g + 1) * G] = o
+                LSE[b, g * G:(g + 1) * G, r] = lse
+    return O, LSE
+
+
+# ----------------------------------------------------------------------------------------
+# Fixed-graph distance attention  [SLM] "Cómo eligen los tokens a quién escuchar"
+# ----------------------------------------------------------------------------------------
+
+def graph_offsets(local: int, n_pow2: int) -> np.ndarray:
+    """The distinct backward offsets: 0 (the token itself), 1..local (near
+    predecessors) and 2^j for j < n_pow2 (distances 1, 2, 4, 8, ...).  Sorted."""
+    offs = set(range(0, local + 1)) | {1 << j for j in range(n_pow2)}
+    return np.array(sorted(offs), dtype=np.int64)
+
+
+def graph_neighbours(t: int, local: int, n_pow2: int) -> np.ndarray:
+    """N(t) = {t - o : o in the offsets, o ≤ t}.  Reading: positions that would be
+    negative are dropped (no future positions, no clamping to 0)."""
+    o = graph_offsets(local, n_pow2)
+    return np.sort(t - o[o <= t])
+
+
+def graph_neighbour_count(t: int, local: int, n_pow2: int) -> int:
+    """Closed form of |N(t)|: min(t, local) + 1 local ones (self included) plus the
+    power-of-two offsets beyond ``local`` that still reach position ≥ 0."""
+    far = sum(1 for j in range(n_pow2) if (1 << j) > local and (1 << j) <= t)
+    return min(t, local) + 1 + far
+
+
+def graph_attn(cq, ck, v, bias, tau: float, local: int, n_pow2: int, rows=None):
+    """O[b,t,h,:] = Σ_{s∈N(t)} softmax_s(-tau·‖cq[b,t,h]-ck[b,s,h]‖² + bias[h]) · v[b,s,h,:].
+
+    Dense over s ≤ t, then the fixed-graph mask.  Returns (O [B,R,H,D], LSE [B,H,R]).
+    Reading: one coordinate triple per head for queries and keys; no dot-product term
+    and no extra scale (the workload gives the whole logit).
+    """
+    B, T, H, D = v.shape
+    rows = list(range(T)) if rows is None else list(rows)
+    O = np.zeros((B, len(rows), H, D))
+    LSE = np.zeros((B, H, len(rows)))
+    bias = _f64(bias)
+    for b in range(B):
+        ckb, vb = _f64(ck[b]), _f64(v[b])
+        for r, t in enumerate(rows):
+            mask = np.zeros(t + 1, dtype=bool)
+            mask[graph_neighbours(t, local, n_pow2)] = True
+            cqt = _f64(cq[b, t])                                      # [H, 3]
+            diff = cqt[None, :, :] - ckb[: t + 1]                     # [t+1, H, 3]
+            dist2 = np.sum(diff * diff, axis=2).T                     # [H, t+1]
+            logits = -tau * dist2 + bias[:, None]
+            vals = np.transpose(vb[: t + 1], (1, 0, 2))               # [H, t+1, D]
+            o, lse = _masked_softmax_attend(logits, mask, vals)
+            O[b, r] = o
+            LSE[b, :, r] = lse
+    return O, LSE
+
+
+# ----------------------------------------------------------------------------------------
+# Block-selected decode  [NSA] "Puntos Clave" (coarse compression, blockwise selection,
+# sliding window), [STAR] paragraph 3 (combine of partial attentions)
+# ----------------------------------------------------------------------------------------
+
+def block_meanpool(kcache, lens, block: int) -> np.ndarray:
+    """kbar[b, j] = (1/block) Σ_{i<block} K[b, block·j + i] for complete blocks
+    j < lens[b] // block; the other rows are NaN.  Shape [B, Lmax//block, Hkv, D]."""
+    B, Lmax, Hkv, D = kcache.shape
+    nb = Lmax // block
+    kbar = np.full((B, nb, Hkv, D), np.nan)
+    for b in range(B):
+        nfull = int(lens[b]) // block
+        if nfull:
+            kb = _f64(kcache[b, : nfull * block]).reshape(nfull, block, Hkv, D)
+            kbar[b, :nfull] = kb.mean(axis=1)
+    return kbar
+
+
+def decode_select(q, kbar, lens, top_blocks: int, block: int) -> np.ndarray:
+    """sel[b, g, :]: the top ``top_blocks`` complete blocks of sequence b for KV head g by
+    score_j = Σ_{h in group g} q[b,h,:] · kbar[b,j,g,:], ties to the lower j, ascending,
+    padded with -1.  Reading: raw dot product (no scale, no softmax); every complete
+    block is a candidate, including those the window also covers."""
+    B, Hq, D = q.shape
+    Hkv = kbar.shape[2]
+    G = Hq // Hkv
+    sel = np.full((B, Hkv, top_blocks), -1, dtype=np.int32)
+    for b in range(B):
+        nfull = int(lens[b]) // block
+        for g in range(Hkv):
+            qg = _f64(q[b, g * G:(g + 1) * G])                          # [G, D]
+            scores = np.matmul(qg, kbar[b, :nfull, g].T).sum(axis=0)   # Σ_h q_h·kbar_j
+            sel[b, g] = topk_select_row(scores, top_blocks)
+    return sel
+
+
+def decode_token_mask(sel_row, L: int, block: int, window: int) -> np.ndarray:
+    """U over s = 0..L-1: tokens of the selected blocks before the window, united with
+    the last ``window`` tokens [max(0, L-window), L).  Each token once."""
+    m = np.zeros(L, dtype=bool)
+    wstart = max(0, L - window)
+    for j in np.asarray(sel_row):
+        if j < 0:
+            continue
+        lo, hi = int(j) * block, min(int(j) * block + block, wstart)
+        if hi > lo:
+            m[lo:hi] = True
+    m[wstart:L] = True
+    return m
+
+
+def sparse_decode(q, kcache, vcache, lens, block: int, top_blocks: int, window: int,
+                  scale: float, kbar=None):
+    """One decode step per sequence: dense attention of q[b,h] over the cache
+    positions [0, lens[b]) under the mask U (selected blocks ∪ window).
+
+    Returns (O [B,Hq,D], LSE [B,Hq], sel [B,Hkv,top_blocks])."""
+    B, Hq, D = q.shape
+    Hkv = kcache.shape[2]
+    G = Hq // Hkv
+    if kbar is None:
+        kbar = block_meanpool(kcache, lens, block)
+    sel = decode_select(q, kbar, lens, top_blocks, block)
+    O = np.zeros((B, Hq, D))
+    LSE = np.zeros((B, Hq))
+    for b in range(B):
+        L = int(lens[b])
+        for g in range(Hkv):
+            mask = decode_token_mask(sel[b, g], L, block, window)
+            qg = _f64(q[b, g * G:(g + 1) * G])
+            kb = _f64(kcache[b, :L, g])
+            vb = _f64(vcache[b, :L, g])
+            logits = scale * np.matmul(qg, kb.T)                        # dense [G, L]
+            o, lse = _masked_softmax_attend(logits, mask, vb)
+            O[b, g * G:(g + 1) * G] = o
+            LSE[b, g * G:(g + 1) * G] = lse
+    return O, LSE, sel
+
+
+# ----------------------------------------------------------------------------------------
+# Cross-layer index reuse  [IC] paragraph 4 (F layers index and cache, S layers reuse)
+# ----------------------------------------------------------------------------------------
+
+def indexcache_prefill(qi, ki, w, layers, pattern: str, topk: int, window: int,
+                       scale: float, rows=None):
+    """Run the layer pattern (e.g. "FSSS"): an F layer computes indexer scores and the
+    top-k indices and caches them; an S layer reuses the indices of the nearest
+    preceding F layer.  ``layers`` is a list of dicts with q, k, v.  Returns the list of
+    (O, LSE) per layer and the number of indexer evaluations made."""
+    if not pattern or pattern[0] != "F":
+        raise ValueError("the first layer must compute indices (F)")
+    B, T = qi.shape[0], qi.shape[1]
+    rows_l = list(range(T)) if rows is None else list(rows)
+    idx = None
+    n_index = 0
+    outs = []
+    for kind, lay in zip(pattern, layers):
+        if kind == "F":
+            sc = indexer_scores(qi, ki, w, rows_l)
+            idx = topk_select(sc, topk, B, T, rows_l)
+            n_index += 1
+        outs.append(sparse_attn(lay["q"], lay["k"], lay["v"], idx, window, scale, rows_l))
+    return outs, n_index

@@ -1,0 +1,420 @@
+"""Pins of the float64 oracle against facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes the oracle module (``oracle.reference``) and raises
+``AssertionError`` when a pin fails.  ``test_oracle_pins.py`` runs them on the real
+oracle; ``test_oracle_mutants.py`` runs them on deliberately broken copies of it and
+requires every copy to fail at least one pin, which shows that the pins bite.
+
+Pins used (none re-types the oracle's formula or re-calls its library routine the
+same way):
+* hand-worked fixtures in tests/golden/ (each cites the passage it follows);
+* exact rational arithmetic (``fractions``) on integer-valued inputs;
+* library special cases: torch's scaled_dot_product_attention in float64 on the CPU
+  (full causal and banded masks, full attention for a decode query);
+* brute force with pure-Python loops and ``math.exp`` on tiny inputs;
+* closed forms (graph neighbour count, its sum 654,896 at T = 16,384) and invariants
+  (softmax rows sum to one, permutation, bias and window invariances).
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import sa_synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sdpa64(q, k, v, mask=None, causal=False):
+    """torch SDPA in float64 on the CPU.  q [H,Tq,D], k/v [H,Tk,D]; mask [Tq,Tk] bool."""
+    import torch
+    import torch.nn.functional as F
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))[None]
+    kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64))[None]
+    m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask))
+    out = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, is_causal=causal,
+                                         scale=1.0)
+    return out[0].numpy()
+
+
+def _lse64(logits, mask):
+    import torch
+    lg = torch.from_numpy(np.where(mask, logits, -np.inf))
+    return torch.logsumexp(lg, dim=-1).numpy()
+
+
+# ------------------------------------------------------------------------------ indexer
+
+def pin_indexer_hand(orc):
+    g = _golden("indexer_hand.json")
+    qi = np.array(g["qi"], dtype=np.float32)
+    ki = np.array(g["ki"], dtype=np.float32)
+    w = np.array(g["w"], dtype=np.float32)
+    for t, want in enumerate(g["scores"]):
+        got = orc.indexer_scores_row(qi, ki, w, 0, t)
+        assert got.shape == (t + 1,), got.shape
+        assert np.array_equal(got, np.array(want)), (t, got, want)
+
+
+def pin_indexer_exact_integers(orc):
+    """Integer inputs and dyadic weights: every score is an exact rational; the
+    float64 oracle must reproduce it exactly (brute force in Fractions)."""
+    x = sa_synth.integer_indexer_inputs(11, 2, 9, 3, 5)
+    qi, ki, w = x["qi"], x["ki"], x["w"]
+    for b in range(2):
+        for t in range(9):
+            got = orc.indexer_scores_row(qi, ki, w, b, t)
+            for s in range(t + 1):
+                want = Fraction(0)
+                for h in range(3):
+                    dot = sum(Fraction(int(qi[b, t, h, d])) * Fraction(int(ki[b, s, d]))
+                              for d in range(5))
+                    want += Fraction(float(w[h])) * max(dot, Fraction(0))
+                assert Fraction(float(got[s])) == want, (b, t, s, got[s], want)
+
+
+def pin_indexer_odd_part(orc):
+    """ReLU(x) - ReLU(-x) = x per head, so S(qi) - S(-qi) = Σ_h w_h qi_h·ki (checked
+    with exact Fractions on integer inputs); S ≥ 0 everywhere since w ≥ 0."""
+    x = sa_synth.integer_indexer_inputs(12, 1, 6, 2, 4)
+    qi, ki, w = x["qi"], x["ki"], x["w"]
+    for t in range(6):
+        a = orc.indexer_scores_row(qi, ki, w, 0, t)
+        bneg = orc.indexer_scores_row(-qi, ki, w, 0, t)
+        assert (a >= 0).all()
+        for s in range(t + 1):
+            lin = sum(Fraction(float(w[h])) * sum(Fraction(int(qi[0, t, h, d])) * int(ki[0, s, d])
+                                                  for d in range(4)) for h in range(2))
+            assert Fraction(float(a[s])) - Fraction(float(bneg[s])) == lin
+
+
+# ------------------------------------------------------------------------------ top-k
+
+def _topk_brute(row, k):
+    order = sorted(range(len(row)), key=lambda s: (-float(row[s]) + 0.0, s))
+    sel = sorted(order[:k])
+    return sel + [-1] * (k - len(sel))
+
+
+def pin_topk_hand(orc):
+    for c in _golden("topk_hand.json")["cases"]:
+        got = orc.topk_select_row(np.array(c["row"], dtype=np.float64), c["k"])
+        assert got.dtype == np.int32
+        assert got.tolist() == c["idx"], (c, got)
+
+
+def pin_topk_brute(orc):
+    """Full stable sort by (score desc, position asc) on tiny rows with many ties."""
+    g = sa_synth.rng(21)
+    for _ in range(300):
+        n = int(g.integers(1, 40))
+        k = int(g.integers(1, 45))
+        row = g.integers(0, 4, size=n).astype(np.float64) * 0.5
+        if g.random() < 0.3:
+            row = g.standard_normal(n)
+        got = orc.topk_select_row(row, k).tolist()
+        assert got == _topk_brute(row, k), (row, k, got)
+
+
+def pin_topk_invariants(orc):
+    g = sa_synth.rng(22)
+    for _ in range(50):
+        n = int(g.integers(50, 400))
+        k = int(g.integers(1, 64))
+        row = g.standard_normal(n)
+        got = orc.topk_select_row(row, k)
+        sel = got[got >= 0]
+        assert sel.shape[0] == min(k, n)
+        assert (np.diff(sel) > 0).all()
+        uns = np.setdiff1d(np.arange(n), sel)
+        if uns.size:
+            assert row[sel].min() >= row[uns].max()
+
+
+# ------------------------------------------------------------------------------ sparse attention
+
+def pin_attn_hand(orc):
+    g = _golden("attn_hand.json")
+    q, k, v = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v"))
+    for c in g["cases"]:
+        idx = np.full((1, 3, 2), -1, dtype=np.int32)
+        idx[0, 2] = c["idx_row2"]
+        O, L = orc.sparse_attn(q, k, v, idx, c["window"], 1.0, rows=[c["row"]])
+        assert abs(O[0, 0, 0, 0] - c["O"]) < 1e-12, (c, O[0, 0, 0, 0])
+        assert abs(L[0, 0, 0] - c["LSE"]) < 1e-12, (c, L[0, 0, 0])
+
+
+def _expand_gqa(x, G):
+    return np.repeat(x, G, axis=0)    # [Hkv, T, D] -> [Hq, T, D]
+
+
+def pin_attn_full_when_k_covers(orc):
+    """k ≥ T (or W ≥ T) selects every earlier key: plain causal attention, checked
+    against torch SDPA(is_causal=True) in float64 and torch.logsumexp, with GQA
+    (Hq=4, Hkv=2)."""
+    B, T, scale = 2, 37, 0.25
+    x = sa_synth.attn_inputs(31, B, T, 4, 2, 16, "f32")
+    q, k, v = x["q"], x["k"], x["v"]
+
+    def listed(kk):
+        ix = np.full((B, T, kk), -1, dtype=np.int32)
+        for t in range(T):
+            n = min(kk, t + 1)
+            ix[:, t, :n] = np.arange(n, dtype=np.int32)
+        return ix
+
+    cases = ((listed(T), 0), (listed(T + 5), 3), (np.full((B, T, 1), -1, np.int32), T))
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    for ix, W in cases:
+        O, L = orc.sparse_attn(q, k, v, ix, W, scale)
+        for b in range(B):
+            qh = np.transpose(q[b], (1, 0, 2)).astype(np.float64) * scale
+            kh = _expand_gqa(np.transpose(k[b], (1, 0, 2)), 2).astype(np.float64)
+            vh = _expand_gqa(np.transpose(v[b], (1, 0, 2)), 2).astype(np.float64)
+            want = _sdpa64(qh, kh, vh, causal=True)
+            assert np.abs(O[b] - np.transpose(want, (1, 0, 2))).max() < 1e-12
+            logits = np.matmul(qh, np.transpose(kh, (0, 2, 1)))
+            assert np.abs(L[b] - _lse64(logits, causal[None])).max() < 1e-12
+
+
+def pin_attn_window_only(orc):
+    """No usable listed index (all -1, or junk outside [0, t]): the textbook
+    sliding-window attention, checked against SDPA with a banded boolean mask."""
+    T, W = 50, 7
+    x = sa_synth.attn_inputs(32, 1, T, 2, 1, 8, "f32")
+    q, k, v = x["q"], x["k"], x["v"]
+    g = sa_synth.rng(5)
+    junk = np.full((1, T, 4), -1, np.int32)
+    for t in range(T):
+        junk[0, t] = g.integers(t + 1, t + 100, size=4)
+        junk[0, t, ::2] = -9
+    ts = np.arange(T)
+    band = (ts[None, :] <= ts[:, None]) & (ts[None, :] > ts[:, None] - W)
+    want = _sdpa64(np.transpose(q[0], (1, 0, 2)) * 0.5,
+                   _expand_gqa(np.transpose(k[0], (1, 0, 2)), 2),
+                   _expand_gqa(np.transpose(v[0], (1, 0, 2)), 2), mask=band)
+    for idx in (np.full((1, T, 4), -1, np.int32), junk):
+        O, _ = orc.sparse_attn(q, k, v, idx, W, 0.5)
+        assert np.abs(O[0] - np.transpose(want, (1, 0, 2))).max() < 1e-12
+
+
+def pin_attn_brute_tiny(orc):
+    """T ≤ 8: pure-Python loops with math.exp over the explicit selected set."""
+    x = sa_synth.attn_inputs(33, 1, 8, 2, 1, 3, "f32")
+    q, k, v = x["q"], x["k"], x["v"]
+    idx = sa_synth.random_topk_idx(6, 1, 8, 2)
+    W, scale = 2, 0.7
+    O, L = orc.sparse_attn(q, k, v, idx, W, scale)
+    for t in range(8):
+        S = {int(s) for s in idx[0, t] if 0 <= s <= t} | set(range(max(0, t - W + 1), t + 1))
+        for h in range(2):
+            lg = {s: scale * sum(float(q[0, t, h, d]) * float(k[0, s, 0, d]) for d in range(3))
+                  for s in S}
+            mx = max(lg.values())
+            wts = {s: math.exp(lg[s] - mx) for s in S}
+            tot = sum(wts.values())
+            for d in range(3):
+                want = sum(wts[s] * float(v[0, s, 0, d]) for s in S) / tot
+                assert abs(O[0, t, h, d] - want) < 1e-12
+            assert abs(L[0, h, t] - (mx + math.log(tot))) < 1e-12
+
+
+def pin_attn_rows_sum_to_one(orc):
+    """With V ≡ 1 every output equals Σ_s p_s, which must be 1."""
+    x = sa_synth.attn_inputs(34, 1, 300, 4, 1, 32, "f32")
+    idx = sa_synth.random_topk_idx(7, 1, 300, 40)
+    O, _ = orc.sparse_attn(x["q"], x["k"], np.ones_like(x["v"]), idx, 16, 0.2)
+    assert np.abs(O - 1.0).max() <= 1e-12
+
+
+def pin_attn_permutation_and_window_dedup(orc):
+    """Permuting a row's listed indices changes nothing; listing only in-window
+    positions gives the window-only result (each key counted once)."""
+    x = sa_synth.attn_inputs(35, 1, 120, 2, 1, 16, "f32")
+    q, k, v = x["q"], x["k"], x["v"]
+    idx = sa_synth.random_topk_idx(8, 1, 120, 24)
+    g = sa_synth.rng(9)
+    perm = idx.copy()
+    for t in range(120):
+        perm[0, t] = perm[0, t, g.permutation(24)]
+    a, _ = orc.sparse_attn(q, k, v, idx, 8, 0.25)
+    b, _ = orc.sparse_attn(q, k, v, perm, 8, 0.25)
+    assert np.array_equal(a, b)
+    inwin = np.full((1, 120, 24), -1, np.int32)
+    for t in range(120):
+        ws = np.arange(max(0, t - 7), t + 1, dtype=np.int32)
+        inwin[0, t, : ws.shape[0]] = ws[::-1]
+    c, _ = orc.sparse_attn(q, k, v, inwin, 8, 0.25)
+    d, _ = orc.sparse_attn(q, k, v, np.full((1, 120, 24), -1, np.int32), 8, 0.25)
+    assert np.abs(c - d).max() < 1e-14
+
+
+# ------------------------------------------------------------------------------ graph
+
+def pin_graph_hand(orc):
+    g = _golden("graph_hand.json")
+    cq, ck, v = (np.array(g[n], dtype=np.float64) for n in ("cq", "ck", "v"))
+    bias = np.array(g["bias"])
+    for t, nb in enumerate(g["neighbours"]):
+        assert orc.graph_neighbours(t, g["local"], g["n_pow2"]).tolist() == nb
+    O, L = orc.graph_attn(cq, ck, v, bias, g["tau"], g["local"], g["n_pow2"])
+    assert np.abs(O[0, :, 0, 0] - np.array(g["O"])).max() < 1e-12, O[0, :, 0, 0]
+    assert np.abs(L[0, 0] - np.array(g["LSE"])).max() < 1e-12, L[0, 0]
+
+
+def pin_graph_count_closed_form(orc):
+    """|N(t)| = min(t,32)+1+#{j in [6,13]: 2^j ≤ t}, and Σ_{t<16384} |N(t)| = 654,896
+    (= 540,144 local + 114,752 power-of-two; the closed-form sums are in the test)."""
+    for t in range(0, 20000, 7):
+        assert orc.graph_neighbours(t, 32, 14).shape[0] == orc.graph_neighbour_count(t, 32, 14)
+        want = min(t, 32) + 1 + sum(1 for j in range(6, 14) if (1 << j) <= t)
+        assert orc.graph_neighbour_count(t, 32, 14) == want
+    T = 16384
+    local_sum = sum(range(1, 34)) + (T - 33) * 33
+    far_sum = sum(T - (1 << j) for j in range(6, 14))
+    assert local_sum + far_sum == 654896
+    assert sum(orc.graph_neighbour_count(t, 32, 14) for t in range(T)) == 654896
+    assert orc.graph_offsets(32, 14).shape[0] == 41
+
+
+def pin_graph_tau0_mean_and_bias(orc):
+    """τ = 0: every neighbour weighs the same, O = plain mean of V over N(t).
+    Adding a constant to the bias leaves O unchanged and shifts LSE by it."""
+    x = sa_synth.graph_inputs(41, 1, 200, 3, 8, "f32")
+    O, _ = orc.graph_attn(x["cq"], x["ck"], x["v"], x["bias"], 0.0, 4, 8)
+    for t in range(200):
+        nb = sorted({t - o for o in list(range(5)) + [1 << j for j in range(8)] if t - o >= 0})
+        assert np.abs(O[0, t] - x["v"][0, nb].astype(np.float64).mean(axis=0)).max() < 1e-12
+    a, la = orc.graph_attn(x["cq"], x["ck"], x["v"], x["bias"], 1.0, 4, 8)
+    b, lb = orc.graph_attn(x["cq"], x["ck"], x["v"], x["bias"].astype(np.float64) + 3.0, 1.0, 4, 8)
+    assert np.abs(a - b).max() < 1e-12
+    assert np.abs((lb - la) - 3.0).max() < 1e-12
+
+
+def pin_graph_brute_short(orc):
+    """T ≤ local+1: N(t) = [0, t]; pure-Python distance softmax."""
+    x = sa_synth.graph_inputs(42, 1, 10, 2, 3, "f32")
+    tau = 0.8
+    O, L = orc.graph_attn(x["cq"], x["ck"], x["v"], x["bias"], tau, 32, 14)
+    for t in range(10):
+        for h in range(2):
+            lg = []
+            for s in range(t + 1):
+                d2 = sum((float(x["cq"][0, t, h, c]) - float(x["ck"][0, s, h, c])) ** 2 for c in range(3))
+                lg.append(-tau * d2 + float(x["bias"][h]))
+            mx = max(lg)
+            wts = [math.exp(a - mx) for a in lg]
+            for d in range(3):
+                want = sum(wts[s] * float(x["v"][0, s, h, d]) for s in range(t + 1)) / sum(wts)
+                assert abs(O[0, t, h, d] - want) < 1e-12
+            assert abs(L[0, h, t] - (mx + math.log(sum(wts)))) < 1e-12
+
+
+# ------------------------------------------------------------------------------ decode
+
+def pin_decode_hand(orc):
+    g = _golden("decode_hand.json")
+    V = np.array(g["V"], dtype=np.float64).reshape(1, 4, 1, 1)
+    for c in g["cases"]:
+        K = np.array(c["K"], dtype=np.float64).reshape(1, 4, 1, 1)
+        q = np.array([[[c["q"]]]])
+        lens = np.array([4], np.int32)
+        kbar = orc.block_meanpool(K, lens, g["block"])
+        assert kbar[0, :, 0, 0].tolist() == c["kbar"]
+        O, L, sel = orc.sparse_decode(q, K, V, lens, g["block"], g["top_blocks"], g["window"],
+                                      g["scale"])
+        assert sel[0, 0].tolist() == c["sel"], sel
+        assert abs(O[0, 0, 0] - c["O"]) < 1e-12, (c, O)
+        assert abs(L[0, 0] - c["LSE"]) < 1e-12, (c, L)
+
+
+def pin_decode_pool_and_scores_brute(orc):
+    """Block means and block scores by loops over raw cache rows (integer-valued cache:
+    exact), and Σ_h q_h·kbar_j = mean over the block of (Σ_h q_h)·K_s."""
+    g = sa_synth.rng(51)
+    B, L, Hkv, D, G, blk = 2, 45, 2, 3, 2, 4
+    K = g.integers(-3, 4, size=(B, L, Hkv, D)).astype(np.float64)
+    q = g.integers(-2, 3, size=(B, Hkv * G, D)).astype(np.float64)
+    lens = np.array([45, 17], np.int32)
+    kbar = orc.block_meanpool(K, lens, blk)
+    for b in range(B):
+        nfull = lens[b] // blk
+        assert np.isnan(kbar[b, nfull:]).all()
+        for j in range(nfull):
+            for hk in range(Hkv):
+                for d in range(D):
+                    want = Fraction(sum(int(K[b, blk * j + i, hk, d]) for i in range(blk)), blk)
+                    assert Fraction(float(kbar[b, j, hk, d])) == want
+    sel = orc.decode_select(q, kbar, lens, 3, blk)
+    for b in range(B):
+        nfull = int(lens[b]) // blk
+        for hk in range(Hkv):
+            sc = []
+            for j in range(nfull):
+                tot = Fraction(0)
+                for i in range(blk):
+                    for h in range(hk * G, hk * G + G):
+                        tot += sum(Fraction(int(q[b, h, d])) * int(K[b, blk * j + i, hk, d])
+                                   for d in range(D))
+                sc.append(tot / blk)
+            assert sel[b, hk].tolist() == _topk_brute(sc, 3), (b, hk, sel[b, hk], sc)
+
+
+def pin_decode_full_when_all_blocks(orc):
+    """L ≤ top_blocks·block: every block is chosen, so the step is full attention of
+    the query over the whole cache (SDPA, float64, no mask)."""
+    x = sa_synth.decode_inputs(52, 3, 200, 4, 2, 16, "f32", lens=[200, 131, 64])
+    O, L, sel = orc.sparse_decode(x["q"], x["kcache"], x["vcache"], x["lens"], 16, 16, 8, 0.25)
+    for b in range(3):
+        n = int(x["lens"][b])
+        assert (sel[b][sel[b] >= 0].shape[0]) == 2 * min(16, n // 16)
+        for hk in range(2):
+            qg = x["q"][b, 2 * hk: 2 * hk + 2][:, None, :] * 0.25
+            kk = np.repeat(x["kcache"][b, :n, hk][None], 2, axis=0)
+            vv = np.repeat(x["vcache"][b, :n, hk][None], 2, axis=0)
+            want = _sdpa64(qg, kk, vv)[:, 0]
+            assert np.abs(O[b, 2 * hk: 2 * hk + 2] - want).max() < 1e-12
+
+
+def pin_decode_window_covers(orc):
+    """window ≥ L: U is the whole cache whatever the blocks; and the mask of U is the
+    chosen blocks' tokens before the window plus the window (checked by enumeration)."""
+    x = sa_synth.decode_inputs(53, 1, 300, 2, 1, 8, "f32")
+    a, _, _ = orc.sparse_decode(x["q"], x["kcache"], x["vcache"], x["lens"], 8, 2, 300, 0.3)
+    want = _sdpa64(x["q"][0][:, None, :].astype(np.float64) * 0.3, np.repeat(x["kcache"][0, :, 0][None], 2, 0),
+                   np.repeat(x["vcache"][0, :, 0][None], 2, 0))[:, 0]
+    assert np.abs(a[0] - want).max() < 1e-12
+    m = orc.decode_token_mask(np.array([3, 36, -1]), 300, 8, 20)
+    expect = set(range(24, 32)) | set(range(280, 300))   # block 36 lies inside the window
+    assert set(np.flatnonzero(m).tolist()) == expect
+
+
+# ------------------------------------------------------------------------------ index reuse
+
+def pin_indexcache(orc):
+    """F,S,S,S: one indexer evaluation; each S layer equals sparse attention with the F
+    layer's indices (the 3 skipped evaluations are the '75%' of the IndexCache page)."""
+    T = 40
+    x = sa_synth.indexer_inputs(61, 1, T, 2, 8, "f32")
+    layers = [sa_synth.attn_inputs(62 + l, 1, T, 2, 1, 8, "f32") for l in range(4)]
+    outs, n_index = orc.indexcache_prefill(x["qi"], x["ki"], x["w"], layers, "FSSS", 6, 3, 0.3)
+    assert n_index == 1
+    sc = orc.indexer_scores(x["qi"], x["ki"], x["w"])
+    idx = orc.topk_select(sc, 6, 1, T)
+    for lay, (O, _) in zip(layers, outs):
+        want, _ = orc.sparse_attn(lay["q"], lay["k"], lay["v"], idx, 3, 0.3)
+        assert np.array_equal(O, want)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

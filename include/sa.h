@@ -1,0 +1,199 @@
+/*
+ * sa.h — C ABI of libsa, causal sparse attention for AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point is asynchronous on the HIP stream it is given (``stream`` is a
+ * hipStream_t passed as void*; NULL means the default stream).  The library never
+ * allocates or frees memory and never synchronises the host: all tensors, including
+ * the decode workspace, belong to the caller, who keeps them alive until the stream
+ * has executed the call.  All tensor pointers are DEVICE pointers to contiguous,
+ * 16-byte-aligned buffers in the layouts documented below (row-major, last index
+ * fastest).  Scalars and sizes are plain host values.
+ *
+ * Error behaviour: every call validates its arguments before touching the GPU and
+ * returns SA_OK or an SA_ERR_* status.  On error nothing is launched and
+ * sa_last_error() (per host thread) describes the problem.  A failed kernel launch
+ * returns SA_ERR_HIP with the HIP error text; faults inside a kernel surface at the
+ * caller's next synchronisation.  No C++ exception crosses this boundary.
+ *
+ * Notation: B batch, T tokens, Hq query heads, Hkv key/value heads (Hq % Hkv == 0,
+ * query head h reads KV head h / (Hq / Hkv)), D head dimension.  "bf16" tensors are
+ * stored as bfloat16 and accumulated in float32; "f32" tensors are float32.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [IC]   "IndexCache ... inferencia 82% más rápida" (larebelion.com, from VentureBeat), body
+ *   [HS2]  "Xiaomi presenta HySparse2 ..." (diariobitcoin.com), sections "Dos niveles para
+ *          compartir la caché" and "Más precisión con menos memoria"
+ *   [SLM]  "SpatialLM-Mini aceleró el entrenamiento con un contexto de 16K en 2,47 veces en
+ *          una RTX 3050" (news.hamidun.com), section "Cómo eligen los tokens a quién escuchar"
+ *   [NSA]  "Native Sparse Attention: Revolucionando el Procesamiento de Contexto Extenso ..."
+ *          (ctol-es.com), sections "Puntos Clave" and "Análisis Profundo"
+ *   [STAR] "NVIDIA AI Research presenta Star Attention ..." (7minutos.es), body paragraph 3
+ */
+#ifndef LIBSA_SA_H
+#define LIBSA_SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_VERSION 100 /* 1.0.0 */
+
+/* Element types of the input/output tensors. */
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* Status codes. */
+enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent shapes */
+  SA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (dtype, D, ...) */
+  SA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace query */
+  SA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  SA_ERR_INTERNAL = 5     /* unexpected internal error */
+};
+
+/*
+ * Indexer scores.  [IC] body paragraphs 2-3: a lightweight indexer scores every
+ * earlier token of every query.
+ *
+ *   scores[b, r, s] = sum_{h < H_I} w[h] * max(0, qi[b, t, h, :] . ki[b, s, :])
+ *   for t = row_begin + r and every s <= t.
+ *
+ * qi     [B, T, H_I, D_I]  dtype
+ * ki     [B, T, D_I]       dtype   (one indexer key per token, shared by the heads)
+ * w      [H_I]             float32 (one weight per indexer head; no scale factor)
+ * scores [B, row_end - row_begin, ld] float32, written for s <= t only; entries with
+ *        s > t are left untouched.  Rows may be computed in chunks by calling with
+ *        consecutive [row_begin, row_end) ranges.
+ * Requires 0 <= row_begin < row_end <= T, ld >= row_end, ld % 4 == 0, 1 <= H_I <= 64,
+ * D_I % 8 == 0 and D_I <= 256.  bf16 with H_I in {1,2,4} and D_I % 32 == 0 runs on MFMA.
+ */
+int sa_indexer_scores(const void* qi, const void* ki, const float* w, int B, int T, int H_I,
+                      int D_I, int dtype, int row_begin, int row_end, float* scores,
+                      int64_t ld, void* stream);
+
+/*
+ * Top-k selection.  [IC] body paragraph 2 (select a small subset) and [HS2] "Más
+ * precisión con menos memoria" (individual tokens).
+ *
+ * For each row t in [row_begin, row_end): the min(k, t+1) positions s <= t with the
+ * largest scores[b, t - row_begin, s]; ties go to the lower s; -0.0 counts as +0.0.
+ * Written ascending to idx[b, t, 0:k] and padded with -1.  Scores must be finite.
+ *
+ * scores [B, row_end - row_begin, ld] float32 (as written by sa_indexer_scores)
+ * idx    [B, T, k] int32; only rows [row_begin, row_end) are written.
+ * Requires 1 <= k <= 4096 and ld >= row_end.
+ */
+int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin, int row_end,
+                   int k, int32_t* idx, void* stream);
+
+/*
+ * Sparse attention forward over the selected set.  [IC] body paragraph 2 (attend only
+ * to the selected subset), [HS2] "Dos niveles ..." (the most recent tokens are forced
+ * into the set), [NSA] "Análisis Profundo" (one selection and one K/V fetch shared by
+ * the query heads of a KV group).
+ *
+ *   S_t = { s in idx[b, t, :] : 0 <= s <= t }  U  { max(0, t-window+1), ..., t }
+ *   out[b, t, h, :] = sum_{s in S_t} softmax_s(scale * q[b,t,h,:] . k[b,s,g,:]) v[b,s,g,:]
+ *   lse[b, h, t]    = log sum_{s in S_t} exp(scale * q . k)       (natural log)
+ *
+ * Each key counts once: listed positions inside the window, -1 and any value outside
+ * [0, t] are ignored.  Listed positions must be distinct (duplicates are a caller
+ * error and are counted twice).  An empty S_t gives out = 0 and lse = -inf.
+ *
+ * q   [B, T, Hq, D]  dtype        k, v [B, T, Hkv, D] dtype
+ * idx [B, T, topk]   int32        (topk may be 0 with idx == NULL)
+ * out [B, T, Hq, D]  dtype        lse  [B, Hq, T] float32, may be NULL
+ * Requires D in {64, 128}, window >= 0, topk >= 0, topk + window >= 1.
+ * bf16 with Hq/Hkv <= 16 runs the grouped-head MFMA kernel; other cases a VALU kernel.
+ */
+int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                       int T, int Hq, int Hkv, int D, int topk, int window, float scale,
+                       int dtype, void* out, float* lse, void* stream);
+
+/*
+ * Fixed-graph distance attention.  [SLM] "Cómo eligen los tokens a quién escuchar": a
+ * fixed list of allowed positions (the token itself, its near predecessors and
+ * positions at distances 1, 2, 4, 8, ...), never future ones; the weight grows as the
+ * distance between learned 3-D query and key coordinates shrinks, shifted by a learned
+ * per-head parameter.
+ *
+ *   N(t) = { t - o : o in {0, 1, ..., local} U {2^j : 0 <= j < n_pow2}, o <= t }
+ *   logit(t, s, h) = -tau * ||cq[b,t,h,:] - ck[b,s,h,:]||^2 + bias[h]
+ *   out[b, t, h, :] = sum_{s in N(t)} softmax_s(logit) v[b, s, h, :]
+ *
+ * Positions that would be negative are dropped.  Distances and softmax run in float32.
+ * cq, ck [B, T, H, 3] dtype     v, out [B, T, H, D] dtype     bias [H] float32
+ * lse    [B, H, T] float32, may be NULL
+ * Requires 0 <= local <= 64, 0 <= n_pow2 <= 30, D % 8 == 0, H * D <= 4096.
+ */
+int sa_graph_attn_fwd(const void* cq, const void* ck, const void* v, const float* bias,
+                      float tau, int B, int T, int H, int D, int local, int n_pow2, int dtype,
+                      void* out, float* lse, void* stream);
+
+/*
+ * Block mean-pooling of a key cache.  [NSA] "Puntos Clave" (coarse compression).
+ *
+ *   kbar[b, j, g, :] = (1/block) sum_{i < block} kcache[b, block*j + i, g, :]
+ *   for complete blocks j < lens[b] / block (integer division); other rows untouched.
+ *
+ * kcache [B, Lmax, Hkv, D] dtype; lens [B] int32 on the device (1 <= lens[b] <= Lmax);
+ * kbar   [B, Lmax / block, Hkv, D] float32.  Meant to run once per cache, not per step.
+ * Requires block in {16, 32, 64, 128}, D % 4 == 0.
+ */
+int sa_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, int Hkv, int D,
+                      int block, int dtype, float* kbar, void* stream);
+
+/*
+ * One block-selected decode step.  [NSA] "Puntos Clave" (blockwise selection plus a
+ * sliding window), [STAR] paragraph 3 (partial attentions merged by a distributed
+ * softmax: here the split-K partials are merged by their log-sum-exp).
+ *
+ * For each sequence b and KV head g, with L = lens[b]:
+ *   score_j = sum_{h in group g} q[b,h,:] . kbar[b,j,g,:]    for complete blocks j < L/block
+ *   sel     = the top_blocks best j (ties to the lower j), ascending, padded with -1
+ *   U       = { s in block j : j in sel, s < L - window }  U  [max(0, L-window), L)
+ *   out[b,h,:] = sum_{s in U} softmax_s(scale * q[b,h,:] . kcache[b,s,g,:]) vcache[b,s,g,:]
+ * computed as n_splits partial softmaxes (m, l, o) over slices of U merged with
+ * M = max m_i, out = sum e^(m_i-M) o_i / sum e^(m_i-M) l_i, lse = M + log sum e^(m_i-M) l_i.
+ *
+ * q [B, Hq, D] dtype; kcache, vcache [B, Lmax, Hkv, D] dtype; kbar from sa_block_meanpool;
+ * lens [B] int32 on the device; out [B, Hq, D] dtype; lse [B, Hq] float32 or NULL;
+ * sel_blocks [B, Hkv, top_blocks] int32 or NULL.
+ * n_splits: 0 = automatic, else 1..64.  workspace: device memory of at least
+ * sa_sparse_decode_workspace(...) bytes, ZERO-FILLED before its first use; every call
+ * leaves its counters at zero again.  Calls that share a workspace must be ordered on
+ * one stream.
+ * Requires D in {64, 128}, bf16, Hq/Hkv <= 16, block in {16, 32, 64, 128},
+ * 1 <= top_blocks <= 64, window >= 0.
+ */
+int sa_sparse_decode(const void* q, const void* kcache, const void* vcache, const float* kbar,
+                     const int32_t* lens, int B, int Lmax, int Hq, int Hkv, int D, int block,
+                     int top_blocks, int window, int n_splits, float scale, int dtype, void* out,
+                     float* lse, int32_t* sel_blocks, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Workspace bytes sa_sparse_decode needs for these sizes (0 on invalid sizes). */
+size_t sa_sparse_decode_workspace(int B, int Lmax, int Hq, int Hkv, int D, int block,
+                                  int top_blocks, int window, int n_splits);
+
+/* The n_splits value sa_sparse_decode uses for n_splits == 0 (0 on invalid sizes). */
+int sa_sparse_decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_blocks,
+                                 int window);
+
+/* Human-readable name of a status code (static storage). */
+const char* sa_status_str(int status);
+
+/* Detail of the last error on the calling host thread ("" if none). */
+const char* sa_last_error(void);
+
+/* SA_VERSION of the built library. */
+int sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSA_SA_H */

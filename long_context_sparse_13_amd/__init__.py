@@ -1,0 +1,280 @@
+"""Python binding of libsa (causal sparse attention for MI355X / gfx950).
+
+A thin ctypes layer over the C ABI declared in ``include/sa.h``: each ``sa_*`` function
+here has the name of the C entry point it calls, checks that the tensors are CUDA (HIP)
+tensors of the expected dtype, allocates the outputs with torch when they are not given,
+and passes raw device pointers plus torch's current stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback: if ``libsa.so`` is
+missing or fails to load, every call raises.
+
+Build the library with ``python -m long_context_sparse_13_amd.build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "SAError", "lib", "library_path", "declared_symbols",
+    "sa_indexer_scores", "sa_topk_select", "sa_sparse_attn_fwd", "sa_graph_attn_fwd",
+    "sa_block_meanpool", "sa_sparse_decode", "sa_sparse_decode_workspace",
+    "sa_sparse_decode_auto_splits", "sa_version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "sa.h")
+SA_F32, SA_BF16 = 0, 1
+
+_c_void_p, _c_int, _c_int64, _c_float, _c_size_t = (
+    ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t)
+
+_SIGS = {
+    "sa_indexer_scores": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_void_p, _c_int64, _c_void_p]),
+    "sa_topk_select": (_c_int, [_c_void_p, _c_int64, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_void_p, _c_void_p]),
+    "sa_sparse_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                    _c_void_p, _c_void_p, _c_void_p]),
+    "sa_graph_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float, _c_int,
+                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p,
+                                   _c_void_p, _c_void_p]),
+    "sa_block_meanpool": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_int, _c_void_p, _c_void_p]),
+    "sa_sparse_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _c_float, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_size_t, _c_void_p]),
+    "sa_sparse_decode_workspace": (_c_size_t, [_c_int] * 9),
+    "sa_sparse_decode_auto_splits": (_c_int, [_c_int] * 6),
+    "sa_status_str": (ctypes.c_char_p, [_c_int]),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_version": (_c_int, []),
+}
+
+_lib = None
+
+
+class SAError(RuntimeError):
+    """A libsa call returned an error status."""
+
+    def __init__(self, fn: str, status: int, name: str, detail: str):
+        super().__init__(f"{fn} failed: {name}: {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+def library_path() -> str:
+    return os.environ.get("SA_LIBRARY", os.path.join(_HERE, "libsa.so"))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsa.so (once).  Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libsa.so not found at {path}; build it with "
+                               "`python -m long_context_sparse_13_amd.build`")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions include/sa.h declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
+
+
+def sa_version() -> int:
+    return lib().sa_version()
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        L = lib()
+        raise SAError(fn, rc, L.sa_status_str(rc).decode(), L.sa_last_error().decode())
+
+
+# ------------------------------------------------------------------------ marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name: str, dtype=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ------------------------------------------------------------------------ entry points
+def sa_indexer_scores(qi, ki, w, row_begin: int = 0, row_end: int | None = None,
+                      scores=None, ld: int | None = None):
+    """scores[b, r, s] = Σ_h w[h]·ReLU(qi[b,t,h]·ki[b,s]) for t = row_begin + r, s ≤ t.
+
+    qi [B,T,H_I,D_I], ki [B,T,D_I] (bf16 or f32), w [H_I] f32.  Returns scores
+    [B, row_end-row_begin, ld] f32 (entries s > t untouched / uninitialised)."""
+    torch = _torch()
+    _dev(qi, "qi"); _dev(ki, "ki", qi.dtype); _dev(w, "w", torch.float32)
+    B, T, H, DI = qi.shape
+    row_end = T if row_end is None else row_end
+    ld = ld if ld is not None else ((row_end + 3) // 4) * 4
+    R = row_end - row_begin
+    if scores is None:
+        scores = torch.empty((B, R, ld), dtype=torch.float32, device=qi.device)
+    _dev(scores, "scores", torch.float32)
+    rc = lib().sa_indexer_scores(_p(qi), _p(ki), _p(w), B, T, H, DI, _dtype_code(qi), row_begin,
+                                 row_end, _p(scores), ld, _stream(qi.device))
+    _check("sa_indexer_scores", rc)
+    return scores
+
+
+def sa_topk_select(scores, k: int, T: int, row_begin: int = 0, row_end: int | None = None,
+                   idx=None, ld: int | None = None):
+    """idx[b, t, :k] for rows [row_begin, row_end): top-k positions, ascending, -1 padded.
+    ``scores`` is [B, row_end-row_begin, ld] f32; ``idx`` is [B, T, k] int32."""
+    torch = _torch()
+    _dev(scores, "scores", torch.float32)
+    B, R, ld0 = scores.shape
+    ld = ld0 if ld is None else ld
+    row_end = row_begin + R if row_end is None else row_end
+    if idx is None:
+        idx = torch.full((B, T, k), -1, dtype=torch.int32, device=scores.device)
+    _dev(idx, "idx", torch.int32)
+    rc = lib().sa_topk_select(_p(scores), ld, B, T, row_begin, row_end, k, _p(idx),
+                              _stream(scores.device))
+    _check("sa_topk_select", rc)
+    return idx
+
+
+def sa_sparse_attn_fwd(q, k, v, idx, window: int, scale: float, out=None, lse=None,
+                       return_lse: bool = False):
+    """O over S_t = idx[t] ∪ window; q [B,T,Hq,D], k/v [B,T,Hkv,D], idx [B,T,topk] int32
+    (or None with topk = 0).  Returns out (and lse [B,Hq,T] f32 if asked)."""
+    torch = _torch()
+    _dev(q, "q"); _dev(k, "k", q.dtype); _dev(v, "v", q.dtype)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    topk = 0
+    if idx is not None:
+        _dev(idx, "idx", torch.int32)
+        topk = idx.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = lib().sa_sparse_attn_fwd(_p(q), _p(k), _p(v), _p(idx), B, T, Hq, Hkv, D, topk, window,
+                                  float(scale), _dtype_code(q), _p(out), _p(lse),
+                                  _stream(q.device))
+    _check("sa_sparse_attn_fwd", rc)
+    return (out, lse) if return_lse else out
+
+
+def sa_graph_attn_fwd(cq, ck, v, bias, tau: float, local: int, n_pow2: int, out=None,
+                      return_lse: bool = False):
+    """Fixed-graph distance attention; cq/ck [B,T,H,3], v [B,T,H,D] (same dtype), bias [H] f32."""
+    torch = _torch()
+    _dev(cq, "cq", v.dtype); _dev(ck, "ck", v.dtype); _dev(v, "v"); _dev(bias, "bias", torch.float32)
+    B, T, H, D = v.shape
+    if out is None:
+        out = torch.empty_like(v)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device) if return_lse else None
+    rc = lib().sa_graph_attn_fwd(_p(cq), _p(ck), _p(v), _p(bias), float(tau), B, T, H, D, local,
+                                 n_pow2, _dtype_code(v), _p(out), _p(lse), _stream(v.device))
+    _check("sa_graph_attn_fwd", rc)
+    return (out, lse) if return_lse else out
+
+
+def sa_block_meanpool(kcache, lens, block: int, kbar=None):
+    """kbar [B, Lmax//block, Hkv, D] f32 of complete blocks (others untouched)."""
+    torch = _torch()
+    _dev(kcache, "kcache"); _dev(lens, "lens", torch.int32)
+    B, Lmax, Hkv, D = kcache.shape
+    if kbar is None:
+        kbar = torch.zeros((B, Lmax // block, Hkv, D), dtype=torch.float32, device=kcache.device)
+    _dev(kbar, "kbar", torch.float32)
+    rc = lib().sa_block_meanpool(_p(kcache), _p(lens), B, Lmax, Hkv, D, block,
+                                 _dtype_code(kcache), _p(kbar), _stream(kcache.device))
+    _check("sa_block_meanpool", rc)
+    return kbar
+
+
+def sa_sparse_decode_workspace(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits=0) -> int:
+    return int(lib().sa_sparse_decode_workspace(B, Lmax, Hq, Hkv, D, block, top_blocks, window,
+                                                n_splits))
+
+
+def sa_sparse_decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window) -> int:
+    return int(lib().sa_sparse_decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window))
+
+
+def sa_sparse_decode(q, kcache, vcache, kbar, lens, block: int, top_blocks: int, window: int,
+                     scale: float, n_splits: int = 0, workspace=None, out=None,
+                     return_lse: bool = False, return_sel: bool = False):
+    """One block-selected decode step.  q [B,Hq,D] bf16; caches [B,Lmax,Hkv,D] bf16;
+    kbar from sa_block_meanpool; lens [B] int32.  ``workspace`` (uint8, zero-filled before
+    its first use) is allocated when not given.  Returns out [, lse] [, sel]."""
+    torch = _torch()
+    _dev(q, "q"); _dev(kcache, "kcache", q.dtype); _dev(vcache, "vcache", q.dtype)
+    _dev(kbar, "kbar", torch.float32); _dev(lens, "lens", torch.int32)
+    B, Hq, D = q.shape
+    _, Lmax, Hkv, _ = kcache.shape
+    need = sa_sparse_decode_workspace(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    sel = (torch.empty((B, Hkv, top_blocks), dtype=torch.int32, device=q.device)
+           if return_sel else None)
+    rc = lib().sa_sparse_decode(_p(q), _p(kcache), _p(vcache), _p(kbar), _p(lens), B, Lmax, Hq,
+                                Hkv, D, block, top_blocks, window, n_splits, float(scale),
+                                _dtype_code(q), _p(out), _p(lse), _p(sel), _p(workspace),
+                                workspace.numel(), _stream(q.device))
+    _check("sa_sparse_decode", rc)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_sel:
+        res.append(sel)
+    return res[0] if len(res) == 1 else tuple(res)

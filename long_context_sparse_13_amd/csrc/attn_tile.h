@@ -1,0 +1,172 @@
+// One wavefront attends one query (all query heads of one KV group, up to 16) to a
+// stream of gathered keys, 32 keys per step, with an online softmax.
+//
+// Both products run on the gfx950 16x16x32 bf16 MFMA with the 16 query heads as the
+// N dimension, so each gathered K/V row is fetched once for the whole group:
+//   S^T[key, h] = K[key, :] . Q[h, :]       A = K rows (straight from memory, 16 B per
+//                                           lane), B = Q (registers)
+//   O^T[d, h]  += V^T[d, key] P^T[key, h]   A = V^T (LDS, transposed read), B = P^T
+//                                           (the S^T accumulators, rounded to bf16)
+// Lane (n = lane % 16, grp = lane / 16) holds, in the 16x16 MFMA C layout, rows
+// grp*4 .. grp*4+3 of column n.  Column n is the query head, so the softmax statistics
+// and the O^T accumulators of a head all live in the four lanes n, n+16, n+32, n+48 and
+// the rescale by exp(m_old - m_new) is lane-local.
+//
+// The reduction (K) slot (grp, j) of the P.V product is mapped to the key
+// kmap(grp, j) = grp*4 + j (j < 4) or 16 + grp*4 + j - 4 (j >= 4): exactly the keys
+// whose scores the lane already holds from the two S^T tiles, so P needs no shuffle.
+#pragma once
+
+#include "sa_device.h"
+
+namespace sa {
+
+template <int D>
+struct GroupAttn {
+  static constexpr int KS = D / 32;        // 32-wide k-steps of Q.K
+  static constexpr int DT = D / 16;        // 16-wide d tiles of the output
+  static constexpr int CH = D * 2 / 16;    // 16-byte chunks per bf16 row
+  static constexpr int LROW = D * 2 + 16;  // LDS bytes per staged V row (padded)
+  static constexpr int LDS_BYTES = 32 * LROW;
+
+  bf16x8 qB[KS];
+  f32x4 acc[DT];
+  float m_run;  // running max of the log2-domain logits (same in the 4 lanes of a head)
+  float l_run;  // lane-partial running sum of exp2(logit - m_run)
+
+  // qrow: this lane's head row (D bf16) or nullptr for a padding head.
+  __device__ __forceinline__ void init(const uint16_t* qrow, int grp) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (qrow) w = ld16(qrow + ks * 32 + grp * 8);
+      qB[ks] = as_bf16x8(w);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  }
+
+  // One step over 32 keys.  Every lane passes `key` = the key of slot (lane & 31)
+  // (any in-bounds row index when that slot is invalid) and the 32-bit slot mask `vm`
+  // (bit i set = slot i attended; vm != 0).  kbase/vbase point at row 0 of this KV head,
+  // `stride` is the element distance between consecutive rows.  `vl` is this wave's LDS
+  // staging area of LDS_BYTES.
+  __device__ __forceinline__ void step(const uint16_t* __restrict__ kbase,
+                                       const uint16_t* __restrict__ vbase, int64_t stride,
+                                       int key, uint32_t vm, unsigned char* vl,
+                                       float scale_log2, int lane) {
+    const int n = lane & 15, grp = lane >> 4;
+
+    // ---- gather: K rows as MFMA A operands, V rows into LDS
+    u32x4 kA[2][KS];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int slot = c2 * 16 + n;
+      const int kr = shfl_i(key, slot);
+      const bool ok = (vm >> slot) & 1u;
+      const uint16_t* kp = kbase + (int64_t)kr * stride + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ok) w = ld16(kp + ks * 32);
+        kA[c2][ks] = w;
+      }
+    }
+    constexpr int RPI = 64 / CH;  // rows per wave instruction
+    u32x4 vw[CH / 2];
+#pragma unroll
+    for (int i = 0; i < CH / 2; ++i) {
+      const int r = lane / CH + RPI * i;
+      const int c = lane % CH;
+      const int vr = shfl_i(key, r);
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if ((vm >> r) & 1u) w = ld16(vbase + (int64_t)vr * stride + c * 8);
+      vw[i] = w;
+    }
+
+    // ---- S^T = K . Q^T for the two 16-key halves
+    f32x4 s[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      s[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kA[c2][ks]), qB[ks], s[c2], 0, 0, 0);
+    }
+
+    // stage V while the score MFMAs drain
+#pragma unroll
+    for (int i = 0; i < CH / 2; ++i) {
+      const int r = lane / CH + RPI * i;
+      const int c = lane % CH;
+      st16(vl + r * LROW + c * 16, vw[i]);
+    }
+
+    // ---- online softmax (log2 domain); head n's max over the 4 lane groups
+    float x[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = c2 * 16 + grp * 4 + i;
+        const float v = ((vm >> slot) & 1u) ? s[c2][i] * scale_log2 : -INFINITY;
+        x[c2 * 4 + i] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, shfl_xor_f(mt, 16));
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = exp2f(x[j] - m_new);
+      psum += x[j];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+
+    const u32x4 pw = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    const bf16x8 pB = as_bf16x8(pw);
+
+    wave_lds_sync();  // V rows written by other lanes are visible
+
+    // ---- O^T += V^T . P^T
+    const unsigned char* vrow[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (j < 4) ? grp * 4 + j : 16 + grp * 4 + (j - 4);
+      vrow[j] = vl + r * LROW + n * 2;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      uint32_t a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(vrow[2 * j] + dt * 32);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(vrow[2 * j + 1] + dt * 32);
+        a[j] = lo | (hi << 16);
+      }
+      const u32x4 aw = {a[0], a[1], a[2], a[3]};
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), pB, acc[dt], 0, 0, 0);
+    }
+
+    wave_lds_sync();  // the staging area may be overwritten by the next step
+  }
+
+  // Sum of the lane-partial l over the 4 lanes of head n.
+  __device__ __forceinline__ float total_l() const {
+    float l = l_run;
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    return l;
+  }
+};
+
+}  // namespace sa

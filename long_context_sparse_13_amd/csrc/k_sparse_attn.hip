@@ -1,0 +1,237 @@
+// Gathered causal sparse attention forward over S_t = listed indices U window.
+//
+// [IC] IndexCache page, body paragraph 2: each query attends only to its selected
+// subset.  [HS2] HySparse2 page, "Dos niveles para compartir la caché": the most
+// recent tokens are forced into the selected set.  [NSA] Native Sparse Attention page,
+// "Análisis Profundo": group-centric loading, one K/V fetch shared by the query heads
+// of a KV group.
+//
+// Two kernels:
+//  * sparse_attn_mfma<D>: bf16, up to 16 query heads per KV head.  One wavefront per
+//    (batch, token, KV head); keys are streamed 32 at a time through GroupAttn (MFMA
+//    over the grouped heads, online softmax).  The listed indices are visited first
+//    (positions inside the window or outside [0, t] are masked out, so each key is
+//    counted once), then the window [t-W+1, t].
+//  * sparse_attn_valu<D, BF16>: any dtype, up to 64 heads per group (G*D <= 4096); plain
+//    float32 vector arithmetic, one wavefront per (batch, token, KV head), 64 keys per
+//    step with one key per lane for the logits and lanes over (head, d) for P.V.
+#include "attn_tile.h"
+#include "sa_launch.h"
+
+namespace sa {
+
+template <int D>
+__global__ __launch_bounds__(64) void sparse_attn_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int B, int T, int Hq,
+    int Hkv, int topk, int window, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  using GA = GroupAttn<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char vl[GA::LDS_BYTES];
+
+  const int lane = threadIdx.x;
+  const int n = lane & 15, grp = lane >> 4;
+  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * T * Hkv);
+  if (item < 0) return;
+  const int g = (int)(item % Hkv);
+  const int t = (int)((item / Hkv) % T);
+  const int b = (int)(item / ((int64_t)Hkv * T));
+  const int G = Hq / Hkv;
+  const int h = g * G + n;
+  const bool hv = n < G;
+
+  GA ga;
+  ga.init(hv ? q + (((int64_t)b * T + t) * Hq + h) * D : nullptr, grp);
+
+  const int64_t stride = (int64_t)Hkv * D;
+  const uint16_t* kbase = k + ((int64_t)b * T * Hkv + g) * D;
+  const uint16_t* vbase = v + ((int64_t)b * T * Hkv + g) * D;
+  const int32_t* irow = idx ? idx + ((int64_t)b * T + t) * topk : nullptr;
+
+  const int n_idx = (topk + 31) / 32;
+  const int n_win = (window + 31) / 32;
+  const int slot = lane & 31;
+  const int last_listed = t - window;  // listed keys must satisfy 0 <= s <= t - window
+  const int wlo = t - window + 1;
+
+  for (int tile = 0; tile < n_idx + n_win; ++tile) {
+    int key;
+    bool ok;
+    if (tile < n_idx) {
+      const int e = tile * 32 + slot;
+      key = e < topk ? irow[e] : -1;
+      ok = key >= 0 && key <= last_listed;
+    } else {
+      key = wlo + (tile - n_idx) * 32 + slot;
+      ok = key >= 0 && key <= t;
+    }
+    const uint32_t vm = (uint32_t)ballot(ok);
+    if (vm == 0u) continue;
+    ga.step(kbase, vbase, stride, ok ? key : 0, vm, vl, scale_log2, lane);
+  }
+
+  const float l = ga.total_l();
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (hv) {
+    uint16_t* orow = out + (((int64_t)b * T + t) * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < GA::DT; ++dt) {
+      const f32x4 a = ga.acc[dt] * inv;
+      const u32x2 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+      st8(orow + dt * 16 + grp * 4, w);
+    }
+    if (lse && grp == 0)
+      lse[((int64_t)b * Hq + h) * T + t] = l > 0.f ? (ga.m_run + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+template <bool BF>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (BF) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  else return reinterpret_cast<const float*>(p)[i];
+}
+
+template <int D, bool BF>
+__global__ __launch_bounds__(64) void sparse_attn_valu(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const int32_t* __restrict__ idx, int B, int T, int Hq, int Hkv, int topk, int window,
+    float scale_log2, void* __restrict__ out, float* __restrict__ lse) {
+  constexpr int MAXE = 4096;              // G * D
+  __shared__ float qs[MAXE];               // scaled queries of the group, [G][D]
+  __shared__ float os[MAXE];               // output accumulators, [G][D]
+  __shared__ float ps[64 * 65];            // probabilities of the step, [key][G] (G <= 64)
+  __shared__ float ms[64], ls[64], al[64]; // per-head running max, sum, rescale
+  __shared__ int keys[64];
+
+  const int lane = threadIdx.x;
+  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * T * Hkv);
+  if (item < 0) return;
+  const int g = (int)(item % Hkv);
+  const int t = (int)((item / Hkv) % T);
+  const int b = (int)(item / ((int64_t)Hkv * T));
+  const int G = Hq / Hkv;
+  const int GD = G * D;
+
+  const int64_t qoff = (((int64_t)b * T + t) * Hq + (int64_t)g * G) * D;
+  for (int e = lane; e < GD; e += 64) {
+    qs[e] = load_elem<BF>(q, qoff + e) * scale_log2;
+    os[e] = 0.f;
+  }
+  for (int hh = lane; hh < G; hh += 64) {
+    ms[hh] = -INFINITY;
+    ls[hh] = 0.f;
+  }
+  __syncthreads();
+
+  const int64_t stride = (int64_t)Hkv * D;
+  const int64_t kvoff = ((int64_t)b * T * Hkv + g) * D;
+  const int32_t* irow = idx ? idx + ((int64_t)b * T + t) * topk : nullptr;
+  const int n_idx = (topk + 63) / 64;
+  const int n_win = (window + 63) / 64;
+  const int wlo = t - window + 1;
+
+  for (int tile = 0; tile < n_idx + n_win; ++tile) {
+    int key;
+    bool ok;
+    if (tile < n_idx) {
+      const int e = tile * 64 + lane;
+      key = e < topk ? irow[e] : -1;
+      ok = key >= 0 && key <= t - window;
+    } else {
+      key = wlo + (tile - n_idx) * 64 + lane;
+      ok = key >= 0 && key <= t;
+    }
+    if (ballot(ok) == 0ull) continue;
+    keys[lane] = ok ? key : -1;
+
+    // logits of this lane's key for every head of the group
+    for (int hh = 0; hh < G; ++hh) ps[lane * 65 + hh] = -INFINITY;
+    if (ok) {
+      const int64_t kr = kvoff + (int64_t)key * stride;
+      for (int hh = 0; hh < G; ++hh) {
+        float acc = 0.f;
+        for (int d = 0; d < D; ++d) acc += qs[hh * D + d] * load_elem<BF>(k, kr + d);
+        ps[lane * 65 + hh] = acc;
+      }
+    }
+    __syncthreads();
+    // per-head max and rescale (one lane per head)
+    for (int hh = lane; hh < G; hh += 64) {
+      float mt = -INFINITY;
+      for (int j = 0; j < 64; ++j) mt = fmaxf(mt, ps[j * 65 + hh]);
+      const float mn = fmaxf(ms[hh], mt);
+      al[hh] = exp2f(ms[hh] - mn);
+      float sum = 0.f;
+      for (int j = 0; j < 64; ++j) {
+        const float p = exp2f(ps[j * 65 + hh] - mn);
+        ps[j * 65 + hh] = p;
+        sum += p;
+      }
+      ls[hh] = ls[hh] * al[hh] + sum;
+      ms[hh] = mn;
+    }
+    __syncthreads();
+    // P.V, lanes over (head, d)
+    for (int e = lane; e < GD; e += 64) {
+      const int hh = e / D, d = e - hh * D;
+      float acc = os[e] * al[hh];
+      for (int j = 0; j < 64; ++j) {
+        const int kk = keys[j];
+        if (kk >= 0) acc += ps[j * 65 + hh] * load_elem<BF>(v, kvoff + (int64_t)kk * stride + d);
+      }
+      os[e] = acc;
+    }
+    __syncthreads();
+  }
+
+  for (int e = lane; e < GD; e += 64) {
+    const int hh = e / D;
+    const float l = ls[hh];
+    const float o = l > 0.f ? os[e] / l : 0.f;
+    if constexpr (BF) reinterpret_cast<uint16_t*>(out)[qoff + e] = (uint16_t)f32_to_bf16_bits(o);
+    else reinterpret_cast<float*>(out)[qoff + e] = o;
+  }
+  if (lse)
+    for (int hh = lane; hh < G; hh += 64) {
+      const float l = ls[hh];
+      lse[((int64_t)b * Hq + (int64_t)g * G + hh) * T + t] =
+          l > 0.f ? (ms[hh] + __log2f(l)) * kLn2 : -INFINITY;
+    }
+}
+
+hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                                  int B, int T, int Hq, int Hkv, int D, int topk, int window,
+                                  float scale, bool bf16, void* out, float* lse, hipStream_t st) {
+  const int G = Hq / Hkv;
+  const float sl2 = scale * kLog2e;
+  const dim3 grid((unsigned)xcd_grid((int64_t)B * T * Hkv));
+  const dim3 block(64);
+  if (bf16 && G <= 16) {
+    if (D == 128)
+      hipLaunchKernelGGL(sparse_attn_mfma<128>, grid, block, 0, st, (const uint16_t*)q,
+                         (const uint16_t*)k, (const uint16_t*)v, idx, B, T, Hq, Hkv, topk, window,
+                         sl2, (uint16_t*)out, lse);
+    else
+      hipLaunchKernelGGL(sparse_attn_mfma<64>, grid, block, 0, st, (const uint16_t*)q,
+                         (const uint16_t*)k, (const uint16_t*)v, idx, B, T, Hq, Hkv, topk, window,
+                         sl2, (uint16_t*)out, lse);
+  } else if (bf16) {
+    if (D == 128)
+      hipLaunchKernelGGL((sparse_attn_valu<128, true>), grid, block, 0, st, q, k, v, idx, B, T, Hq,
+                         Hkv, topk, window, sl2, out, lse);
+    else
+      hipLaunchKernelGGL((sparse_attn_valu<64, true>), grid, block, 0, st, q, k, v, idx, B, T, Hq,
+                         Hkv, topk, window, sl2, out, lse);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((sparse_attn_valu<128, false>), grid, block, 0, st, q, k, v, idx, B, T,
+                         Hq, Hkv, topk, window, sl2, out, lse);
+    else
+      hipLaunchKernelGGL((sparse_attn_valu<64, false>), grid, block, 0, st, q, k, v, idx, B, T, Hq,
+                         Hkv, topk, window, sl2, out, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

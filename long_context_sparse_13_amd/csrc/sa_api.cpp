@@ -1,0 +1,259 @@
+// C ABI of libsa: argument validation, kernel selection and launch on the caller's
+// stream.  Validation runs entirely on the host before any HIP call, so an invalid
+// request never touches the GPU.  See include/sa.h for the contract of each entry point.
+#include "../../include/sa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                 \
+  do {                                                     \
+    if (!(cond)) return fail(SA_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+#define REQUIRE_PTR(p)                                                        \
+  do {                                                                        \
+    if (!(p)) return fail(SA_ERR_INVALID_ARG, "%s is NULL", #p);              \
+    if (!aligned16(p)) return fail(SA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define SUPPORT(cond, ...)                                 \
+  do {                                                     \
+    if (!(cond)) return fail(SA_ERR_UNSUPPORTED, __VA_ARGS__); \
+  } while (0)
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxElems = (int64_t)1 << 46;  // sanity bound on tensor sizes
+
+}  // namespace
+
+extern "C" {
+
+int sa_version(void) { return SA_VERSION; }
+
+const char* sa_status_str(int status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARG: return "SA_ERR_INVALID_ARG";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+    case SA_ERR_INTERNAL: return "SA_ERR_INTERNAL";
+    default: return "SA_ERR_UNKNOWN";
+  }
+}
+
+const char* sa_last_error(void) { return g_err; }
+
+int sa_indexer_scores(const void* qi, const void* ki, const float* w, int B, int T, int H_I,
+                      int D_I, int dtype, int row_begin, int row_end, float* scores, int64_t ld,
+                      void* stream) {
+  try {
+    REQUIRE_PTR(qi);
+    REQUIRE_PTR(ki);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(scores);
+    REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(H_I >= 1 && H_I <= 64, "H_I must be in [1, 64] (got %d)", H_I);
+    REQUIRE(D_I >= 8 && D_I <= 256 && D_I % 8 == 0, "D_I must be a multiple of 8 in [8, 256] (got %d)", D_I);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(0 <= row_begin && row_begin < row_end && row_end <= T,
+            "need 0 <= row_begin < row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
+    REQUIRE(ld >= row_end && ld % 4 == 0, "ld must be >= row_end and a multiple of 4 (got %lld)",
+            (long long)ld);
+    REQUIRE((int64_t)B * (row_end - row_begin) * ld <= kMaxElems, "scores buffer too large");
+    REQUIRE(B <= 65535, "B must be <= 65535 (got %d)", B);
+    SUPPORT(H_I * D_I <= 4096, "H_I * D_I must be <= 4096 (got %d)", H_I * D_I);
+    return hip_status(sa::launch_indexer_scores(qi, ki, w, B, T, H_I, D_I, dtype == SA_BF16,
+                                                row_begin, row_end, scores, ld, as_stream(stream)),
+                      "sa_indexer_scores launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_indexer_scores: unexpected exception");
+  }
+}
+
+int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin, int row_end,
+                   int k, int32_t* idx, void* stream) {
+  try {
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(idx);
+    REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(0 <= row_begin && row_begin < row_end && row_end <= T,
+            "need 0 <= row_begin < row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
+    REQUIRE(ld >= row_end, "ld must be >= row_end (got %lld)", (long long)ld);
+    REQUIRE(k >= 1 && k <= 4096, "k must be in [1, 4096] (got %d)", k);
+    REQUIRE((int64_t)B * (row_end - row_begin) <= 0x7fffffff, "too many rows in one call");
+    SUPPORT(row_end <= 262144, "rows longer than 262144 are not supported (row_end=%d)", row_end);
+    return hip_status(sa::launch_topk_select(scores, ld, B, T, row_begin, row_end, k, idx,
+                                             as_stream(stream)),
+                      "sa_topk_select launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_topk_select: unexpected exception");
+  }
+}
+
+int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                       int T, int Hq, int Hkv, int D, int topk, int window, float scale,
+                       int dtype, void* out, float* lse, void* stream) {
+  try {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
+    REQUIRE(topk >= 0 && window >= 0 && topk + window >= 1,
+            "need topk >= 0, window >= 0 and topk + window >= 1 (topk=%d window=%d)", topk, window);
+    REQUIRE(topk == 0 || idx, "idx is NULL with topk=%d", topk);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * T * Hq * D <= kMaxElems, "tensors too large");
+    REQUIRE(((int64_t)B * T * Hkv + 7) / 8 * 8 <= 0x7fffffffLL, "too many (token, KV head) items");
+    SUPPORT(D == 64 || D == 128, "head dim D=%d is not supported (64, 128)", D);
+    const int G = Hq / Hkv;
+    SUPPORT(G <= 64 && G * D <= 4096, "Hq/Hkv=%d with D=%d is not supported", G, D);
+    if (lse) REQUIRE(aligned16(lse), "lse is not 16-byte aligned");
+    if (idx) REQUIRE(aligned16(idx), "idx is not 16-byte aligned");
+    return hip_status(sa::launch_sparse_attn_fwd(q, k, v, idx, B, T, Hq, Hkv, D, topk, window,
+                                                 scale, dtype == SA_BF16, out, lse,
+                                                 as_stream(stream)),
+                      "sa_sparse_attn_fwd launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_sparse_attn_fwd: unexpected exception");
+  }
+}
+
+int sa_graph_attn_fwd(const void* cq, const void* ck, const void* v, const float* bias,
+                      float tau, int B, int T, int H, int D, int local, int n_pow2, int dtype,
+                      void* out, float* lse, void* stream) {
+  try {
+    REQUIRE(cq && ck, "cq/ck is NULL");
+    REQUIRE_PTR(v);
+    REQUIRE(bias, "bias is NULL");
+    REQUIRE_PTR(out);
+    REQUIRE(B >= 1 && T >= 1 && H >= 1, "B, T and H must be >= 1 (B=%d T=%d H=%d)", B, T, H);
+    REQUIRE(D >= 8 && D % 8 == 0, "D must be a positive multiple of 8 (got %d)", D);
+    REQUIRE(local >= 0 && local <= 64, "local must be in [0, 64] (got %d)", local);
+    REQUIRE(n_pow2 >= 0 && n_pow2 <= 30, "n_pow2 must be in [0, 30] (got %d)", n_pow2);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * T * H * D <= kMaxElems, "tensors too large");
+    SUPPORT(H * D <= 4096, "H * D must be <= 4096 (got %d)", H * D);
+    REQUIRE(((int64_t)B * T * ((H * D / 8 + 63) / 64) + 7) / 8 * 8 <= 0x7fffffffLL, "too many tokens");
+    return hip_status(sa::launch_graph_attn_fwd(cq, ck, v, bias, tau, B, T, H, D, local, n_pow2,
+                                                dtype == SA_BF16, out, lse, as_stream(stream)),
+                      "sa_graph_attn_fwd launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_graph_attn_fwd: unexpected exception");
+  }
+}
+
+int sa_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, int Hkv, int D,
+                      int block, int dtype, float* kbar, void* stream) {
+  try {
+    REQUIRE_PTR(kcache);
+    REQUIRE(lens, "lens is NULL");
+    REQUIRE_PTR(kbar);
+    REQUIRE(B >= 1 && Lmax >= 1 && Hkv >= 1, "B, Lmax and Hkv must be >= 1");
+    REQUIRE(D >= 4 && D % 4 == 0, "D must be a positive multiple of 4 (got %d)", D);
+    REQUIRE(block == 16 || block == 32 || block == 64 || block == 128,
+            "block must be 16, 32, 64 or 128 (got %d)", block);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
+    return hip_status(sa::launch_block_meanpool(kcache, lens, B, Lmax, Hkv, D, block,
+                                                dtype == SA_BF16, kbar, as_stream(stream)),
+                      "sa_block_meanpool launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_block_meanpool: unexpected exception");
+  }
+}
+
+static int decode_check_sizes(int B, int Lmax, int Hq, int Hkv, int D, int block, int top_blocks,
+                              int window, int n_splits) {
+  REQUIRE(B >= 1 && Lmax >= 1, "B and Lmax must be >= 1 (B=%d Lmax=%d)", B, Lmax);
+  REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
+  REQUIRE(block == 16 || block == 32 || block == 64 || block == 128,
+          "block must be 16, 32, 64 or 128 (got %d)", block);
+  REQUIRE(top_blocks >= 1 && top_blocks <= 64, "top_blocks must be in [1, 64] (got %d)", top_blocks);
+  REQUIRE(window >= 0, "window must be >= 0 (got %d)", window);
+  REQUIRE(n_splits >= 0 && n_splits <= 64, "n_splits must be in [0, 64] (got %d)", n_splits);
+  REQUIRE((int64_t)B * Hkv <= 65535, "B * Hkv must be <= 65535");
+  SUPPORT(D == 64 || D == 128, "head dim D=%d is not supported (64, 128)", D);
+  SUPPORT(Hq / Hkv <= 16, "Hq/Hkv=%d is not supported by the decode kernel (<= 16)", Hq / Hkv);
+  SUPPORT(Lmax / block <= 262144, "too many blocks per sequence");
+  return SA_OK;
+}
+
+size_t sa_sparse_decode_workspace(int B, int Lmax, int Hq, int Hkv, int D, int block,
+                                  int top_blocks, int window, int n_splits) {
+  if (decode_check_sizes(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits) != SA_OK)
+    return 0;
+  const int ns = n_splits ? n_splits : sa::decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window);
+  return sa::decode_workspace_bytes(B, Lmax, Hq, Hkv, D, block, top_blocks, ns);
+}
+
+int sa_sparse_decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_blocks, int window) {
+  if (B < 1 || Lmax < 1 || Hkv < 1 || block < 1 || top_blocks < 1 || window < 0) return 0;
+  return sa::decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window);
+}
+
+int sa_sparse_decode(const void* q, const void* kcache, const void* vcache, const float* kbar,
+                     const int32_t* lens, int B, int Lmax, int Hq, int Hkv, int D, int block,
+                     int top_blocks, int window, int n_splits, float scale, int dtype, void* out,
+                     float* lse, int32_t* sel_blocks, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  try {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(kcache);
+    REQUIRE_PTR(vcache);
+    REQUIRE_PTR(kbar);
+    REQUIRE(lens, "lens is NULL");
+    REQUIRE_PTR(out);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    const int rc = decode_check_sizes(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits);
+    if (rc != SA_OK) return rc;
+    SUPPORT(dtype == SA_BF16, "sa_sparse_decode supports bf16 only");
+    REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
+    const int ns = n_splits ? n_splits : sa::decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window);
+    const size_t need = sa::decode_workspace_bytes(B, Lmax, Hq, Hkv, D, block, top_blocks, ns);
+    if (!workspace || !aligned16(workspace))
+      return fail(SA_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+    if (ws_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+    const sa::DecodeWs ws = sa::decode_workspace_carve(workspace, B, Lmax, Hq, Hkv, D, block, top_blocks, ns);
+    return hip_status(sa::launch_sparse_decode(q, kcache, vcache, kbar, lens, B, Lmax, Hq, Hkv, D,
+                                               block, top_blocks, window, ns, scale, out, lse,
+                                               sel_blocks, ws, as_stream(stream)),
+                      "sa_sparse_decode launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_sparse_decode: unexpected exception");
+  }
+}
+
+}  // extern "C"

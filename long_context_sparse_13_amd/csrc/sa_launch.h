@@ -1,0 +1,48 @@
+// Internal launchers: host functions in the kernel translation units, called by the
+// C ABI layer (sa_api.cpp) after it has validated every argument.  Each returns the
+// hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+hipError_t launch_indexer_scores(const void* qi, const void* ki, const float* w, int B, int T,
+                                 int H_I, int D_I, bool bf16, int row_begin, int row_end,
+                                 float* scores, int64_t ld, hipStream_t st);
+
+hipError_t launch_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
+                              int row_end, int k, int32_t* idx, hipStream_t st);
+
+hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                                  int B, int T, int Hq, int Hkv, int D, int topk, int window,
+                                  float scale, bool bf16, void* out, float* lse, hipStream_t st);
+
+hipError_t launch_graph_attn_fwd(const void* cq, const void* ck, const void* v, const float* bias,
+                                 float tau, int B, int T, int H, int D, int local, int n_pow2,
+                                 bool bf16, void* out, float* lse, hipStream_t st);
+
+hipError_t launch_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, int Hkv,
+                                 int D, int block, bool bf16, float* kbar, hipStream_t st);
+
+struct DecodeWs {
+  float* block_scores;   // [B, Hkv, nblk]
+  int32_t* sel;          // [B, Hkv, top_blocks]
+  float* partials;       // [B, Hkv, n_splits, G, D + 4]  (o[D], m, l, pad)
+  uint32_t* counters;    // [B * Hkv] selection counters, then [B * Hkv] merge counters
+};
+size_t decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int D, int block, int top_blocks,
+                              int n_splits);
+int decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_blocks, int window);
+DecodeWs decode_workspace_carve(void* ws, int B, int Lmax, int Hq, int Hkv, int D, int block,
+                                int top_blocks, int n_splits);
+
+hipError_t launch_sparse_decode(const void* q, const void* kcache, const void* vcache,
+                                const float* kbar, const int32_t* lens, int B, int Lmax, int Hq,
+                                int Hkv, int D, int block, int top_blocks, int window,
+                                int n_splits, float scale, void* out, float* lse,
+                                int32_t* sel_out, const DecodeWs& ws, hipStream_t st);
+
+}  // namespace sa

@@ -1,0 +1,49 @@
+"""sa_graph_attn_fwd against the oracle (GPU)."""
+
+import numpy as np
+import pytest
+
+import oracle.reference as orc
+import sa_synth
+import long_context_sparse_13_amd as sa
+from tests.gpu_util import BF16_TOL, F32_TOL, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(seed, B, T, H, D, dtype, tau, local, n_pow2, rows=None):
+    note(f"graph seed={seed} B={B} T={T} H={H} D={D} {dtype} tau={tau} local={local} n_pow2={n_pow2}")
+    x = sa_synth.graph_inputs(seed, B, T, H, D, dtype)
+    out, lse = sa.sa_graph_attn_fwd(dev(x["cq"], dtype), dev(x["ck"], dtype), dev(x["v"], dtype),
+                                    dev(x["bias"], "f32"), tau, local, n_pow2, return_lse=True)
+    rows = list(range(T)) if rows is None else rows
+    O, L = orc.graph_attn(x["cq"], x["ck"], x["v"], x["bias"], tau, local, n_pow2, rows)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    err = np.abs(host(out)[:, rows] - O).max()
+    lerr = np.abs(host(lse)[:, :, rows] - L).max()
+    assert err <= tol, err
+    assert lerr <= 1e-3, lerr
+
+
+def test_small_bf16_and_f32():
+    _run(501, 2, 300, 8, 64, "bf16", 1.0, 32, 14)
+    _run(502, 1, 200, 3, 32, "f32", 0.7, 5, 9)
+
+
+def test_degenerate_graphs():
+    _run(503, 1, 50, 2, 64, "bf16", 1.0, 0, 0)     # self only: out = v
+    _run(504, 1, 70, 2, 64, "bf16", 0.0, 3, 4)     # tau = 0: plain mean over N(t)
+    _run(505, 1, 1, 8, 64, "bf16", 1.0, 32, 14)    # one token
+
+
+def test_wide_heads():
+    _run(506, 1, 100, 16, 128, "bf16", 1.0, 32, 14)   # H*D = 2048: 4 chunk groups per token
+
+
+@pytest.mark.slow
+def test_graph_workload_16k_sampled():
+    p = sa_synth.WORKLOADS[2].params
+    g = sa_synth.rng(88)
+    rows = sorted(set(list(range(0, 40)) + g.integers(40, p["T"], size=60).tolist()
+                      + [8192, 8193, p["T"] - 1]))
+    _run(1002, 1, p["T"], p["H"], p["D"], "bf16", p["tau"], p["local"], p["n_pow2"], rows)

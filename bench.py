@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Throughput of causal sparse attention on one MI355X.
+
+One step = the whole DSA-style prefill hot path on the 64K workload (T = 65,536 tokens,
+16 query heads on 1 KV head of dim 128, bf16; indexer of 4 heads x 64; top-2048 per query
+united with a 128-token window): sa_indexer_scores + sa_topk_select over row chunks, then
+sa_sparse_attn_fwd.  Inputs are seeded synthetic tensors (sa_synth), resident in HBM
+before the timed region.  ``value`` is query tokens per second of the whole step.
+
+The JSON line also carries the roofline of the dominant kernel (sparse attention; bytes
+gathered per launch / its average HIP-event duration / 8 TB/s), the float64 CPU oracle
+timed on a bounded row sample, and the other hot-path rows: fixed-graph attention (16K),
+block-sparse decode (32 x 128K) and cross-layer index reuse (128K, F,S,S,S).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk ROWS] [--no-extra]
+       [--no-cpu] [--only attn|prefill]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=8192, help="indexer/top-k rows per chunk")
+    ap.add_argument("--no-extra", action="store_true", help="skip graph/decode/reuse rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["attn", "prefill"], default=None,
+                    help="time only one part (for profiling runs)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every sa_* call launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.setdefault(name, []).append((e0, e1))
+
+    def ms(self, name):
+        ps = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in ps), len(ps)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        print("bench.py: multi-GPU runs are not part of this build (one GPU per box); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_sparse_13_amd as sa
+    import sa_synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    sa.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        t = t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)
+        return t.to(dev)
+
+    W3 = sa_synth.WORKLOADS[3]
+    p = W3.params
+    T, Hq, Hkv, D, HI, DI = p["T"], p["Hq"], p["Hkv"], p["D"], p["H_I"], p["D_I"]
+    topk, window, scale = p["topk"], p["window"], p["scale"]
+    log(f"generating the 64K prefill inputs (seed {W3.seed})")
+    x = sa_synth.prefill_inputs(W3.seed, 1, T, Hq, Hkv, D, HI, DI, "bf16")
+    qi, ki, w = to_dev(x["qi"], "bf16"), to_dev(x["ki"], "bf16"), to_dev(x["w"], "f32")
+    q, k, v = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16")
+    chunk = min(args.chunk, T)
+    ld = ((T + 3) // 4) * 4
+    scores = torch.empty((1, chunk, ld), dtype=torch.float32, device=dev)
+    idx = torch.full((1, T, topk), -1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    tm = Timer(torch)
+
+    def prefill_indices(timer):
+        for r0 in range(0, T, chunk):
+            r1 = min(T, r0 + chunk)
+            timer.run("indexer", lambda: sa.sa_indexer_scores(qi, ki, w, r0, r1, scores, ld))
+            timer.run("topk", lambda: sa.sa_topk_select(scores, topk, T, r0, r1, idx, ld))
+
+    def step(timer):
+        if args.only != "attn":
+            prefill_indices(timer)
+        if args.only != "prefill":
+            timer.run("attn", lambda: sa.sa_sparse_attn_fwd(q, k, v, idx, window, scale, out=out))
+
+    if args.only == "attn":
+        prefill_indices(Timer(torch))
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(Timer(torch))
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(tm)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    kern = {n: tm.ms(n) for n in ("indexer", "topk", "attn")}
+    log("timed: " + ", ".join(f"{n} {m / max(1, args.steps):.3f} ms/step ({c} launches)"
+                              for n, (m, c) in kern.items()))
+
+    # ---- algorithmic work of the attention launch (exact |S_t| from the indices)
+    tt = torch.arange(T, device=dev, dtype=torch.int32)[:, None]
+    listed = ((idx[0] >= 0) & (idx[0] <= tt - window)).sum(dim=1, dtype=torch.int64)
+    win = torch.clamp(torch.arange(T, device=dev) + 1, max=window)
+    n_sel = int((listed + win).sum().item())
+    bytes_kv = n_sel * 2 * D * 2                       # K and V rows, fetched once per group
+    bytes_qo = T * Hq * D * 2 * 2                      # Q read, O written
+    bytes_idx = T * topk * 4
+    attn_bytes = bytes_kv + bytes_qo + bytes_idx
+    attn_flops = 4.0 * Hq * D * n_sel
+    attn_ms, attn_n = kern["attn"]
+    attn_avg_ms = attn_ms / max(1, attn_n)
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9 if attn_n else None
+
+    idx_ms = kern["indexer"][0] / args.steps
+    topk_ms = kern["topk"][0] / args.steps
+    n_pairs = T * (T + 1) // 2
+    res = {
+        "metric": "sparse-attn fwd query-tokens/s at 64K ctx, top-k=2048; % HBM/MFMA roofline",
+        "value": T / (ms_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 tensors, indexer weights U(0,1))",
+        "config": {"workload": "dsa-prefill-bf16-64k: indexer(4x64) + top-2048 + window-128 "
+                               "sparse attention, T=65536, Hq=16, Hkv=1, D=128, batch 1",
+                   "global_batch": 1, "seq_len": T, "parallelism": "none (1 GPU)",
+                   "row_chunk": chunk, "only": args.only},
+        "step_breakdown_ms": {"indexer": idx_ms, "topk": topk_ms, "sparse_attn": attn_avg_ms},
+        "sparse_attn_query_tokens_per_s": T / (attn_avg_ms * 1e-3) if attn_n else None,
+        "roofline": {
+            "kernel": "sparse_attn_mfma<128>",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "selected_keys_per_launch": n_sel,
+            "avg_launch_ms": attn_avg_ms,
+            "mfma_tflops": attn_flops / (attn_avg_ms * 1e-3) / 1e12 if attn_n else None,
+        },
+        "indexer": {
+            "avg_ms_per_step": idx_ms,
+            "tflops": (n_pairs * 2 * HI * DI) / (idx_ms * 1e-3) / 1e12 if idx_ms else None,
+            "mfma_frac": ((n_pairs * 2 * HI * DI) / (idx_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+            if idx_ms else None,
+            "score_write_GBps": n_pairs * 4 / (idx_ms * 1e-3) / 1e9 if idx_ms else None,
+        },
+        "topk": {
+            "avg_ms_per_step": topk_ms,
+            "score_read_GBps": n_pairs * 4 / (topk_ms * 1e-3) / 1e9 if topk_ms else None,
+        },
+        "context_figures_from_pages": {
+            "SpatialLM-Mini": "2.47x training speedup at 16,384 tokens, RTX 3050 8 GB",
+            "IndexCache": "prefill 19.5 s -> 10.7 s at 200K tokens, GLM-4.7 Flash",
+            "NSA": "9x forward speedup at 64K, NVIDIA GPUs",
+        },
+    }
+    del scores
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        res["rows"] = extra_rows(torch, np, sa, sa_synth, to_dev, args, q, k, v, idx)
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(np, sa_synth, x, p, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
+    dev = q64.device
+    rows = {}
+    reps = 20
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # ---- fixed-graph distance attention, 16K
+    W2 = sa_synth.WORKLOADS[2]
+    p = W2.params
+    log("graph attention (16K)")
+    g = sa_synth.graph_inputs(W2.seed, 1, p["T"], p["H"], p["D"], "bf16")
+    cq, ck, vg, bias = (to_dev(g["cq"], "bf16"), to_dev(g["ck"], "bf16"), to_dev(g["v"], "bf16"),
+                        to_dev(g["bias"], "f32"))
+    og = torch.empty_like(vg)
+    ms = timed(lambda: sa.sa_graph_attn_fwd(cq, ck, vg, bias, p["tau"], p["local"], p["n_pow2"],
+                                            out=og), reps)
+    T2, H2, D2 = p["T"], p["H"], p["D"]
+    edges = sum(min(t, 32) + 1 + sum(1 for j in range(6, 14) if (1 << j) <= t) for t in range(T2))
+    comp = T2 * H2 * (2 * D2 * 2 + 2 * 3 * 2)
+    rows["graph_attn_16k"] = {
+        "ms": ms, "query_tokens_per_s": T2 / (ms * 1e-3),
+        "compulsory_bytes": comp, "compulsory_GBps": comp / (ms * 1e-3) / 1e9,
+        "edge_bytes": edges * H2 * (D2 * 2 + 6), "edge_GBps": edges * H2 * (D2 * 2 + 6) / (ms * 1e-3) / 1e9,
+        "hbm_frac_compulsory": comp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+    del cq, ck, vg, bias, og
+
+    # ---- block-sparse decode, 32 x 128K
+    W5 = sa_synth.WORKLOADS[5]
+    p = W5.params
+    log("block-sparse decode (32 x 128K): generating caches")
+    dx = sa_synth.decode_inputs(W5.seed, p["B"], p["L"], p["Hq"], p["Hkv"], p["D"], "bf16")
+    qd = to_dev(dx["q"], "bf16")
+    kc = to_dev(dx["kcache"], "bf16")
+    vc = to_dev(dx["vcache"], "bf16")
+    del dx
+    lens = torch.full((p["B"],), p["L"], dtype=torch.int32, device=dev)
+    t_pool = timed(lambda: sa.sa_block_meanpool(kc, lens, p["block"]), 3)
+    kbar = sa.sa_block_meanpool(kc, lens, p["block"])
+    need = sa.sa_sparse_decode_workspace(p["B"], p["L"], p["Hq"], p["Hkv"], p["D"], p["block"],
+                                         p["top_blocks"], p["window"], 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    od = torch.empty_like(qd)
+    ms = timed(lambda: sa.sa_sparse_decode(qd, kc, vc, kbar, lens, p["block"], p["top_blocks"],
+                                           p["window"], p["scale"], workspace=ws, out=od), 50)
+    _, sel = sa.sa_sparse_decode(qd, kc, vc, kbar, lens, p["block"], p["top_blocks"], p["window"],
+                                 p["scale"], workspace=ws, return_sel=True)
+    wstart = p["L"] - p["window"]
+    sel_h = sel.cpu().numpy()
+    u_tok = 0
+    for b in range(p["B"]):
+        for j in sel_h[b, 0]:
+            if j >= 0:
+                u_tok += max(0, min(p["block"], wstart - int(j) * p["block"]))
+        u_tok += p["window"]
+    nb = p["L"] // p["block"]
+    dbytes = p["B"] * nb * p["D"] * 4 + u_tok * 2 * p["D"] * 2 + p["B"] * p["Hq"] * p["D"] * 2 * 2
+    rows["sparse_decode_b32_128k"] = {
+        "us_per_step": ms * 1e3, "tokens_per_s": p["B"] / (ms * 1e-3),
+        "algorithmic_bytes_per_step": dbytes, "achieved_GBps": dbytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "n_splits": sa.sa_sparse_decode_auto_splits(p["B"], p["L"], p["Hkv"], p["block"],
+                                                    p["top_blocks"], p["window"]),
+        "meanpool_ms_once_per_cache": t_pool,
+    }
+    del qd, kc, vc, kbar, ws, od
+    torch.cuda.empty_cache()
+
+    # ---- cross-layer index reuse, 128K, F,S,S,S
+    W4 = sa_synth.WORKLOADS[4]
+    p = W4.params
+    T = p["T"]
+    log("index reuse F,S,S,S (128K): generating inputs")
+    xi = sa_synth.indexer_inputs(W4.seed, 1, T, p["H_I"], p["D_I"], "bf16")
+    qi, ki, w = to_dev(xi["qi"], "bf16"), to_dev(xi["ki"], "bf16"), to_dev(xi["w"], "f32")
+    layers = []
+    for l in range(4):
+        lx = sa_synth.attn_inputs(sa_synth.layer_seed(l), 1, T, p["Hq"], p["Hkv"], p["D"], "bf16")
+        layers.append(tuple(to_dev(lx[n], "bf16") for n in ("q", "k", "v")))
+        del lx
+    chunk = 8192
+    ld = T
+    sc = torch.empty((1, chunk, ld), dtype=torch.float32, device=dev)
+    idx = torch.full((1, T, p["topk"]), -1, dtype=torch.int32, device=dev)
+    o4 = torch.empty_like(layers[0][0])
+
+    def index_once():
+        for r0 in range(0, T, chunk):
+            r1 = min(T, r0 + chunk)
+            sa.sa_indexer_scores(qi, ki, w, r0, r1, sc, ld)
+            sa.sa_topk_select(sc, p["topk"], T, r0, r1, idx, ld)
+
+    def attn(l):
+        qq, kk, vv = layers[l]
+        sa.sa_sparse_attn_fwd(qq, kk, vv, idx, p["window"], p["scale"], out=o4)
+
+    t_index = timed(index_once, 2)
+    t_attn = [timed(lambda l=l: attn(l), 3) for l in range(4)]
+    reuse = t_index + sum(t_attn)
+    no_reuse = 4 * t_index + sum(t_attn)
+    rows["indexcache_FSSS_128k"] = {
+        "index_ms": t_index, "attn_ms_per_layer": t_attn,
+        "four_layers_ms_with_reuse": reuse, "four_layers_ms_indexing_every_layer": no_reuse,
+        "indexer_time_saved_ms": 3 * t_index, "saved_frac": 3 * t_index / no_reuse,
+        "attn_query_tokens_per_s": T / (sum(t_attn) / 4 * 1e-3),
+    }
+    del sc, idx, layers, qi, ki, w, o4
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(np, sa_synth, x, p, seconds):
+    """The float64 oracle, as it stands, on a bounded sample of the 64K workload: rows
+    drawn uniformly from [k + W, T), each through indexer scores, exact top-k and
+    dense-masked attention.  Scaled to query tokens per second."""
+    import oracle.reference as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    T, k, W = p["T"], p["topk"], p["window"]
+    g = sa_synth.rng(4242)
+    done = 0
+    idx = np.full((1, T, k), -1, np.int32)
+    t0 = time.perf_counter()
+    while True:
+        rows = sorted(g.integers(k + W, T, size=8).tolist())
+        for t in rows:
+            idx[0, t] = orc.topk_select_row(orc.indexer_scores_row(x["qi"], x["ki"], x["w"], 0, t), k)
+        orc.sparse_attn(x["q"], x["k"], x["v"], idx, W, p["scale"], rows)
+        done += len(rows)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} rows drawn uniformly from [k+W, T) of the 64K prefill workload "
+                      f"(indexer row + exact top-k + dense-masked float64 attention), {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -48,19 +48,23 @@ struct GroupAttn {
     l_run = 0.f;
   }
 
-  // One step over 32 keys.  Every lane passes `key` = the key of slot (lane & 31)
-  // (any in-bounds row index when that slot is invalid) and the 32-bit slot mask `vm`
-  // (bit i set = slot i attended; vm != 0).  kbase/vbase point at row 0 of this KV head,
-  // `stride` is the element distance between consecutive rows.  `vl` is this wave's LDS
-  // staging area of LDS_BYTES.
-  __device__ __forceinline__ void step(const uint16_t* __restrict__ kbase,
-                                       const uint16_t* __restrict__ vbase, int64_t stride,
-                                       int key, uint32_t vm, unsigned char* vl,
-                                       float scale_log2, int lane) {
-    const int n = lane & 15, grp = lane >> 4;
-
-    // ---- gather: K rows as MFMA A operands, V rows into LDS
+  // Registers of one gathered 32-key tile: K rows as MFMA A operands, V rows waiting to
+  // be staged in LDS, and the slot mask (bit i set = slot i attended).
+  struct Tile {
     u32x4 kA[2][KS];
+    u32x4 vw[CH / 2];
+    uint32_t vm;
+  };
+
+  // Issue the loads of one tile.  Every lane passes `key` = the key of slot (lane & 31)
+  // (any in-bounds row index when that slot is invalid) and the slot mask `vm`.
+  // kbase/vbase point at row 0 of this KV head; `stride` is the element distance between
+  // consecutive rows.
+  __device__ __forceinline__ void load(Tile& tl, const uint16_t* __restrict__ kbase,
+                                       const uint16_t* __restrict__ vbase, int64_t stride,
+                                       int key, uint32_t vm, int lane) const {
+    const int n = lane & 15, grp = lane >> 4;
+    tl.vm = vm;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int slot = c2 * 16 + n;
@@ -71,11 +75,10 @@ struct GroupAttn {
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 w = {0u, 0u, 0u, 0u};
         if (ok) w = ld16(kp + ks * 32);
-        kA[c2][ks] = w;
+        tl.kA[c2][ks] = w;
       }
     }
     constexpr int RPI = 64 / CH;  // rows per wave instruction
-    u32x4 vw[CH / 2];
 #pragma unroll
     for (int i = 0; i < CH / 2; ++i) {
       const int r = lane / CH + RPI * i;
@@ -83,8 +86,17 @@ struct GroupAttn {
       const int vr = shfl_i(key, r);
       u32x4 w = {0u, 0u, 0u, 0u};
       if ((vm >> r) & 1u) w = ld16(vbase + (int64_t)vr * stride + c * 8);
-      vw[i] = w;
+      tl.vw[i] = w;
     }
+  }
+
+  // Online-softmax update with one loaded tile (no-op for an empty mask).  `vl` is this
+  // wave's LDS staging area of LDS_BYTES.
+  __device__ __forceinline__ void compute(const Tile& tl, unsigned char* vl, float scale_log2,
+                                          int lane) {
+    const uint32_t vm = tl.vm;
+    if (vm == 0u) return;
+    const int n = lane & 15, grp = lane >> 4;
 
     // ---- S^T = K . Q^T for the two 16-key halves
     f32x4 s[2];
@@ -93,15 +105,16 @@ struct GroupAttn {
       s[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kA[c2][ks]), qB[ks], s[c2], 0, 0, 0);
+        s[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.kA[c2][ks]), qB[ks], s[c2], 0, 0, 0);
     }
 
     // stage V while the score MFMAs drain
+    constexpr int RPI = 64 / CH;
 #pragma unroll
     for (int i = 0; i < CH / 2; ++i) {
       const int r = lane / CH + RPI * i;
       const int c = lane % CH;
-      st16(vl + r * LROW + c * 16, vw[i]);
+      st16(vl + r * LROW + c * 16, tl.vw[i]);
     }
 
     // ---- online softmax (log2 domain); head n's max over the 4 lane groups
@@ -157,7 +170,56 @@ struct GroupAttn {
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), pB, acc[dt], 0, 0, 0);
     }
 
-    wave_lds_sync();  // the staging area may be overwritten by the next step
+    wave_lds_sync();  // the staging area may be overwritten by the next tile
+  }
+
+  // Streams `ntiles` tiles with the loads of tile i+1 in flight while tile i is
+  // computed.  fetch(i) returns this lane's raw key of tile i (it may issue a load, which
+  // is started two tiles ahead); finish(i, raw, key, vm) turns it into the slot key and
+  // the tile's slot mask.
+  // With PIPE = false one tile is loaded and computed at a time (half the registers, so
+  // twice the wavefronts per SIMD).
+  template <bool PIPE, typename Fetch, typename Finish>
+  __device__ __forceinline__ void run(int ntiles, Fetch&& fetch, Finish&& finish,
+                                      const uint16_t* __restrict__ kbase,
+                                      const uint16_t* __restrict__ vbase, int64_t stride,
+                                      unsigned char* vl, float scale_log2, int lane) {
+    if (ntiles <= 0) return;
+    if constexpr (!PIPE) {
+      Tile A;
+      int key;
+      uint32_t vm;
+      int r = fetch(0);
+      for (int i = 0; i < ntiles; ++i) {
+        finish(i, r, key, vm);
+        if (i + 1 < ntiles) r = fetch(i + 1);  // the next raw key is in flight meanwhile
+        if (vm == 0u) continue;
+        load(A, kbase, vbase, stride, key, vm, lane);
+        compute(A, vl, scale_log2, lane);
+      }
+      return;
+    }
+    Tile A, B;
+    int key;
+    uint32_t vm;
+    int r1 = ntiles > 1 ? fetch(1) : 0;
+    finish(0, fetch(0), key, vm);
+    load(A, kbase, vbase, stride, key, vm, lane);
+    for (int i = 0; i < ntiles; i += 2) {
+      const int r2 = i + 2 < ntiles ? fetch(i + 2) : 0;
+      if (i + 1 < ntiles) {
+        finish(i + 1, r1, key, vm);
+        load(B, kbase, vbase, stride, key, vm, lane);
+      }
+      compute(A, vl, scale_log2, lane);
+      if (i + 1 >= ntiles) break;
+      r1 = i + 3 < ntiles ? fetch(i + 3) : 0;
+      if (i + 2 < ntiles) {
+        finish(i + 2, r2, key, vm);
+        load(A, kbase, vbase, stride, key, vm, lane);
+      }
+      compute(B, vl, scale_log2, lane);
+    }
   }
 
   // Sum of the lane-partial l over the 4 lanes of head n.

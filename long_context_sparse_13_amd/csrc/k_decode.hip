@@ -9,13 +9,16 @@
 //
 // Kernels of one decode step (two launches):
 //  1. decode_block_scores: score_j = (sum_h q_h) . kbar_j for every complete block;
-//     the last workgroup of each (sequence, KV head) to finish (an atomic counter)
-//     selects the top blocks with the workgroup radix select of select.h.
-//  2. decode_split_attn: one wavefront per (sequence, KV head, split) attends the
-//     group's query heads to its slice of U = selected blocks' tokens before the window
-//     followed by the window, through GroupAttn (MFMA over the grouped heads); the last
-//     wavefront of each (sequence, KV head) merges the splits.
-// The counters return to zero at the end of every call.
+//     each workgroup hands on the exact top-16 of its blocks as candidates.
+//  2. decode_split_attn: one workgroup of 4 wavefronts per (sequence, KV head, split)
+//     selects the top blocks from the candidates; each wavefront attends the group's query heads to its sub-slice of U = selected
+//     blocks' tokens before the window followed by the window, through GroupAttn (MFMA
+//     over the grouped heads); the workgroup merges its wavefronts in LDS and the last
+//     workgroup of each (sequence, KV head) merges the splits.
+// The kernel boundary makes the candidates visible to kernel 2.  Inside kernel 2 the
+// split partials travel through agent-scope atomic stores/loads and one counter per
+// (sequence, KV head), avoiding a device-wide cache flush per workgroup.  The counters
+// return to zero at the end of every call.
 #include "attn_tile.h"
 #include "sa_launch.h"
 #include "select.h"
@@ -76,27 +79,43 @@ hipError_t launch_block_meanpool(const void* kcache, const int32_t* lens, int B,
 
 // ------------------------------------------------------------------------ workspace
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+static int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+constexpr int kScoreThreads = 256;
+constexpr int kScoreChunk = 256;   // blocks scored per workgroup pass (64 per wavefront)
+constexpr int kCandMax = 64;       // most candidates a scoring workgroup hands on
+constexpr int kMaxScoreWGs = 64;   // scoring workgroups per (sequence, KV head)
+constexpr int kSplitWaves = 4;     // wavefronts per split workgroup
+constexpr int kSplitGrain = kSplitWaves * 32;  // positions of U per split step
+
+// Scoring workgroups per (sequence, KV head) and blocks each one covers.
+static void score_grid(int nb, int& nwg, int& per_wg) {
+  const int chunks = (int)imax(1, (nb + kScoreChunk - 1) / kScoreChunk);
+  nwg = (int)imin(chunks, kMaxScoreWGs);
+  per_wg = ((chunks + nwg - 1) / nwg) * kScoreChunk;
+}
 
 size_t decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int D, int block, int top_blocks,
                               int n_splits) {
   const size_t bh = (size_t)B * Hkv;
-  const size_t nb = (size_t)(Lmax / block);
   const size_t G = (size_t)(Hq / Hkv);
-  return align256(bh * nb * 4) + align256(bh * top_blocks * 4) +
-         align256(bh * n_splits * G * (D + 4) * 4) + align256(bh * 2 * 4);
+  int nwg, per;
+  score_grid(Lmax / block, nwg, per);
+  return align256(bh * nwg * kCandMax * 8) + align256(bh * n_splits * G * (D + 4) * 4) +
+         align256(bh * 4);
 }
 
 DecodeWs decode_workspace_carve(void* ws, int B, int Lmax, int Hq, int Hkv, int D, int block,
                                 int top_blocks, int n_splits) {
   const size_t bh = (size_t)B * Hkv;
-  const size_t nb = (size_t)(Lmax / block);
   const size_t G = (size_t)(Hq / Hkv);
+  int nwg, per;
+  score_grid(Lmax / block, nwg, per);
   char* p = static_cast<char*>(ws);
   DecodeWs w;
-  w.block_scores = reinterpret_cast<float*>(p);
-  p += align256(bh * nb * 4);
-  w.sel = reinterpret_cast<int32_t*>(p);
-  p += align256(bh * top_blocks * 4);
+  w.cand = reinterpret_cast<uint32_t*>(p);
+  p += align256(bh * nwg * kCandMax * 8);
   w.partials = reinterpret_cast<float*>(p);
   p += align256(bh * n_splits * G * (D + 4) * 4);
   w.counters = reinterpret_cast<uint32_t*>(p);
@@ -104,9 +123,6 @@ DecodeWs decode_workspace_carve(void* ws, int B, int Lmax, int Hq, int Hkv, int 
 }
 
 // Largest |U|: every selected block fully before the window, plus the window.
-static int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
-static int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
-
 static int decode_u_max(int Lmax, int block, int top_blocks, int window) {
   const int64_t nb = Lmax / block;
   const int64_t u = imin(top_blocks, nb) * block + imin(window, Lmax);
@@ -114,26 +130,52 @@ static int decode_u_max(int Lmax, int block, int top_blocks, int window) {
 }
 
 int decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_blocks, int window) {
+  // one 32-key tile per wavefront (the step is latency-bound), up to ~8 waves per CU
   const int64_t umax = decode_u_max(Lmax, block, top_blocks, window);
-  const int64_t steps = imax(1, (umax + 31) / 32);           // 32-key steps of the whole U
-  const int64_t want = (512 + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);  // ~2 waves per CU
-  return (int)imax(1, imin(imin(want, steps), 64));
+  const int64_t steps = imax(1, (umax + kSplitGrain - 1) / kSplitGrain);
+  const int64_t cap = imax(1, (2048 / kSplitWaves) / ((int64_t)B * Hkv));
+  return (int)imax(1, imin(imin(steps, cap), 64));
+}
+
+// (order key, position) packed so that a larger value is a better entry: larger key, or
+// equal key and lower position.  0 marks an empty entry.
+__device__ __forceinline__ uint64_t pack_rank(uint32_t key, int pos) {
+  return pos < 0 ? 0ull : ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)pos);
+}
+__device__ __forceinline__ int unpack_pos(uint64_t c) { return (int)(0xffffffffu - (uint32_t)c); }
+
+// Exact top-m of n packed entries in LDS (n a multiple of 8, padded with 0): an entry's
+// rank is the number of entries better than it; entries with rank < m are handed to
+// keep(rank, entry).  All threads read the same LDS words (broadcast), 8 per step.
+template <int NT, typename Keep>
+__device__ __forceinline__ void rank_select(const uint64_t* comb, int n, int m, Keep&& keep) {
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint64_t ci = comb[i];
+    int rank = 0;
+    for (int j = 0; j < n; j += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rank += comb[j + u] > ci;
+    }
+    if (ci != 0ull && rank < m) keep(rank, ci);
+  }
 }
 
 // ------------------------------------------------------------------------ kernel 1
-constexpr int kScoreThreads = 256;
-constexpr int kScoreBlocksPerWG = 256;
-
+// score_j = (sum of the group's query heads) . kbar_j for this workgroup's blocks; the
+// workgroup hands on its own exact top-cpw (cpw = top_blocks rounded up to 8) as packed
+// (key, block) candidates.  Any block of the global top is in the top of its own
+// workgroup, so the candidates suffice.
 template <int D>
 __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
-    const int32_t* __restrict__ lens, int Lmax, int Hq, int Hkv, int block, int top_blocks,
-    float* __restrict__ bscore, int32_t* __restrict__ sel, int32_t* __restrict__ sel_out,
-    uint32_t* __restrict__ counters) {
-  __shared__ SelectShared<kScoreThreads> sh;
-  __shared__ int last;
-  constexpr int LPR = D / 4;        // lanes per kbar row (16 bytes each)
-  constexpr int RPI = 64 / LPR;     // rows per wave instruction
+    const int32_t* __restrict__ lens, int Lmax, int Hq, int Hkv, int block, int per_wg, int cpw,
+    uint32_t* __restrict__ cand) {
+  __shared__ uint64_t scomb[kScoreChunk + kCandMax];
+  __shared__ uint64_t best[kCandMax];
+  // a row (D floats) is read by 8 lanes, C = D/8 consecutive floats each; 8 rows per
+  // group of loads, 8 groups for the wave's 64 rows; rows are reduced with DPP
+  constexpr int C = D / 8;
+  constexpr int NL = C / 4;         // 16-byte loads per lane per row
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bg = blockIdx.x;        // (sequence, KV head)
   const int b = bg / Hkv, g = bg % Hkv;
@@ -141,75 +183,95 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
   const int nb = Lmax / block;
   const int L = min(max(lens[b], 0), Lmax);  // lengths outside [0, Lmax] are clamped
   const int nfull = L / block;
-  float* sc = bscore + (int64_t)bg * nb;
 
-  // (sum of the group's query heads) for this lane's 4 columns
-  const int d0 = (lane % LPR) * 4;
-  float qb[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int hh = 0; hh < G; ++hh) {
-    const u32x2 w = ld8(q + ((int64_t)b * Hq + g * G + hh) * D + d0);
-    qb[0] += bf16_lo(w[0]);
-    qb[1] += bf16_hi(w[0]);
-    qb[2] += bf16_lo(w[1]);
-    qb[3] += bf16_hi(w[1]);
+  const int d0 = (lane & 7) * C;
+  float qb[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) qb[i] = 0.f;
+  {
+    u32x4 w[16][C / 8];
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh)  // G <= 16: all head rows in flight at once
+#pragma unroll
+      for (int c = 0; c < C / 8; ++c)
+        w[hh][c] = hh < G ? ld16(q + ((int64_t)b * Hq + g * G + hh) * D + d0 + c * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh)
+#pragma unroll
+      for (int c = 0; c < C / 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qb[c * 8 + 2 * i] += bf16_lo(w[hh][c][i]);
+          qb[c * 8 + 2 * i + 1] += bf16_hi(w[hh][c][i]);
+        }
   }
-  const int j_lo = blockIdx.y * kScoreBlocksPerWG;
-  const int j_hi = min(j_lo + kScoreBlocksPerWG, nfull);
-  for (int j0 = j_lo + wv * RPI; j0 < j_hi; j0 += 4 * RPI) {
-    const int j = j0 + lane / LPR;
-    float part = 0.f;
-    if (j < j_hi) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(kbar + (((int64_t)b * nb + j) * Hkv + g) * D + d0);
-      part = a[0] * qb[0] + a[1] * qb[1] + a[2] * qb[2] + a[3] * qb[3];
+  if (tid < cpw) best[tid] = 0ull;
+  const int j_begin = blockIdx.y * per_wg;
+  const int j_end = min(j_begin + per_wg, nfull);
+  for (int c0 = j_begin; c0 < j_end; c0 += kScoreChunk) {
+    const int jw = c0 + wv * 64 + (lane >> 3);  // this lane's row in group 0
+    f32x4 a[8][NL];
+#pragma unroll
+    for (int gi = 0; gi < 8; ++gi) {  // all of the wave's rows in flight at once
+      const int j = jw + gi * 8;
+      const float* rp = kbar + (((int64_t)b * nb + (j < j_end ? j : 0)) * Hkv + g) * D + d0;
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        a[gi][l] = j < j_end ? *reinterpret_cast<const f32x4*>(rp + 4 * l) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-    if (j < j_hi && lane % LPR == 0) sc[j] = part;
-  }
-
-  // the last workgroup of this (sequence, KV head) selects
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = atomicAdd(&counters[bg], 1u) == gridDim.y - 1;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  int32_t* so = sel + (int64_t)bg * top_blocks;
-  int32_t* uo = sel_out ? sel_out + (int64_t)bg * top_blocks : nullptr;
-  if (nfull <= top_blocks) {
-    for (int i = tid; i < top_blocks; i += kScoreThreads) {
-      const int v = i < nfull ? i : -1;
-      so[i] = v;
-      if (uo) uo[i] = v;
+    for (int gi = 0; gi < 8; ++gi) {
+      float part = 0.f;
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += a[gi][l][i] * qb[4 * l + i];
+      part = sum8_dpp(part);
+      const int j = jw + gi * 8;
+      if ((lane & 7) == 0)
+        scomb[wv * 64 + gi * 8 + (lane >> 3)] = pack_rank(order_key(part), j < j_end ? j : -1);
     }
-  } else {
-    for (int i = tid; i < top_blocks; i += kScoreThreads) so[i] = -1;
+    if (tid < cpw) scomb[kScoreChunk + tid] = best[tid];  // running candidates compete
     __syncthreads();
-    wg_topk<kScoreThreads, 0>(
-        nfull, top_blocks, [&](int e) { return order_key(__builtin_nontemporal_load(sc + e)); },
-        [&](int pos, int e) {
-          so[pos] = e;
-          if (uo) uo[pos] = e;
-        },
-        sh);
+    rank_select<kScoreThreads>(scomb, kScoreChunk + cpw, cpw,
+                               [&](int rank, uint64_t c) { best[rank] = c; });
+    __syncthreads();
   }
-  if (tid == 0) counters[bg] = 0u;
+  if (tid < cpw)
+    reinterpret_cast<uint64_t*>(cand)[((int64_t)bg * gridDim.y + blockIdx.y) * cpw + tid] = best[tid];
 }
 
 // ------------------------------------------------------------------------ kernel 2
+// One workgroup of kSplitWaves wavefronts per (sequence, KV head, split).  It picks the
+// top blocks from the scoring candidates (every split does so identically), takes its
+// slice of U = selected blocks' tokens before the window followed by the window, gives one
+// sub-slice to each wavefront, merges the wavefronts' partial softmaxes in LDS and
+// publishes the split's partial.  The last split to finish (a counter) merges all splits
+// into the output.  Partials are written and read with agent-scope atomic accesses, which
+// go straight to the memory side, so no cache flush is needed between workgroups.
 template <int D>
-__global__ __launch_bounds__(64) void decode_split_attn(
+__global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ lens, int Lmax, int Hq,
-    int Hkv, int block, int top_blocks, int window, int n_splits, float scale_log2,
-    const int32_t* __restrict__ sel, float* __restrict__ partials, uint32_t* __restrict__ counters,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int Hkv, int block, int top_blocks, int window, int n_splits, int n_cand, float scale_log2,
+    const uint32_t* __restrict__ cand, float* __restrict__ partials,
+    uint32_t* __restrict__ counters, int32_t* __restrict__ sel_out, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
   using GA = GroupAttn<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char vl[GA::LDS_BYTES];
+  constexpr int PS = D + 4;  // floats per (split, head) partial: o[D], m, l, 2 pad
+  // per-wave staging area, also used for the wave's merge slot and (all of it) for the
+  // candidate list
+  constexpr int CAND_BYTES = kMaxScoreWGs * kCandMax * 8 + 64 * 4;
+  constexpr int STAGE = GA::LDS_BYTES * kSplitWaves >= CAND_BYTES
+                            ? GA::LDS_BYTES
+                            : (CAND_BYTES + kSplitWaves - 1) / kSplitWaves;
+  static_assert(16 * D * 4 + 2 * 16 * 4 <= STAGE, "merge area must fit the stage");
+  __shared__ __attribute__((aligned(16))) unsigned char vl[kSplitWaves][(STAGE + 15) / 16 * 16];
   __shared__ int pre[65];   // token offsets of the selected blocks inside U
-  __shared__ int blk[64];
+  __shared__ int blk[64];   // selected blocks, ascending
   __shared__ int last;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int bg = blockIdx.x;
   const int split = blockIdx.y;
@@ -217,107 +279,203 @@ __global__ __launch_bounds__(64) void decode_split_attn(
   const int G = Hq / Hkv;
   const int L = min(max(lens[b], 0), Lmax);
   const int wstart = max(0, L - window);
-
-  // tokens each selected block contributes before the window (blocks ascending)
-  {
-    int j = -1, cnt = 0;
-    if (lane < top_blocks) {
-      j = sel[(int64_t)bg * top_blocks + lane];
-      if (j >= 0) cnt = max(0, min(block, wstart - j * block));
-    }
-    int x = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane < top_blocks) {
-      pre[lane] = x - cnt;
-      blk[lane] = j;
-    }
-    if (lane == 63) pre[64] = x;  // lanes >= top_blocks add 0
-  }
-  __syncthreads();
-  const int nsel = pre[64];
-  const int U = nsel + (L - wstart);
-  const int per = ((U + n_splits - 1) / n_splits + 31) / 32 * 32;
-  const int u_lo = split * per;
-  const int u_hi = min(U, u_lo + per);
-
+  const int nfull = L / block;
+  const int nsel_blocks = min(top_blocks, nfull);
   const int h = g * G + n;
   const bool hv = n < G;
-  GA ga;
+  GA ga;  // the query rows are requested before the selection work
   ga.init(hv ? q + ((int64_t)b * Hq + h) * D : nullptr, grp);
+
+  // ---- top blocks from the candidates (by score), then ascending by block
+  {
+    uint64_t* cc = reinterpret_cast<uint64_t*>(&vl[0][0]);
+    int* rsel = reinterpret_cast<int*>(cc + n_cand);  // blocks in score order
+    const uint64_t* cb = reinterpret_cast<const uint64_t*>(cand) + (int64_t)bg * n_cand;
+    for (int i = tid; i < n_cand; i += 64 * kSplitWaves) cc[i] = cb[i];
+    __syncthreads();
+    rank_select<64 * kSplitWaves>(cc, n_cand, nsel_blocks,
+                                  [&](int rank, uint64_t c) { rsel[rank] = unpack_pos(c); });
+    __syncthreads();
+    if (tid < nsel_blocks) {  // ascending block order
+      const int v = rsel[tid];
+      int r = 0;
+#pragma unroll 8
+      for (int j = 0; j < nsel_blocks; ++j) r += rsel[j] < v;
+      blk[r] = v;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const int j = lane < nsel_blocks ? blk[lane] : -1;
+      const int cnt = j >= 0 ? max(0, min(block, wstart - j * block)) : 0;
+      int x = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane < top_blocks) pre[lane] = x - cnt;
+      if (lane == 63) pre[64] = x;
+      if (sel_out && split == 0 && lane < top_blocks)
+        sel_out[(int64_t)bg * top_blocks + lane] = j;
+    }
+    __syncthreads();
+  }
+  const int nsel = pre[64];
+  const int U = nsel + (L - wstart);
+  const int per = ((U + n_splits - 1) / n_splits + kSplitGrain - 1) / kSplitGrain * kSplitGrain;
+  const int wper = per / kSplitWaves;
+  const int u_lo = min(U, split * per + wv * wper);
+  const int u_hi = min(U, u_lo + wper);
+
   const int64_t stride = (int64_t)Hkv * D;
   const uint16_t* kbase = kc + ((int64_t)b * Lmax * Hkv + g) * D;
   const uint16_t* vbase = vc + ((int64_t)b * Lmax * Hkv + g) * D;
 
-  for (int u0 = u_lo; u0 < u_hi; u0 += 32) {
-    const int u = u0 + (lane & 31);
-    const bool ok = u < u_hi;
-    int key = 0;
-    if (ok) {
-      if (u < nsel) {
-        int i = 0;  // the selected block holding position u
-        while (i + 1 < top_blocks && pre[i + 1] <= u) ++i;
-        key = blk[i] * block + (u - pre[i]);
-      } else {
-        key = wstart + (u - nsel);
+  auto fetch = [&](int i) -> int {  // U position -> token
+    const int u = u_lo + i * 32 + (lane & 31);
+    if (u >= u_hi) return -1;
+    if (u >= nsel) return wstart + (u - nsel);
+    int lo = 0, hi = nsel_blocks - 1;  // last selected block with pre[.] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= u) lo = mid;
+      else hi = mid - 1;
+    }
+    return blk[lo] * block + (u - pre[lo]);
+  };
+  auto finish = [&](int, int raw, int& key, uint32_t& vm) {
+    vm = (uint32_t)ballot(raw >= 0);
+    key = raw >= 0 ? raw : 0;
+  };
+  __syncthreads();  // the candidate area in vl[0] is reused as staging
+  ga.template run<false>((u_hi - u_lo + 31) / 32, fetch, finish, kbase, vbase, stride, vl[wv],
+                         scale_log2, lane);
+
+  // ---- merge the wavefronts' partials in LDS (the staging areas are free now)
+  const float lw = ga.total_l();
+  __syncthreads();
+  {
+    float* mo = reinterpret_cast<float*>(vl[wv]);  // [16 heads][D] then m[16], l[16]
+    if (hv) {
+#pragma unroll
+      for (int dt = 0; dt < GA::DT; ++dt)
+        *reinterpret_cast<f32x4*>(mo + n * D + dt * 16 + grp * 4) = ga.acc[dt];
+      if (grp == 0) {
+        mo[16 * D + n] = ga.m_run;
+        mo[16 * D + 16 + n] = lw;
       }
     }
-    const uint32_t vm = (uint32_t)ballot(ok);
-    ga.step(kbase, vbase, stride, key, vm, vl, scale_log2, lane);
   }
-
-  // partial (o unnormalised, m in log2 units, l) of this split
-  const float l = ga.total_l();
-  constexpr int PS = D + 4;  // floats per (split, head) partial: o[D], m, l, 2 pad
-  const int64_t pbase = (((int64_t)bg * n_splits + split) * G) * PS;
-  if (hv) {
-    float* pp = partials + pbase + (int64_t)n * PS;
+  __syncthreads();
+  const int64_t pbase = ((int64_t)bg * n_splits + split) * G * PS;
+  for (int it = tid; it < G * (D / 8); it += 64 * kSplitWaves) {
+    const int hh = it / (D / 8), dd = (it % (D / 8)) * 8;
+    float M = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < GA::DT; ++dt)
-      *reinterpret_cast<f32x4*>(pp + dt * 16 + grp * 4) = ga.acc[dt];
-    if (grp == 0) {
-      pp[D] = ga.m_run;
-      pp[D + 1] = l;
+    for (int w2 = 0; w2 < kSplitWaves; ++w2)
+      M = fmaxf(M, reinterpret_cast<const float*>(vl[w2])[16 * D + hh]);
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float lt = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w2 = 0; w2 < kSplitWaves; ++w2) {
+        const float* mo = reinterpret_cast<const float*>(vl[w2]);
+        const float f = exp2f(mo[16 * D + hh] - M);
+        lt += f * mo[16 * D + 16 + hh];
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(mo + hh * D + dd);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(mo + hh * D + dd + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] += f * x0[i];
+          o[4 + i] += f * x1[i];
+        }
+      }
+    }
+    float* pp = partials + pbase + (int64_t)hh * PS;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __hip_atomic_store(pp + dd + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dd == 0) {
+      __hip_atomic_store(pp + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pp + D + 1, lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-  // the last split of this (sequence, KV head) merges
-  __threadfence();
+  // ---- the last split of this (sequence, KV head) merges all splits
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
-  if (lane == 0) last = atomicAdd(&counters[bg], 1u) == (uint32_t)(n_splits - 1);
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(&counters[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)(n_splits - 1);
   __syncthreads();
   if (!last) return;
-  __threadfence();
-  const float* pb = partials + ((int64_t)bg * n_splits) * G * PS;
-  for (int hh = 0; hh < G; ++hh) {
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s)
-      M = fmaxf(M, __builtin_nontemporal_load(pb + ((int64_t)s * G + hh) * PS + D));
-    float lt = 0.f;
-    float o[D / 64];
+  const float* pb = partials + (int64_t)bg * n_splits * G * PS;
+  auto ald = [](const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int it = tid; it < G * (D / 4); it += 64 * kSplitWaves) {
+    const int hh = it / (D / 4), dd = (it % (D / 4)) * 4;
+    float M = -INFINITY, lt = 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {  // 8 splits' loads in flight
+      float ms[8], ls[8], os[8][4];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-    if (M > -INFINITY) {
-      for (int s = 0; s < n_splits; ++s) {
-        const float* ps = pb + ((int64_t)s * G + hh) * PS;
-        const float ms = __builtin_nontemporal_load(ps + D);
-        const float f = exp2f(ms - M);  // 0 for an empty split (ms = -inf)
-        lt += f * __builtin_nontemporal_load(ps + D + 1);
+      for (int u = 0; u < 8; ++u) {
+        ms[u] = -INFINITY;
+        ls[u] = 0.f;
+        os[u][0] = os[u][1] = os[u][2] = os[u][3] = 0.f;
+        if (s0 + u < n_splits) {
+          const float* ps = pb + ((int64_t)(s0 + u) * G + hh) * PS;
+          ms[u] = ald(ps + D);
+          ls[u] = ald(ps + D + 1);
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) o[i] += f * __builtin_nontemporal_load(ps + lane + 64 * i);
+          for (int i = 0; i < 4; ++i) os[u][i] = ald(ps + dd + i);
+        }
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, ms[u]);
+      if (Mn > -INFINITY) {
+        const float a = exp2f(M - Mn);  // 0 while M is -inf
+        lt *= a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= a;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float f = exp2f(ms[u] - Mn);  // 0 for empty splits
+          lt += f * ls[u];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] += f * os[u][i];
+        }
+        M = Mn;
       }
     }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* orow = out + ((int64_t)b * Hq + g * G + hh) * D;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) orow[lane + 64 * i] = (uint16_t)f32_to_bf16_bits(o[i] * inv);
-    if (lse && lane == 0)
+    uint16_t* orow = out + ((int64_t)b * Hq + g * G + hh) * D + dd;
+    st8(orow, u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)});
+    if (lse && dd == 0)
       lse[(int64_t)b * Hq + g * G + hh] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
   }
-  if (lane == 0) counters[bg] = 0u;
+  if (tid == 0) __hip_atomic_store(&counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+static void launch_decode_d(const void* q, const void* kcache, const void* vcache,
+                            const float* kbar, const int32_t* lens, int B, int Lmax, int Hq,
+                            int Hkv, int block, int top_blocks, int window, int n_splits,
+                            float sl2, void* out, float* lse, int32_t* sel_out,
+                            const DecodeWs& ws, hipStream_t st) {
+  int nwg, per_wg;
+  score_grid(Lmax / block, nwg, per_wg);
+  const int cpw = (top_blocks + 7) / 8 * 8;
+  const dim3 g1((unsigned)(B * Hkv), (unsigned)nwg);
+  const dim3 g2((unsigned)(B * Hkv), (unsigned)n_splits);
+  hipLaunchKernelGGL(decode_block_scores<D>, g1, dim3(kScoreThreads), 0, st, (const uint16_t*)q,
+                     kbar, lens, Lmax, Hq, Hkv, block, per_wg, cpw, ws.cand);
+  hipLaunchKernelGGL(decode_split_attn<D>, g2, dim3(64 * kSplitWaves), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)kcache, (const uint16_t*)vcache, lens, Lmax, Hq, Hkv, block,
+                     top_blocks, window, n_splits, nwg * cpw, sl2, ws.cand, ws.partials,
+                     ws.counters, sel_out, (uint16_t*)out, lse);
 }
 
 hipError_t launch_sparse_decode(const void* q, const void* kcache, const void* vcache,
@@ -325,27 +483,13 @@ hipError_t launch_sparse_decode(const void* q, const void* kcache, const void* v
                                 int Hkv, int D, int block, int top_blocks, int window,
                                 int n_splits, float scale, void* out, float* lse,
                                 int32_t* sel_out, const DecodeWs& ws, hipStream_t st) {
-  const int nb = Lmax / block;
-  const dim3 g1((unsigned)(B * Hkv), (unsigned)imax(1, (nb + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG));
-  const dim3 g2((unsigned)(B * Hkv), (unsigned)n_splits);
   const float sl2 = scale * kLog2e;
-  if (D == 128) {
-    hipLaunchKernelGGL(decode_block_scores<128>, g1, dim3(kScoreThreads), 0, st, (const uint16_t*)q,
-                       kbar, lens, Lmax, Hq, Hkv, block, top_blocks, ws.block_scores, ws.sel,
-                       sel_out, ws.counters);
-    hipLaunchKernelGGL(decode_split_attn<128>, g2, dim3(64), 0, st, (const uint16_t*)q,
-                       (const uint16_t*)kcache, (const uint16_t*)vcache, lens, Lmax, Hq, Hkv, block,
-                       top_blocks, window, n_splits, sl2, ws.sel, ws.partials,
-                       ws.counters + B * Hkv, (uint16_t*)out, lse);
-  } else {
-    hipLaunchKernelGGL(decode_block_scores<64>, g1, dim3(kScoreThreads), 0, st, (const uint16_t*)q,
-                       kbar, lens, Lmax, Hq, Hkv, block, top_blocks, ws.block_scores, ws.sel,
-                       sel_out, ws.counters);
-    hipLaunchKernelGGL(decode_split_attn<64>, g2, dim3(64), 0, st, (const uint16_t*)q,
-                       (const uint16_t*)kcache, (const uint16_t*)vcache, lens, Lmax, Hq, Hkv, block,
-                       top_blocks, window, n_splits, sl2, ws.sel, ws.partials,
-                       ws.counters + B * Hkv, (uint16_t*)out, lse);
-  }
+  if (D == 128)
+    launch_decode_d<128>(q, kcache, vcache, kbar, lens, B, Lmax, Hq, Hkv, block, top_blocks,
+                         window, n_splits, sl2, out, lse, sel_out, ws, st);
+  else
+    launch_decode_d<64>(q, kcache, vcache, kbar, lens, B, Lmax, Hq, Hkv, block, top_blocks,
+                        window, n_splits, sl2, out, lse, sel_out, ws, st);
   return hipGetLastError();
 }
 

@@ -10,6 +10,8 @@
 // heads of one token (H = 4), so ReLU, the head weights and the head sum are lane-local.
 // A workgroup of 4 wavefronts owns 128 consecutive rows (32 per wavefront); its
 // wavefronts walk the same key range, so the key rows they load are shared in cache.
+// Each wavefront computes 32 rows x 64 keys of scores into LDS and writes them back as
+// 16-byte-per-lane stores of whole 256-byte row pieces.
 // Key ranges are cut into chunks of 1024 and handed round-robin to 8 workgroups per
 // row strip, which balances the triangular (causal) work.
 //
@@ -36,6 +38,9 @@ __global__ __launch_bounds__(256) void indexer_mfma(const uint16_t* __restrict__
   constexpr int TPT = 16 / H;                        // tokens per 16-row M tile
   constexpr int TM = kIdxRowsPerWave / TPT;          // M tiles per wavefront
   constexpr int TPL = 4 / H;                         // tokens per lane in the C layout
+  constexpr int SB = 64;                             // keys per staged block
+  constexpr int SROW = SB + 4;                       // padded LDS row (floats)
+  __shared__ __attribute__((aligned(16))) float stage[kIdxWaves][kIdxRowsPerWave * SROW];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int R = row_end - row_begin;
@@ -47,6 +52,7 @@ __global__ __launch_bounds__(256) void indexer_mfma(const uint16_t* __restrict__
   if (t0 >= row_end) return;
   const int t_last = min(t0 + kIdxRowsPerWave, row_end) - 1;
   const int wave_chunks = t_last / kIdxChunk + 1;  // chunks that meet this wave's rows
+  float* st = stage[wv];
 
   float w[H];
 #pragma unroll
@@ -56,7 +62,7 @@ __global__ __launch_bounds__(256) void indexer_mfma(const uint16_t* __restrict__
   u32x4 a[TM][KS];
 #pragma unroll
   for (int m = 0; m < TM; ++m) {
-    const int row = m * 16 + n;                      // (token, head) row inside the strip
+    const int row = m * 16 + n;                      // (token, head) row inside the wave
     const int tt = t0 + row / H;
     const bool ok = tt < row_end;
     const uint16_t* p = qi + (((int64_t)b * T + (ok ? tt : t0)) * H + row % H) * DI + grp * 8;
@@ -73,30 +79,50 @@ __global__ __launch_bounds__(256) void indexer_mfma(const uint16_t* __restrict__
   for (int c = group; c < wave_chunks; c += kIdxGroups) {
     const int s_lo = c * kIdxChunk;
     const int s_hi = min(s_lo + kIdxChunk, t_last + 1);
-    for (int s0 = s_lo; s0 < s_hi; s0 += 16) {
-      const int s = s0 + n;
-      const bool sok = s < s_hi;
-      u32x4 bk[KS];
-      const uint16_t* kp = kib + (int64_t)(sok ? s : s0) * DI + grp * 8;
+    for (int s0 = s_lo; s0 < s_hi; s0 += SB) {
+      // ---- 32 rows x 64 keys of scores into this wave's LDS stage
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bk[ks] = ld16(kp + ks * 32);
+      for (int nt = 0; nt < SB / 16; ++nt) {
+        const int s = min(s0 + nt * 16 + n, T - 1);
+        u32x4 bk[KS];
+        const uint16_t* kp = kib + (int64_t)s * DI + grp * 8;
 #pragma unroll
-      for (int m = 0; m < TM; ++m) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = ld16(kp + ks * 32);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m][ks]), as_bf16x8(bk[ks]),
-                                                        acc, 0, 0, 0);
-        // lane rows grp*4 .. grp*4+3 of tile m = TPL tokens x H heads
+        for (int m = 0; m < TM; ++m) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < TPL; ++u) {
-          float sc = 0.f;
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m][ks]), as_bf16x8(bk[ks]),
+                                                          acc, 0, 0, 0);
 #pragma unroll
-          for (int hh = 0; hh < H; ++hh) sc += w[hh] * fmaxf(acc[u * H + hh], 0.f);
-          const int tt = t0 + m * TPT + grp * TPL + u;
-          if (sok && s <= tt && tt < row_end) sb[(int64_t)(tt - row_begin) * ld + s] = sc;
+          for (int u = 0; u < TPL; ++u) {
+            float sc = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) sc += w[hh] * fmaxf(acc[u * H + hh], 0.f);
+            st[(m * TPT + grp * TPL + u) * SROW + nt * 16 + n] = sc;
+          }
         }
       }
+      wave_lds_sync();
+      // ---- 16 B per lane: 4 rows x 64 keys per instruction
+      const bool full = s0 + SB - 1 <= t0;  // every key of the block precedes every row
+#pragma unroll
+      for (int i = 0; i < kIdxRowsPerWave / 4; ++i) {
+        const int rr = i * 4 + (lane >> 4);
+        const int tt = t0 + rr;
+        const int sc0 = s0 + (lane & 15) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + rr * SROW + (lane & 15) * 4);
+        float* dst = sb + (int64_t)(tt - row_begin) * ld + sc0;
+        if (full && tt < row_end) {
+          *reinterpret_cast<f32x4*>(dst) = v;
+        } else if (tt < row_end) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (sc0 + j <= tt && sc0 + j < s_hi) dst[j] = v[j];
+        }
+      }
+      wave_lds_sync();
     }
   }
 }

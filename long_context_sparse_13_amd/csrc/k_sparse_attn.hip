@@ -53,22 +53,19 @@ __global__ __launch_bounds__(64) void sparse_attn_mfma(
   const int slot = lane & 31;
   const int last_listed = t - window;  // listed keys must satisfy 0 <= s <= t - window
   const int wlo = t - window + 1;
-
-  for (int tile = 0; tile < n_idx + n_win; ++tile) {
-    int key;
-    bool ok;
+  auto fetch = [&](int tile) -> int {
     if (tile < n_idx) {
       const int e = tile * 32 + slot;
-      key = e < topk ? irow[e] : -1;
-      ok = key >= 0 && key <= last_listed;
-    } else {
-      key = wlo + (tile - n_idx) * 32 + slot;
-      ok = key >= 0 && key <= t;
+      return e < topk ? irow[e] : -1;
     }
-    const uint32_t vm = (uint32_t)ballot(ok);
-    if (vm == 0u) continue;
-    ga.step(kbase, vbase, stride, ok ? key : 0, vm, vl, scale_log2, lane);
-  }
+    return wlo + (tile - n_idx) * 32 + slot;
+  };
+  auto finish = [&](int tile, int raw, int& key, uint32_t& vm) {
+    const bool ok = tile < n_idx ? (raw >= 0 && raw <= last_listed) : (raw >= 0 && raw <= t);
+    vm = (uint32_t)ballot(ok);
+    key = ok ? raw : 0;
+  };
+  ga.template run<false>(n_idx + n_win, fetch, finish, kbase, vbase, stride, vl, scale_log2, lane);
 
   const float l = ga.total_l();
   const float inv = l > 0.f ? 1.f / l : 0.f;

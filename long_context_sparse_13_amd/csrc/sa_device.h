@@ -54,6 +54,15 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over each aligned group of 8 lanes with DPP moves (no LDS round trip): xor 1,
+// xor 2 within quads, then the mirror inside each half row pairs the two quads.
+__device__ __forceinline__ float sum8_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+  return v;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 // Orders LDS accesses of the lanes of one wavefront (LDS executes a wavefront's

@@ -28,10 +28,9 @@ hipError_t launch_block_meanpool(const void* kcache, const int32_t* lens, int B,
                                  int D, int block, bool bf16, float* kbar, hipStream_t st);
 
 struct DecodeWs {
-  float* block_scores;   // [B, Hkv, nblk]
-  int32_t* sel;          // [B, Hkv, top_blocks]
+  uint32_t* cand;        // [B, Hkv, scoring workgroups, 16] packed (order key, block)
   float* partials;       // [B, Hkv, n_splits, G, D + 4]  (o[D], m, l, pad)
-  uint32_t* counters;    // [B * Hkv] selection counters, then [B * Hkv] merge counters
+  uint32_t* counters;    // [B * Hkv] merge counters
 };
 size_t decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int D, int block, int top_blocks,
                               int n_splits);

@@ -72,3 +72,14 @@ def test_streaming_path_long_rows():
     # rows longer than 65,536 re-read the scores every pass (the 128K reuse workload)
     _check(208, 1, 131072, 131072 - 6, 131072, 2048, "normal")
     _check(209, 1, 70001, 69990, 70001, 3000, "ties")
+
+
+def test_overflowing_tie_digit_uses_fallback():
+    # more than 4096 positions share the digit of the k-th key: multi-pass fallback
+    _check(210, 1, 12000, 11990, 12000, 100, "allequal")
+    _check(211, 1, 65536, 65530, 65536, 2048, "ties")
+
+
+def test_largest_k_and_k_near_n():
+    _check(212, 1, 9000, 8990, 9000, 4096, "normal")
+    _check(213, 1, 3000, 2990, 3000, 2995, "relu")

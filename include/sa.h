@@ -84,7 +84,7 @@ int sa_indexer_scores(const void* qi, const void* ki, const float* w, int B, int
  *
  * scores [B, row_end - row_begin, ld] float32 (as written by sa_indexer_scores)
  * idx    [B, T, k] int32; only rows [row_begin, row_end) are written.
- * Requires 1 <= k <= 4096 and ld >= row_end.
+ * Requires 1 <= k <= 4096, ld >= row_end and ld % 4 == 0.
  */
 int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin, int row_end,
                    int k, int32_t* idx, void* stream);

@@ -5,57 +5,58 @@
 // subset is made of individual tokens).  For row t the result is the min(k, t+1)
 // positions s <= t with the largest scores, ties to the lower s, written ascending.
 //
-// One 512-thread workgroup (8 wavefronts) per row; scores become order-preserving
+// One 256-thread workgroup (4 wavefronts) per row; scores become order-preserving
 // 32-bit keys (-0.0 and +0.0 share a key).  Each wavefront owns one contiguous segment
 // of the row.
-//  pass 1 (reads the row from HBM): every wavefront builds its own histogram of the top
-//         11 key bits (16-bit counters, two per LDS word).  Summed over wavefronts they
-//         give the digit d* holding the k-th largest key and kk1, how many keys of that
-//         digit are kept; each wavefront's own counts above and at d* give it the offsets
-//         of its positions in two LDS lists.
-//  pass 2 (reads the row again, now cache-resident): positions with a digit above d* are
-//         kept for sure and appended, in position order, to the "sure" list; positions at
-//         d* go with their keys to the candidate list.  Order is kept with ballots and
-//         mbcnt, so both lists are ascending without any sort.
-//  resolve (LDS only): two more radix digits (11 + 10 bits) over the candidates find the
-//         exact k-th key a; candidates above a, and the first ones equal to a (lower
-//         positions first, i.e. the tie rule), are appended ascending after the sure list.
-//  merge: the two ascending lists are merged by binary search into the output row.
-// Rows whose candidate digit holds more than kCap positions (massive exact ties) fall
-// back to the multi-pass workgroup select of select.h reading the row from memory.
-// Rows are issued longest first.
+//  pass 1 (reads the row from HBM): every wavefront counts the top 11 key bits (the
+//         digit) of its segment into its own LDS histogram.  Summed, the histograms give
+//         the digit d* holding the k-th largest key and kk1, how many keys of digit d* are
+//         kept; each wavefront's own count of digits >= d* gives its offset in the hit
+//         list.
+//  pass 2 (reads the row again, now cache-resident): positions with digit >= d* ("hits")
+//         go with their keys to the hit list, in position order (ballot + mbcnt).
+//  resolve (LDS only): hits above d* are all kept; among hits at d*, two more radix
+//         digits (11 + 10 bits) find the exact k-th key a; keys above a, and the first
+//         ones equal to a (lower positions first: the tie rule), are kept.
+//  output: one order-preserving compaction of the kept hits is the ascending answer.
+// Rows with more hits than kHitCap (massive exact ties) fall back to the multi-pass
+// workgroup select of select.h reading the row from memory.  Rows are issued longest
+// first.
 #include "sa_launch.h"
 #include "select.h"
 
 namespace sa {
 
-constexpr int kTkThreads = 512;
+constexpr int kTkThreads = 256;
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kD1Bins = 2048;  // first digit: key bits [31:21]
-constexpr int kCap = 4096;     // candidate capacity
-constexpr int kKMax = 4096;    // largest k
-constexpr int kUnroll = 32;    // loads in flight per lane while streaming
+constexpr int kD1Bins = 2048;   // first digit: key bits [31:21]
+constexpr int kHitCap = 6144;   // hit list capacity
+constexpr int kLoads = 8;                // 16-byte loads per lane in flight while streaming
+constexpr int kChunk = 64 * 4 * kLoads;  // positions a wavefront streams per step
 
 struct TopkShared {
   union {
-    uint32_t whist[kTkWaves][kD1Bins / 2];  // pass 1: per-wave 16-bit counters
+    uint32_t whist[kTkWaves][kD1Bins];  // pass 1: per-wave counters
     struct {
-      uint32_t key[kCap];
-      int pos[kCap];
-    } cand;                                 // pass 2 / resolve: candidate list
-    SelectShared<kTkThreads> fallback;      // rows with too many candidates
+      uint32_t key[kHitCap];
+      int pos[kHitCap];
+    } hit;                              // pass 2 / resolve: the hit list
+    SelectShared<kTkThreads> fallback;  // rows with too many hits
   } u;
-  int sel[kKMax];        // sure list, then the chosen candidates
   uint32_t hist2[2048];  // resolve histograms
-  int run_gt[kCap / 64 + 1];
-  int run_eq[kCap / 64 + 1];
-  int wsure[kTkWaves], wcand[kTkWaves];
+  int run_gt[kHitCap / 64];
+  int run_eq[kHitCap / 64];
+  int whits[kTkWaves];
   int wsum[2][kTkWaves];
   int misc[8];
 };
 
-__device__ __forceinline__ uint32_t get16(const uint32_t* h, int d) {
-  return (h[d >> 1] >> ((d & 1) << 4)) & 0xffffu;
+// Digit (top 11 bits of the order-preserving key) of a float, -0.0 counted as +0.0:
+// positive u -> (u >> 21) | 0x400, negative u -> ~(u >> 21) & 0x7ff.
+__device__ __forceinline__ uint32_t digit11(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  const uint32_t s = (uint32_t)((int32_t)u >> 31);
+  return (u >> 21) ^ ((s & 0x3ffu) | 0x400u);
 }
 
 // Finds, over nb bins (counts from cnt(d)), the digit holding the kk-th largest element:
@@ -66,18 +67,16 @@ __device__ __forceinline__ void find_digit(int nb, int kk, Cnt&& cnt, TopkShared
   const int tid = threadIdx.x;
   const int bpt = (nb + kTkThreads - 1) / kTkThreads;
   const int top = nb - 1 - bpt * tid;
-  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  uint32_t c[8];
   int local = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i < bpt && top - i >= 0) {
-      c[i] = cnt(top - i);
-      local += (int)c[i];
-    }
+  for (int i = 0; i < 8; ++i) {
+    c[i] = (i < bpt && top - i >= 0) ? cnt(top - i) : 0u;
+    local += (int)c[i];
   }
   int above = wg_excl_scan<kTkThreads>(local, sh.wsum[0]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     if (i < bpt && top - i >= 0) {
       if (above < kk && kk <= above + (int)c[i]) {
         sh.misc[o] = top - i;
@@ -88,6 +87,49 @@ __device__ __forceinline__ void find_digit(int nb, int kk, Cnt&& cnt, TopkShared
     }
   }
   __syncthreads();
+}
+
+// Streams positions [lo, hi) of the row (lo a multiple of 4, the row 16-byte aligned) in
+// groups of 4 consecutive positions per lane: f(e, x[4], valid[4]) with e the first
+// position of the group.  A wavefront's call order covers its positions in increasing
+// order, 256 per call round (lane-major inside a round); kLoads loads per lane are in
+// flight, and full chunks run without per-position guards.
+template <typename F>
+__device__ __forceinline__ void stream_segment(const float* __restrict__ row, int lo, int hi,
+                                               int lane, F&& f) {
+  int e0 = lo;
+  for (; e0 + kChunk <= hi; e0 += kChunk) {
+    f32x4 v[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(row + e0 + u * 256 + lane * 4);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const bool ok[4] = {true, true, true, true};
+      const float x[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
+      f(e0 + u * 256 + lane * 4, x, ok);
+    }
+  }
+  if (e0 < hi) {  // the last, partial chunk: 16-byte loads where the group is whole
+    f32x4 v[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int e = e0 + u * 256 + lane * 4;
+      if (e + 3 < hi) {
+        v[u] = *reinterpret_cast<const f32x4*>(row + e);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[u][c] = e + c < hi ? row[e + c] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int e = e0 + u * 256 + lane * 4;
+      const bool ok[4] = {e < hi, e + 1 < hi, e + 2 < hi, e + 3 < hi};
+      const float x[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
+      f(e, x, ok);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_rows(const float* __restrict__ scores,
@@ -109,123 +151,104 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows(const float* __restrict_
     return;
   }
 
-  // ---- pass 1: per-wave histograms of the top 11 key bits
+  // ---- pass 1: per-wave digit histograms
   const int seg = ((n + kTkThreads - 1) / kTkThreads) * 64;
   const int lo = min(n, w * seg), hi = min(n, lo + seg);
-  for (int i = tid; i < kTkWaves * kD1Bins / 2; i += kTkThreads) (&sh.u.whist[0][0])[i] = 0u;
+  for (int i = tid; i < kTkWaves * kD1Bins; i += kTkThreads) (&sh.u.whist[0][0])[i] = 0u;
   __syncthreads();
   uint32_t* wh = sh.u.whist[w];
-  for (int e0 = lo; e0 < hi; e0 += 64 * kUnroll) {
-    float v[kUnroll];
+  stream_segment(row, lo, hi, lane, [&](int, const float* x, const bool* ok) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = e0 + u * 64 + lane;
-      v[u] = e < hi ? row[e] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = e0 + u * 64 + lane;
-      if (e < hi) {
-        const uint32_t d = order_key(v[u]) >> 21;
-        atomicAdd(&wh[d >> 1], 1u << ((d & 1u) << 4));
-      }
-    }
-  }
+    for (int c = 0; c < 4; ++c)
+      if (ok[c]) atomicAdd(&wh[digit11(x[c])], 1u);
+  });
   __syncthreads();
 
-  // ---- digit of the k-th largest key; per-wave counts above / at it
+  // ---- digit of the k-th largest key; per-wave counts of hits (digit >= d*)
   find_digit(kD1Bins, k, [&](int d) {
     uint32_t s = 0;
 #pragma unroll
-    for (int ww = 0; ww < kTkWaves; ++ww) s += get16(sh.u.whist[ww], d);
+    for (int ww = 0; ww < kTkWaves; ++ww) s += sh.u.whist[ww][d];
     return s;
   }, sh, 0);
-  const int dstar = sh.misc[0];
+  const uint32_t dstar = (uint32_t)sh.misc[0];
   const int kk1 = sh.misc[1];
   {
-    int above = 0;
-    for (int d = dstar + 1 + lane; d < kD1Bins; d += 64) above += (int)get16(wh, d);
+    int cnt = 0;
+    for (int d = (int)dstar + lane; d < kD1Bins; d += 64) cnt += (int)wh[d];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) above += __shfl_xor(above, m, 64);
-    if (lane == 0) {
-      sh.wsure[w] = above;
-      sh.wcand[w] = (int)get16(wh, dstar);
-    }
+    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
+    if (lane == 0) sh.whits[w] = cnt;
   }
   __syncthreads();
-  int sure_off = 0, cand_off = 0, n_cand = 0;
+  int hit_off = 0, n_hits = 0;
 #pragma unroll
   for (int ww = 0; ww < kTkWaves; ++ww) {
-    sure_off += ww < w ? sh.wsure[ww] : 0;
-    cand_off += ww < w ? sh.wcand[ww] : 0;
-    n_cand += sh.wcand[ww];
+    hit_off += ww < w ? sh.whits[ww] : 0;
+    n_hits += sh.whits[ww];
   }
-  const int n_sure = k - kk1;
-  __syncthreads();  // the histogram region becomes the candidate list
+  const int n_sure = k - kk1;  // hits above d*
+  const int n_cand = n_hits - n_sure;
+  __syncthreads();  // the histogram region becomes the hit list
 
-  if (n_cand > kCap) {
+  if (n_hits > kHitCap) {
     wg_topk<kTkThreads, 0>(
         n, k, [&](int e) { return order_key(row[e]); }, [&](int pos, int e) { out[pos] = e; },
         sh.u.fallback);
     return;
   }
 
-  // ---- pass 2: sure positions and candidates, in position order
-  for (int e0 = lo; e0 < hi; e0 += 64 * kUnroll) {
-    float v[kUnroll];
+  // ---- pass 2: the hit list, in position order
+  stream_segment(row, lo, hi, lane, [&](int e, const float* x, const bool* ok) {
+    bool hit[4];
+    uint64_t m[4];
+    int before = 0;  // hits of the lower lanes in this round (lane-major order)
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = e0 + u * 64 + lane;
-      v[u] = e < hi ? row[e] : 0.f;
+    for (int c = 0; c < 4; ++c) {
+      hit[c] = ok[c] && digit11(x[c]) >= dstar;
+      m[c] = ballot(hit[c]);
+      before += lanes_below(m[c]);
     }
+    if ((m[0] | m[1] | m[2] | m[3]) != 0ull) {
+      int p = hit_off + before;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = e0 + u * 64 + lane;
-      const uint32_t key = order_key(v[u]);
-      const int d = (int)(key >> 21);
-      const bool in = e < hi;
-      const bool sure = in && d > dstar;
-      const bool cand = in && d == dstar;
-      const uint64_t ms = ballot(sure), mc = ballot(cand);
-      if (sure) sh.sel[sure_off + lanes_below(ms)] = e;
-      if (cand) {
-        const int p = cand_off + lanes_below(mc);
-        sh.u.cand.key[p] = key;
-        sh.u.cand.pos[p] = e;
+      for (int c = 0; c < 4; ++c) {
+        if (hit[c]) {
+          sh.u.hit.key[p] = order_key(x[c]);
+          sh.u.hit.pos[p] = e + c;
+          ++p;
+        }
       }
-      sure_off += __popcll(ms);
-      cand_off += __popcll(mc);
+      hit_off += __popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]);
     }
-  }
+  });
   __syncthreads();
 
-  // ---- resolve the candidates: keep kk1 of them (largest keys, lower positions on ties)
-  uint32_t thr_gt, thr_eq;
-  int take_eq;
-  if (kk1 == n_cand) {  // every candidate is kept
-    thr_gt = 0u;
-    thr_eq = 0u;
-    take_eq = 0;
-  } else {
+  // ---- resolve: keep all hits above d*, and kk1 of the hits at d*
+  const uint32_t dlo = dstar << 21;   // smallest key of digit d*
+  const uint32_t dhi = dlo + (1u << 21);
+  uint32_t thr_gt = dlo;              // keys >= thr_gt are kept
+  uint32_t thr_eq = 0u;               // keys == thr_eq are kept while fewer than take_eq precede
+  int take_eq = 0;
+  if (kk1 < n_cand) {
     for (int i = tid; i < 2048; i += kTkThreads) sh.hist2[i] = 0u;
     __syncthreads();
-    for (int e = tid; e < n_cand; e += kTkThreads)
-      atomicAdd(&sh.hist2[(sh.u.cand.key[e] >> 10) & 2047u], 1u);
+    for (int e = tid; e < n_hits; e += kTkThreads) {
+      const uint32_t key = sh.u.hit.key[e];
+      if (key < dhi) atomicAdd(&sh.hist2[(key >> 10) & 2047u], 1u);
+    }
     __syncthreads();
     find_digit(2048, kk1, [&](int d) { return sh.hist2[d]; }, sh, 3);
-    const uint32_t d2 = (uint32_t)sh.misc[3];
+    const uint32_t pre2 = dlo | ((uint32_t)sh.misc[3] << 10);
     const int kk2 = sh.misc[4];
-    const uint32_t pre2 = ((uint32_t)dstar << 21) | (d2 << 10);
     if (sh.misc[5]) {
       thr_gt = pre2;
-      thr_eq = 0u;
-      take_eq = 0;
     } else {
       __syncthreads();
       for (int i = tid; i < 1024; i += kTkThreads) sh.hist2[i] = 0u;
       __syncthreads();
-      for (int e = tid; e < n_cand; e += kTkThreads) {
-        const uint32_t key = sh.u.cand.key[e];
+      for (int e = tid; e < n_hits; e += kTkThreads) {
+        const uint32_t key = sh.u.hit.key[e];
         if ((key >> 10) == (pre2 >> 10)) atomicAdd(&sh.hist2[key & 1023u], 1u);
       }
       __syncthreads();
@@ -236,24 +259,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows(const float* __restrict_
       take_eq = sh.misc[6];
     }
   }
-  // order-preserving compaction of the chosen candidates after the sure list
-  const int runs = (n_cand + 63) / 64;
-  const int slots = (n_cand + kTkThreads - 1) / kTkThreads;
+
+  // ---- output: order-preserving compaction of the kept hits
+  const int runs = (n_hits + 63) / 64;
+  const int slots = (n_hits + kTkThreads - 1) / kTkThreads;
   for (int j = 0; j < slots; ++j) {
     const int e = j * kTkThreads + tid;
-    const uint32_t key = e < n_cand ? sh.u.cand.key[e] : 0u;
-    const bool in = e < n_cand;
+    const bool in = e < n_hits;
+    const uint32_t key = in ? sh.u.hit.key[e] : 0u;
     const bool gt = in && key >= thr_gt;
     const bool eq = in && !gt && take_eq > 0 && key == thr_eq;
     const uint64_t mg = ballot(gt), me = ballot(eq);
-    const int run = e >> 6;
-    if (lane == 0 && run < runs) {
-      sh.run_gt[run] = __popcll(mg);
-      sh.run_eq[run] = __popcll(me);
+    if (lane == 0 && (e >> 6) < runs) {
+      sh.run_gt[e >> 6] = __popcll(mg);
+      sh.run_eq[e >> 6] = __popcll(me);
     }
   }
   __syncthreads();
-  if (w == 0) {  // exclusive scan of the (few) runs by one wavefront
+  if (w == 0) {  // exclusive scan of the runs by one wavefront
     int gsum = 0, esum = 0;
     for (int r0 = 0; r0 < runs; r0 += 64) {
       const int ri = r0 + lane;
@@ -278,33 +301,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows(const float* __restrict_
   __syncthreads();
   for (int j = 0; j < slots; ++j) {
     const int e = j * kTkThreads + tid;
-    const bool in = e < n_cand;
-    const uint32_t key = in ? sh.u.cand.key[e] : 0u;
+    const bool in = e < n_hits;
+    const uint32_t key = in ? sh.u.hit.key[e] : 0u;
     const bool gt = in && key >= thr_gt;
     const bool eq = in && !gt && take_eq > 0 && key == thr_eq;
     const uint64_t mg = ballot(gt), me = ballot(eq);
-    const int run = e >> 6;
     if (in) {
-      const int gb = sh.run_gt[run] + lanes_below(mg);
-      const int eb = sh.run_eq[run] + lanes_below(me);
-      if (gt) sh.sel[n_sure + gb + min(eb, take_eq)] = sh.u.cand.pos[e];
-      else if (eq && eb < take_eq) sh.sel[n_sure + gb + eb] = sh.u.cand.pos[e];
+      const int gb = sh.run_gt[e >> 6] + lanes_below(mg);
+      const int eb = sh.run_eq[e >> 6] + lanes_below(me);
+      if (gt) out[gb + min(eb, take_eq)] = sh.u.hit.pos[e];
+      else if (eq && eb < take_eq) out[gb + eb] = sh.u.hit.pos[e];
     }
-  }
-  __syncthreads();
-
-  // ---- merge the two ascending lists sel[0, n_sure) and sel[n_sure, k)
-  const int nc = k - n_sure;
-  for (int i = tid; i < k; i += kTkThreads) {
-    const int v = sh.sel[i];
-    const int* other = i < n_sure ? sh.sel + n_sure : sh.sel;
-    int lo2 = 0, hi2 = i < n_sure ? nc : n_sure;  // count of entries of the other list < v
-    while (lo2 < hi2) {
-      const int mid = (lo2 + hi2) >> 1;
-      if (other[mid] < v) lo2 = mid + 1;
-      else hi2 = mid;
-    }
-    out[(i < n_sure ? i : i - n_sure) + lo2] = v;
   }
 }
 

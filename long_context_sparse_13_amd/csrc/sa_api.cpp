@@ -108,7 +108,8 @@ int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
     REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
     REQUIRE(0 <= row_begin && row_begin < row_end && row_end <= T,
             "need 0 <= row_begin < row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
-    REQUIRE(ld >= row_end, "ld must be >= row_end (got %lld)", (long long)ld);
+    REQUIRE(ld >= row_end && ld % 4 == 0, "ld must be >= row_end and a multiple of 4 (got %lld)",
+            (long long)ld);
     REQUIRE(k >= 1 && k <= 4096, "k must be in [1, 4096] (got %d)", k);
     REQUIRE((int64_t)B * (row_end - row_begin) <= 0x7fffffff, "too many rows in one call");
     SUPPORT(row_end <= 262144, "rows longer than 262144 are not supported (row_end=%d)", row_end);

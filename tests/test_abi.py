@@ -78,6 +78,7 @@ def test_indexer_and_topk_validation(L):
     assert t(P, 16, 1, 16, 0, 16, 0, P, None) == 1                # k
     assert t(P, 16, 1, 16, 0, 16, 5000, P, None) == 1             # k too big
     assert t(P, 8, 1, 16, 0, 16, 4, P, None) == 1                 # ld < row_end
+    assert t(P, 18, 1, 16, 0, 16, 4, P, None) == 1                # ld % 4
     assert t(P, 300000, 1, 300000, 0, 300000, 4, P, None) == 2    # rows too long
 
 

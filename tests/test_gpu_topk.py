@@ -30,7 +30,7 @@ def _scores(seed, B, R, ld, kind):
 def _check(seed, B, T, row_begin, row_end, k, kind, ld=None, sample=None):
     note(f"topk seed={seed} B={B} T={T} rows=[{row_begin},{row_end}) k={k} kind={kind}")
     R = row_end - row_begin
-    ld = ld or row_end
+    ld = ld or ((row_end + 3) // 4 * 4)
     s = _scores(seed, B, R, ld, kind)
     idx = sa.sa_topk_select(dev(s, "f32"), k, T, row_begin, row_end)
     got = host(idx)
@@ -71,7 +71,7 @@ def test_register_path_64k_rows():
 def test_streaming_path_long_rows():
     # rows longer than 65,536 re-read the scores every pass (the 128K reuse workload)
     _check(208, 1, 131072, 131072 - 6, 131072, 2048, "normal")
-    _check(209, 1, 70001, 69990, 70001, 3000, "ties")
+    _check(209, 1, 70001, 69990, 70001, 3000, "ties")   # ld = 70004 > row_end
 
 
 def test_overflowing_tie_digit_uses_fallback():

@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["attn", "prefill"], default=None,
                     help="time only one part (for profiling runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="first copy MB megabytes 3 times with torch (a plain copy kernel of "
+                         "known size, to calibrate the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -87,6 +90,15 @@ def main():
     sa.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 x {args.copy_probe} MiB")
+        del src, dst
 
     def to_dev(a, dtype):
         t = torch.from_numpy(np.ascontiguousarray(a))

@@ -39,7 +39,7 @@ struct GroupAttn {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qrow) w = ld16(qrow + ks * 32 + grp * 8);
+      if (qrow) w = ld16_nt(qrow + ks * 32 + grp * 8);
       qB[ks] = as_bf16x8(w);
     }
 #pragma unroll
@@ -141,8 +141,10 @@ struct GroupAttn {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (ballot(alpha != 1.f) != 0ull) {  // no head's maximum moved: nothing to rescale
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
 
     const u32x4 pw = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};

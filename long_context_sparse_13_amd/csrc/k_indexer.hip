@@ -12,7 +12,7 @@
 // wavefronts walk the same key range, so the key rows they load are shared in cache.
 // Each wavefront computes 32 rows x 64 keys of scores into LDS and writes them back as
 // 16-byte-per-lane stores of whole 256-byte row pieces.
-// Key ranges are cut into chunks of 1024 and handed round-robin to 8 workgroups per
+// Key ranges are cut into chunks of 256 and handed round-robin to 64 workgroups per
 // row strip, which balances the triangular (causal) work.
 //
 // indexer_valu<BF>: any dtype, H * DI <= 4096; float32 FMAs, one thread per key and 4
@@ -25,8 +25,8 @@ namespace sa {
 constexpr int kIdxRowsPerWave = 32;
 constexpr int kIdxWaves = 4;
 constexpr int kIdxStrip = kIdxRowsPerWave * kIdxWaves;  // 128 rows per workgroup
-constexpr int kIdxChunk = 1024;                          // keys per chunk
-constexpr int kIdxGroups = 8;                            // workgroups per row strip
+constexpr int kIdxChunk = 256;                           // keys per chunk
+constexpr int kIdxGroups = 64;                           // workgroups per row strip
 
 template <int H, int DI>
 __global__ __launch_bounds__(256) void indexer_mfma(const uint16_t* __restrict__ qi,

@@ -9,7 +9,10 @@
 // Two kernels:
 //  * sparse_attn_mfma<D>: bf16, up to 16 query heads per KV head.  One wavefront per
 //    (batch, token, KV head); keys are streamed 32 at a time through GroupAttn (MFMA
-//    over the grouped heads, online softmax).  The listed indices are visited first
+//    over the grouped heads, online softmax).  Held to 3 wavefronts per SIMD (<= 168
+//    registers): the kernel is bound by gathered-row latency, so more resident
+//    wavefronts beat a deeper per-wavefront pipeline.  Q, the index row and O are
+//    streamed with non-temporal accesses so they do not evict gathered K/V rows.  The listed indices are visited first
 //    (positions inside the window or outside [0, t] are masked out, so each key is
 //    counted once), then the window [t-W+1, t].
 //  * sparse_attn_valu<D, BF16>: any dtype, up to 64 heads per group (G*D <= 4096); plain
@@ -21,7 +24,7 @@
 namespace sa {
 
 template <int D>
-__global__ __launch_bounds__(64) void sparse_attn_mfma(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int B, int T, int Hq,
     int Hkv, int topk, int window, float scale_log2, uint16_t* __restrict__ out,
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(64) void sparse_attn_mfma(
   auto fetch = [&](int tile) -> int {
     if (tile < n_idx) {
       const int e = tile * 32 + slot;
-      return e < topk ? irow[e] : -1;
+      return e < topk ? ld_nt(irow + e) : -1;
     }
     return wlo + (tile - n_idx) * 32 + slot;
   };
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(64) void sparse_attn_mfma(
     for (int dt = 0; dt < GA::DT; ++dt) {
       const f32x4 a = ga.acc[dt] * inv;
       const u32x2 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-      st8(orow + dt * 16 + grp * 4, w);
+      st8_nt(orow + dt * 16 + grp * 4, w);
     }
     if (lse && grp == 0)
       lse[((int64_t)b * Hq + h) * T + t] = l > 0.f ? (ga.m_run + __log2f(l)) * kLn2 : -INFINITY;

@@ -28,6 +28,33 @@ import time
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ATTN_SOURCES = ("k_sparse_attn.hip", "attn_tile.h", "sa_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def attn_sources_hash() -> str:
+    """sha256 over the sources of the sparse-attention kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "long_context_sparse_13_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter runs, or None when the
+    kernel sources changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != attn_sources_hash():
+        return None
+    return t.get("bytes_per_launch")
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -196,7 +223,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": attn_bytes,
             "selected_keys_per_launch": n_sel,
             "avg_launch_ms": attn_avg_ms,

@@ -11,8 +11,9 @@
 //    (batch, token, KV head); keys are streamed 32 at a time through GroupAttn (MFMA
 //    over the grouped heads, online softmax).  Held to 3 wavefronts per SIMD (<= 168
 //    registers): the kernel is bound by gathered-row latency, so more resident
-//    wavefronts beat a deeper per-wavefront pipeline.  Q, the index row and O are
-//    streamed with non-temporal accesses so they do not evict gathered K/V rows.  The listed indices are visited first
+//    wavefronts beat a deeper per-wavefront pipeline.  Q and the index row are read
+//    with non-temporal loads so they do not evict gathered K/V rows (O is written with
+//    ordinary stores, which L2 combines into whole lines).  The listed indices are visited first
 //    (positions inside the window or outside [0, t] are masked out, so each key is
 //    counted once), then the window [t-W+1, t].
 //  * sparse_attn_valu<D, BF16>: any dtype, up to 64 heads per group (G*D <= 4096); plain
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     for (int dt = 0; dt < GA::DT; ++dt) {
       const f32x4 a = ga.acc[dt] * inv;
       const u32x2 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-      st8_nt(orow + dt * 16 + grp * 4, w);
+      st8(orow + dt * 16 + grp * 4, w);
     }
     if (lse && grp == 0)
       lse[((int64_t)b * Hq + h) * T + t] = l > 0.f ? (ga.m_run + __log2f(l)) * kLn2 : -INFINITY;

@@ -41,9 +41,6 @@ __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ void st8_nt(void* p, u32x2 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
-}
 __device__ __forceinline__ int ld_nt(const int* p) { return __builtin_nontemporal_load(p); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=8192, help="indexer/top-k rows per chunk")
+    ap.add_argument("--indices", choices=["fused", "two-step"], default="fused",
+                    help="how the step builds the indices: sa_indexer_topk, or "
+                         "sa_indexer_scores + sa_topk_select")
     ap.add_argument("--no-extra", action="store_true", help="skip graph/decode/reuse rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -142,16 +145,27 @@ def main():
     q, k, v = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16")
     chunk = min(args.chunk, T)
     ld = ((T + 3) // 4) * 4
+    fused = args.indices == "fused"
     scores = torch.empty((1, chunk, ld), dtype=torch.float32, device=dev)
+    # the last row chunk is the longest, so its workspace serves every chunk
+    ws = torch.empty(sa.sa_indexer_topk_workspace(1, T, HI, DI, T - chunk, T, topk),
+                     dtype=torch.uint8, device=dev)
     idx = torch.full((1, T, topk), -1, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     tm = Timer(torch)
 
-    def prefill_indices(timer):
+    def two_step_indices(timer):
         for r0 in range(0, T, chunk):
             r1 = min(T, r0 + chunk)
             timer.run("indexer", lambda: sa.sa_indexer_scores(qi, ki, w, r0, r1, scores, ld))
             timer.run("topk", lambda: sa.sa_topk_select(scores, topk, T, r0, r1, idx, ld))
+
+    def fused_indices(timer):
+        for r0 in range(0, T, chunk):
+            r1 = min(T, r0 + chunk)
+            timer.run("indexer_topk", lambda: sa.sa_indexer_topk(qi, ki, w, topk, r0, r1, idx, ws))
+
+    prefill_indices = fused_indices if fused else two_step_indices
 
     def step(timer):
         if args.only != "attn":
@@ -176,7 +190,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_step = total_ms / args.steps
-    kern = {n: tm.ms(n) for n in ("indexer", "topk", "attn")}
+    kern = {n: tm.ms(n) for n in ("indexer_topk", "indexer", "topk", "attn")}
     log("timed: " + ", ".join(f"{n} {m / max(1, args.steps):.3f} ms/step ({c} launches)"
                               for n, (m, c) in kern.items()))
 
@@ -194,8 +208,24 @@ def main():
     attn_avg_ms = attn_ms / max(1, attn_n)
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9 if attn_n else None
 
-    idx_ms = kern["indexer"][0] / args.steps
-    topk_ms = kern["topk"][0] / args.steps
+    # the other way of building the indices, timed beside (not part of the step)
+    other = Timer(torch)
+    if args.only != "attn":
+        (two_step_indices if fused else fused_indices)(Timer(torch))
+        for _ in range(3):
+            (two_step_indices if fused else fused_indices)(other)
+        torch.cuda.synchronize()
+        if fused:
+            prefill_indices(Timer(torch))  # leave the step's own indices in idx
+            torch.cuda.synchronize()
+    tsrc = other if fused else tm
+    nsteps_two = 3 if fused else args.steps
+    idx_ms = tsrc.ms("indexer")[0] / nsteps_two
+    topk_ms = tsrc.ms("topk")[0] / nsteps_two
+    fsrc = tm if fused else other
+    nsteps_f = args.steps if fused else 3
+    fused_ms = fsrc.ms("indexer_topk")[0] / nsteps_f
+    n_recomputed = int(ws[:4].view(torch.int32).item()) if fused_ms else None
     n_pairs = T * (T + 1) // 2
     res = {
         "metric": "sparse-attn fwd query-tokens/s at 64K ctx, top-k=2048; % HBM/MFMA roofline",
@@ -213,8 +243,9 @@ def main():
         "config": {"workload": "dsa-prefill-bf16-64k: indexer(4x64) + top-2048 + window-128 "
                                "sparse attention, T=65536, Hq=16, Hkv=1, D=128, batch 1",
                    "global_batch": 1, "seq_len": T, "parallelism": "none (1 GPU)",
-                   "row_chunk": chunk, "only": args.only},
-        "step_breakdown_ms": {"indexer": idx_ms, "topk": topk_ms, "sparse_attn": attn_avg_ms},
+                   "row_chunk": chunk, "indices": args.indices, "only": args.only},
+        "step_breakdown_ms": ({"indexer_topk": fused_ms} if fused else
+                              {"indexer": idx_ms, "topk": topk_ms}) | {"sparse_attn": attn_avg_ms},
         "sparse_attn_query_tokens_per_s": T / (attn_avg_ms * 1e-3) if attn_n else None,
         "roofline": {
             "kernel": "sparse_attn_mfma<128>",
@@ -228,6 +259,15 @@ def main():
             "selected_keys_per_launch": n_sel,
             "avg_launch_ms": attn_avg_ms,
             "mfma_tflops": attn_flops / (attn_avg_ms * 1e-3) / 1e12 if attn_n else None,
+        },
+        "indexer_topk": {
+            "avg_ms_per_step": fused_ms,
+            "effective_tflops": (n_pairs * 2 * HI * DI) / (fused_ms * 1e-3) / 1e12
+            if fused_ms else None,
+            "mfma_frac": ((n_pairs * 2 * HI * DI) / (fused_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+            if fused_ms else None,
+            "rows_recomputed_last_chunk": n_recomputed,
+            "vs_two_step": (idx_ms + topk_ms) / fused_ms if fused_ms and idx_ms else None,
         },
         "indexer": {
             "avg_ms_per_step": idx_ms,
@@ -246,7 +286,7 @@ def main():
             "NSA": "9x forward speedup at 64K, NVIDIA GPUs",
         },
     }
-    del scores
+    del scores, ws
     torch.cuda.empty_cache()
 
     if not args.no_extra:
@@ -349,16 +389,15 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         layers.append(tuple(to_dev(lx[n], "bf16") for n in ("q", "k", "v")))
         del lx
     chunk = 8192
-    ld = T
-    sc = torch.empty((1, chunk, ld), dtype=torch.float32, device=dev)
+    ws = torch.empty(sa.sa_indexer_topk_workspace(1, T, p["H_I"], p["D_I"], T - chunk, T,
+                                                  p["topk"]), dtype=torch.uint8, device=dev)
     idx = torch.full((1, T, p["topk"]), -1, dtype=torch.int32, device=dev)
     o4 = torch.empty_like(layers[0][0])
 
     def index_once():
         for r0 in range(0, T, chunk):
             r1 = min(T, r0 + chunk)
-            sa.sa_indexer_scores(qi, ki, w, r0, r1, sc, ld)
-            sa.sa_topk_select(sc, p["topk"], T, r0, r1, idx, ld)
+            sa.sa_indexer_topk(qi, ki, w, p["topk"], r0, r1, idx, ws)
 
     def attn(l):
         qq, kk, vv = layers[l]
@@ -374,7 +413,7 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         "indexer_time_saved_ms": 3 * t_index, "saved_frac": 3 * t_index / no_reuse,
         "attn_query_tokens_per_s": T / (sum(t_attn) / 4 * 1e-3),
     }
-    del sc, idx, layers, qi, ki, w, o4
+    del ws, idx, layers, qi, ki, w, o4
     torch.cuda.empty_cache()
     return rows
 

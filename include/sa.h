@@ -90,6 +90,38 @@ int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
                    int k, int32_t* idx, void* stream);
 
 /*
+ * Fused indexer scores + top-k selection.  [IC] body paragraphs 2-3 (the indexer scores
+ * every earlier token; only the selected subset is used afterwards).
+ *
+ * Writes to idx[b, t, 0:k], for t in [row_begin, row_end), exactly what
+ * sa_indexer_scores followed by sa_topk_select write (bit for bit), without
+ * materialising the score matrix: a strided sample of each row's scores gives a
+ * threshold, only scores above it are kept (per 256-key chunk, in position order), and
+ * the exact selection runs over those (in registers up to 4096 kept scores, else by
+ * passes over the kept lists).  A row whose kept set turns out smaller than k is
+ * recomputed in full inside the call; the result never depends on the inputs'
+ * distribution, only the time does.
+ *
+ * qi [B, T, H_I, D_I] bf16; ki [B, T, D_I] bf16; w [H_I] float32; idx [B, T, k] int32.
+ * workspace: device memory of at least sa_indexer_topk_workspace(...) bytes, no
+ * initialisation needed; it holds per-row samples, thresholds and candidate lists
+ * (about (row_end / 256) * 2 KB per row), so long rows are best processed in row chunks.
+ * Once the call has run, the first 4 bytes of the workspace hold, as a uint32, the
+ * number of rows that were recomputed in full (a diagnostic; 0 in the usual case).  The
+ * kept set is about 1.3-1.6 k entries; beyond k of about 3000 most rows are selected by
+ * list passes, which is slower (the two-step path may be faster there).
+ * Requires bf16, H_I in {1, 2, 4}, D_I in {32, 64, 128} (else SA_ERR_UNSUPPORTED: use the
+ * two-step path), 1 <= k <= 4096, 0 <= row_begin < row_end <= T <= 262144.
+ */
+int sa_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T, int H_I,
+                    int D_I, int dtype, int row_begin, int row_end, int k, int32_t* idx,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes sa_indexer_topk needs for these sizes (0 on invalid sizes). */
+size_t sa_indexer_topk_workspace(int B, int T, int H_I, int D_I, int row_begin, int row_end,
+                                 int k);
+
+/*
  * Sparse attention forward over the selected set.  [IC] body paragraph 2 (attend only
  * to the selected subset), [HS2] "Dos niveles ..." (the most recent tokens are forced
  * into the set), [NSA] "Análisis Profundo" (one selection and one K/V fetch shared by

@@ -35,6 +35,10 @@ _SIGS = {
                                    _c_int, _c_int, _c_int, _c_void_p, _c_int64, _c_void_p]),
     "sa_topk_select": (_c_int, [_c_void_p, _c_int64, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 _c_void_p, _c_void_p]),
+    "sa_indexer_topk": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_size_t,
+                                 _c_void_p]),
+    "sa_indexer_topk_workspace": (_c_size_t, [_c_int] * 7),
     "sa_sparse_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_void_p, _c_void_p, _c_void_p]),
@@ -180,6 +184,34 @@ def sa_topk_select(scores, k: int, T: int, row_begin: int = 0, row_end: int | No
     rc = lib().sa_topk_select(_p(scores), ld, B, T, row_begin, row_end, k, _p(idx),
                               _stream(scores.device))
     _check("sa_topk_select", rc)
+    return idx
+
+
+def sa_indexer_topk_workspace(B, T, H_I, D_I, row_begin, row_end, k) -> int:
+    return int(lib().sa_indexer_topk_workspace(B, T, H_I, D_I, row_begin, row_end, k))
+
+
+def sa_indexer_topk(qi, ki, w, k: int, row_begin: int = 0, row_end: int | None = None,
+                    idx=None, workspace=None):
+    """Fused indexer + top-k: the idx rows [row_begin, row_end) that sa_indexer_scores
+    followed by sa_topk_select would write, without the score matrix.  qi [B,T,H_I,D_I],
+    ki [B,T,D_I] bf16, w [H_I] f32; ``idx`` [B,T,k] int32; ``workspace`` (uint8, no
+    initialisation needed) is allocated when not given."""
+    torch = _torch()
+    _dev(qi, "qi"); _dev(ki, "ki", qi.dtype); _dev(w, "w", torch.float32)
+    B, T, H, DI = qi.shape
+    row_end = T if row_end is None else row_end
+    need = sa_indexer_topk_workspace(B, T, H, DI, row_begin, row_end, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=qi.device)
+    _dev(workspace, "workspace", torch.uint8)
+    if idx is None:
+        idx = torch.full((B, T, k), -1, dtype=torch.int32, device=qi.device)
+    _dev(idx, "idx", torch.int32)
+    rc = lib().sa_indexer_topk(_p(qi), _p(ki), _p(w), B, T, H, DI, _dtype_code(qi), row_begin,
+                               row_end, k, _p(idx), _p(workspace), workspace.numel(),
+                               _stream(qi.device))
+    _check("sa_indexer_topk", rc)
     return idx
 
 

@@ -30,6 +30,14 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags: the indexer kernels keep their MFMA accumulators in VGPRs
+# (the epilogue reads every accumulator element, so AGPR copies would cost VALU slots).
+EXTRA_FLAGS = {
+    "k_indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "k_indexer_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -45,7 +53,8 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc(), *FLAGS, *lang, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *lang, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

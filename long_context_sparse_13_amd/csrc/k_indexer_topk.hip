@@ -1,0 +1,631 @@
+// Fused indexer -> top-k: the exact per-row top-k of the indexer scores without writing
+// the score matrix.
+//
+// [IC] IndexCache page, body paragraphs 2-3: the indexer scores every earlier token
+// and only a small subset is kept; writing and re-reading all scores (4 bytes per
+// (t, s) pair) is what bounds the two-step path, so here the scores stay on chip.
+//
+// The result is the same as sa_indexer_scores followed by sa_topk_select, bit for bit:
+// every kernel below scores through IdxWave (indexer_tile.h), so a (t, s) score is the
+// same float32 value wherever it is computed.
+//
+//  1. sample  (indexer_mfma, sshift > 0): scores of the key slots s = j * 2^sshift.
+//  2. sample_threshold: per row, thr = a lower bound of the jrank-th largest sample score
+//     (the floor of its 22-bit key prefix).  About k / 2^sshift sampled scores are
+//     expected above the row's k-th largest score; jrank adds four standard deviations,
+//     so thr is almost always below the k-th largest score.
+//  3. indexer_cand: full MFMA scoring of 32 rows x 64 keys per wavefront step, staged in
+//     LDS; then, row by row, one ballot over the 64 keys finds the scores >= thr, which
+//     go as (score bits, position) to the row's list for that 256-key chunk, in position
+//     order (list length in counts[row, chunk]).  Nothing else is written.
+//  4. cand_topk: one wavefront per row; the chunk lists, concatenated in position order,
+//     are spread over the lanes' registers (up to 4096 entries) and the exact top-k is
+//     taken from them: a radix select whose digits cover only the key range actually
+//     present (so a few hot bins do not serialise the histogram), then output ranks
+//     from two wavefront scans.  Every score >= thr is in the lists, so when they hold
+//     at least k entries they hold the k largest.  Rows with more than 4096 entries are
+//     selected with streaming passes over the lists instead; rows with fewer than k (thr
+//     was above the k-th score) are recomputed in full into their own list area and
+//     selected there with passes over global memory: the answer is exact in every case.
+#include "indexer_tile.h"
+#include "sa_launch.h"
+#include "sa_device.h"
+
+#include <type_traits>
+
+namespace sa {
+
+namespace {
+
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key ^ 0x80000000u) : ~key;
+  return __uint_as_float(u);
+}
+
+// Within one wavefront: the bin d (of nb bins in h, top bin first) holding the kk-th
+// largest element, kk minus the count above it, and whether that is the bin's whole
+// count.  Lane L owns bins [top - per + 1, top], top = nb - 1 - L * per.
+__device__ __forceinline__ void wave_find_bin(const uint32_t* h, int nb, int kk, int lane,
+                                              int& digit, int& rem, bool& whole) {
+  const int per = (nb + 63) / 64;
+  const int top = nb - 1 - lane * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (top - i >= 0) local += (int)h[top - i];
+  int total;
+  const int above0 = wave_excl_sum(local, total);
+  const bool mine = above0 < kk && kk <= above0 + local;
+  int d = 0, r = 0, wh = 0;
+  if (mine) {
+    int above = above0;
+    for (int i = 0; i < per; ++i) {
+      const int c = top - i >= 0 ? (int)h[top - i] : 0;
+      if (above + c >= kk) {
+        d = top - i;
+        r = kk - above;
+        wh = r == c;
+        break;
+      }
+      above += c;
+    }
+  }
+  const int src = (int)__builtin_ctzll(ballot(mine));
+  digit = __builtin_amdgcn_readlane(d, src);
+  rem = __builtin_amdgcn_readlane(r, src);
+  whole = __builtin_amdgcn_readlane(wh, src) != 0;
+}
+
+__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+}
+
+constexpr int kRadixBins = 1024;
+
+// One wavefront: the kk-th largest key v among the keys its lanes enumerate with
+// for_each(f) (all within [lo, lo + span]) and take = how many keys equal to v are kept
+// (keys > v are all kept).  Radix digits of up to 10 bits over the remaining range
+// (bins hold (key - lo) >> shift); stops early when the digit holding the kk-th key is
+// kept whole.
+template <typename ForEach>
+__device__ __forceinline__ void wave_radix_kth(uint32_t lo, uint32_t span, int kk,
+                                               ForEach&& for_each, uint32_t* hist, int lane,
+                                               uint32_t& v, int& take) {
+  for (;;) {
+    const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
+    const int shift = bits > 10 ? bits - 10 : 0;
+    const int nb = (int)(span >> shift) + 1;
+    for (int i = lane; i < nb; i += 64) hist[i] = 0u;
+    wave_lds_sync();
+    for_each([&](uint32_t key) {
+      const uint32_t d = key - lo;
+      if (key >= lo && d <= span) atomicAdd(&hist[d >> shift], 1u);
+    });
+    wave_lds_sync();
+    int dbin, rem;
+    bool wh;
+    wave_find_bin(hist, nb, kk, lane, dbin, rem, wh);
+    const uint32_t bin = (uint32_t)dbin;
+    wave_lds_sync();  // hist is rewritten by the next round
+    const uint32_t blo = lo + (bin << shift);
+    if (shift == 0) {
+      v = blo;
+      take = rem;
+      return;
+    }
+    if (wh) {  // every key of the bin is kept: keep keys >= blo
+      v = blo - 1u;
+      take = 0;
+      return;
+    }
+    lo = blo;
+    span = (1u << shift) - 1u;
+    kk = rem;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- 2. thresholds
+// One wavefront per row.  thr = +inf for rows that keep all their positions (t + 1 <= k),
+// -inf when the row has no more than jrank samples (every score is a candidate).
+// Block 0 also clears the recompute counter of this call.
+__global__ __launch_bounds__(256) void sample_threshold(const float* __restrict__ samp,
+                                                        int64_t lds, int B, int row_begin,
+                                                        int row_end, int k, int sshift,
+                                                        int jrank, float* __restrict__ thr,
+                                                        uint32_t* __restrict__ n_recomputed) {
+  __shared__ uint32_t hist[4][2048];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_recomputed = 0u;
+  const int R = row_end - row_begin;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+  if (item >= (int64_t)B * R) return;
+  const int t = row_begin + (int)(item % R);
+  if (t + 1 <= k || ((t >> sshift) + 1) <= jrank) {
+    if (lane == 0) thr[item] = t + 1 <= k ? INFINITY : -INFINITY;
+    return;
+  }
+  const int ns = (t >> sshift) + 1;
+  const float* __restrict__ row = samp + item * lds;
+  uint32_t* h = hist[wv];
+
+  for (int i = lane; i < 2048; i += 64) h[i] = 0u;
+  wave_lds_sync();
+  for (int e = lane; e < ns; e += 64) atomicAdd(&h[order_key(row[e]) >> 21], 1u);
+  wave_lds_sync();
+  int d1, j1;
+  bool w1;
+  wave_find_bin(h, 2048, jrank, lane, d1, j1, w1);
+  wave_lds_sync();
+  for (int i = lane; i < 2048; i += 64) h[i] = 0u;
+  wave_lds_sync();
+  for (int e = lane; e < ns; e += 64) {
+    const uint32_t key = order_key(row[e]);
+    if ((int)(key >> 21) == d1) atomicAdd(&h[(key >> 10) & 2047u], 1u);
+  }
+  wave_lds_sync();
+  int d2, j2;
+  bool w2;
+  wave_find_bin(h, 2048, j1, lane, d2, j2, w2);
+  if (lane == 0) thr[item] = key_to_float(((uint32_t)d1 << 21) | ((uint32_t)d2 << 10));
+}
+
+// ---------------------------------------------------------------- 3. candidates
+template <int H, int DI>
+__global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__ qi,
+                                                     const uint16_t* __restrict__ ki,
+                                                     const float* __restrict__ wgt, int T,
+                                                     int row_begin, int row_end, int k,
+                                                     const float* __restrict__ thr,
+                                                     uint16_t* __restrict__ counts,
+                                                     u32x2* __restrict__ cand, int nch) {
+  using IW = IdxWave<H, DI>;
+  constexpr int KS = IW::KS;
+  constexpr int SB = 64;        // keys per staged block (4 tiles)
+  constexpr int SROW = SB + 4;  // padded LDS row (floats)
+  __shared__ __attribute__((aligned(16))) float stage[kIdxWaves][IW::ROWS * SROW];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, grp = lane >> 4;
+  const int R = row_end - row_begin;
+  const int strips = (R + kIdxStrip - 1) / kIdxStrip;
+  const int strip = strips - 1 - (int)(blockIdx.x / kIdxGroups);  // longest strips first
+  const int group = (int)(blockIdx.x % kIdxGroups);
+  const int b = blockIdx.y;
+  const int t0 = row_begin + strip * kIdxStrip + wv * IW::ROWS;
+  if (t0 >= row_end) return;
+  const int t_last = min(t0 + IW::ROWS, row_end) - 1;
+  if (t_last < k) return;  // every row of this wavefront keeps all its positions
+  const int wave_chunks = t_last / kIdxChunk + 1;
+
+  IW iw;
+  iw.load(qi + (int64_t)b * T * H * DI, t0, row_end, wgt, n, grp);
+  const uint16_t* kib = ki + (int64_t)b * T * DI;
+  float* st = stage[wv];
+
+  // row rr of the wavefront is kept by lane rr: its threshold (+inf: no candidates)
+  const int my_t = t0 + (lane & 31);
+  const bool my_ok = lane < IW::ROWS && my_t < row_end && my_t >= k;
+  const float thr_v = my_ok ? thr[(int64_t)b * R + (my_t - row_begin)] : INFINITY;
+  const int64_t row0 = (int64_t)b * R + (t0 - row_begin);
+
+  for (int c = group; c < wave_chunks; c += kIdxGroups) {
+    const int s_lo = c * kIdxChunk;
+    const int s_hi = min(s_lo + kIdxChunk, t_last + 1);
+    uint32_t cnt_s[IW::ROWS];  // list length of row rr in this chunk so far (uniform)
+#pragma unroll
+    for (int rr = 0; rr < IW::ROWS; ++rr) cnt_s[rr] = 0u;
+    u32x4 bk[KS];
+    IW::load_keys(kib, min(s_lo + n, T - 1), grp, bk);
+    for (int j0 = s_lo; j0 < s_hi; j0 += SB) {
+#pragma unroll
+      for (int nt = 0; nt < SB / 16; ++nt) {
+        u32x4 bn[KS];
+        IW::load_keys(kib, min(j0 + nt * 16 + 16 + n, T - 1), grp, bn);
+        float sc[IW::NSC];
+        iw.scores(bk, sc);
+#pragma unroll
+        for (int i = 0; i < IW::NSC; ++i) st[IW::token(i, grp) * SROW + nt * 16 + n] = sc[i];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = bn[ks];
+      }
+      wave_lds_sync();
+      // ---- row by row: one lane per key of the block
+      const int s = j0 + lane;
+      float vals[IW::ROWS];
+#pragma unroll
+      for (int rr = 0; rr < IW::ROWS; ++rr) vals[rr] = st[rr * SROW + lane];
+      auto compact = [&](auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        u32x2* rowp = cand + (row0 * nch + c) * kIdxChunk;  // list of row rr in chunk c
+#pragma unroll
+        for (int rr = 0; rr < IW::ROWS; ++rr) {
+          const float th = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr_v), rr));
+          const bool hit = vals[rr] >= th && (!DIAG || s <= t0 + rr);
+          const uint64_t m = ballot(hit);
+          if (m) {
+            const uint32_t base = cnt_s[rr];
+            if (hit) rowp[base + (uint32_t)lanes_below(m)] = u32x2{__float_as_uint(vals[rr]), (uint32_t)s};
+            cnt_s[rr] = base + (uint32_t)__popcll(m);
+          }
+          rowp += (int64_t)nch * kIdxChunk;
+        }
+      };
+      if (j0 + SB - 1 > t0) compact(std::true_type{});  // some key follows some row
+      else compact(std::false_type{});
+      wave_lds_sync();
+    }
+    uint32_t cnt_v = 0u;  // lane rr takes cnt_s[rr]
+#pragma unroll
+    for (int rr = 0; rr < IW::ROWS; ++rr) cnt_v = lane == rr ? cnt_s[rr] : cnt_v;
+    if (my_ok) counts[(row0 + lane) * nch + c] = (uint16_t)cnt_v;
+  }
+}
+
+// ---------------------------------------------------------------- 4. selection
+// One wavefront per row (4 rows per workgroup, longest rows first).  The row's
+// non-empty chunk lists, concatenated in position order, are held in registers with
+// entry e = 64 j + lane in slot j (up to 64 slots: 4096 entries), so that loads and the
+// output stores of a slot are contiguous.  The list holding entry e is found from a
+// table in LDS that marks where each list starts, with a running maximum over the lanes.
+constexpr int kCandPerLane = 64;
+constexpr int kMarkCap = 64 * kCandPerLane;  // entries the mark table covers
+
+template <int H, int DI>
+__global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi,
+                                                  const uint16_t* __restrict__ ki,
+                                                  const float* __restrict__ wgt, int B, int T,
+                                                  int row_begin, int row_end, int k,
+                                                  const uint16_t* __restrict__ counts,
+                                                  u32x2* __restrict__ cand, int nch,
+                                                  int32_t* __restrict__ idx,
+                                                  uint32_t* __restrict__ n_recomputed) {
+  using IW = IdxWave<H, DI>;
+  constexpr int J = kCandPerLane;
+  // per wavefront: the list-start marks (during the gather) or the radix histogram
+  __shared__ uint32_t work_s[4][kMarkCap / 2 > kRadixBins ? kMarkCap / 2 : kRadixBins];
+  __shared__ uint32_t nz_s[4][1028];  // (chunk << 16) | list offset, non-empty lists only
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = row_end - row_begin;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+  if (item >= (int64_t)B * R) return;
+  const int b = (int)(item / R);
+  const int r = R - 1 - (int)(item % R);  // longest rows first
+  const int t = row_begin + r;
+  const int n = t + 1;
+  int32_t* __restrict__ out = idx + ((int64_t)b * T + t) * k;
+  if (n <= k) {
+    for (int i = lane; i < k; i += 64) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int64_t rowi = (int64_t)b * R + r;
+  const uint16_t* __restrict__ cr = counts + rowi * nch;
+  u32x2* __restrict__ cl = cand + rowi * nch * kIdxChunk;
+  uint32_t* hist = work_s[wv];
+  uint16_t* mark = reinterpret_cast<uint16_t*>(work_s[wv]);
+  uint32_t* nz = nz_s[wv];
+  const int nc = t / kIdxChunk + 1;  // chunks of this row (<= 1024)
+
+  // ---- list lengths: lane L holds chunks 256 g + 4 L + i (g < 4, i < 4) in registers
+  uint32_t len4[4][2];  // two u16 lengths per word
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int c = 256 * g + 4 * lane;
+    u32x2 x = {0u, 0u};
+    if (c < nc) x = *reinterpret_cast<const u32x2*>(cr + c);  // (nch is a multiple of 4)
+    len4[g][0] = x[0];
+    len4[g][1] = x[1];
+  }
+  auto len_of = [&](int g, int i) -> int {
+    const int c = 256 * g + 4 * lane + i;
+    return c < nc ? (int)((len4[g][i >> 1] >> (16 * (i & 1))) & 0xffffu) : 0;
+  };
+  int n_hits = 0, n_nz = 0, run[4], zrun[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    int l = 0, z = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l += len_of(g, i);
+      z += len_of(g, i) > 0;
+    }
+    int tl, tz;
+    run[g] = n_hits + wave_excl_sum(l, tl);
+    zrun[g] = n_nz + wave_excl_sum(z, tz);
+    n_hits += tl;
+    n_nz += tz;
+  }
+
+  uint32_t v;
+  int take_eq;
+  if (n_hits >= k && n_hits <= 64 * J) {
+    // ---- the non-empty lists (chunk, offset), and a mark where each one starts
+    const int nw = (n_hits + 1) / 2;
+    for (int i = lane; i < nw; i += 64) work_s[wv][i] = 0xffffffffu;  // no mark
+    wave_lds_sync();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      int o = run[g], zo = zrun[g];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int x = len_of(g, i);
+        if (x > 0) {
+          nz[zo] = ((uint32_t)(256 * g + 4 * lane + i) << 16) | (uint32_t)o;
+          mark[o] = (uint16_t)zo;
+          ++zo;
+        }
+        o += x;
+      }
+    }
+    wave_lds_sync();
+    // ---- gather: slot j holds entry 64 j + lane
+    uint32_t key[J];
+    int pos[J];
+    int carry = 0;  // list of the previous slot's last entry
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (64 * j < n_hits) {
+        const int e = 64 * j + lane;
+        const int mk = e < n_hits ? (mark[e] == 0xffffu ? -1 : (int)mark[e]) : -1;
+        const int m = max(carry, wave_incl_scan(mk, -1, [](int x, int y) { return max(x, y); }));
+        carry = __builtin_amdgcn_readlane(m, 63);
+        if (e < n_hits) {
+          const uint32_t info = nz[m];
+          const u32x2 ent = cl[(int64_t)(info >> 16) * kIdxChunk + (e - (int)(info & 0xffffu))];
+          key[j] = ent[0];
+          pos[j] = (int)ent[1];
+        }
+      }
+    }
+    const int jn = (n_hits + 63) / 64;  // slots in use (the last one partly)
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (j < jn && 64 * j + lane < n_hits) {
+        key[j] = order_key(__uint_as_float(key[j]));
+        mn = min(mn, key[j]);
+        mx = max(mx, key[j]);
+      }
+    }
+    wave_minmax(mn, mx);
+    wave_lds_sync();  // the marks are dead: the histogram takes their place
+    wave_radix_kth(mn, mx - mn, k,
+                   [&](auto&& f) {
+#pragma unroll
+                     for (int j = 0; j < J; ++j)
+                       if (j < jn && 64 * j + lane < n_hits) f(key[j]);
+                   },
+                   hist, lane, v, take_eq);
+    // ---- output: per slot, ranks from ballots (keys > v; the first take_eq keys == v)
+    int gr = 0, er = 0;  // kept keys > v and keys == v in the slots before
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (j < jn) {
+        const bool in = 64 * j + lane < n_hits;
+        const bool g = in && key[j] > v, e = in && key[j] == v;
+        const uint64_t mg = ballot(g), me = ballot(e);
+        const int gb = gr + lanes_below(mg), eb = er + lanes_below(me);
+        if (g) out[gb + min(eb, take_eq)] = pos[j];
+        else if (e && eb < take_eq) out[gb + eb] = pos[j];
+        gr += __popcll(mg);
+        er += __popcll(me);
+      }
+    }
+    return;
+  }
+
+  if (n_hits > k) {
+    // ---- more entries than the registers hold: streaming passes over the lists, lane L
+    // taking the chunks L, L + 64, ... (each list read in batches of 16 entries)
+    auto each_entry = [&](int c, auto&& f) {
+      const int len = cr[c];
+      const u32x2* src = cl + (int64_t)c * kIdxChunk;
+      for (int e0 = 0; e0 < len; e0 += 16) {
+        u32x2 ev[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (e0 + u < len) ev[u] = src[e0 + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (e0 + u < len) f(order_key(__uint_as_float(ev[u][0])), (int)ev[u][1]);
+      }
+    };
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for (int c = lane; c < nc; c += 64)
+      each_entry(c, [&](uint32_t key, int) {
+        mn = min(mn, key);
+        mx = max(mx, key);
+      });
+    wave_minmax(mn, mx);
+    wave_radix_kth(mn, mx - mn, k,
+                   [&](auto&& f) {
+                     for (int c = lane; c < nc; c += 64)
+                       each_entry(c, [&](uint32_t key, int) { f(key); });
+                   },
+                   hist, lane, v, take_eq);
+    // output in chunk order: 64 consecutive chunks per round, one per lane
+    int gsum = 0, esum = 0;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const int c = c0 + lane;
+      int ng = 0, ne = 0;
+      if (c < nc)
+        each_entry(c, [&](uint32_t key, int) {
+          ng += key > v;
+          ne += key == v;
+        });
+      int tg, te;
+      int gb = gsum + wave_excl_sum(ng, tg);
+      int eb = esum + wave_excl_sum(ne, te);
+      gsum += tg;
+      esum += te;
+      if (c < nc)
+        each_entry(c, [&](uint32_t key, int p) {
+          const bool g = key > v, e = key == v;
+          const int at = g ? gb + min(eb, take_eq) : gb + eb;
+          if (g || (e && eb < take_eq)) out[at] = p;
+          gb += g;
+          eb += e;
+        });
+    }
+    return;
+  }
+
+  // ---- fewer entries than k (the threshold was above the k-th score): recompute the
+  // row in full into its own list area (16-byte aligned, (t/256 + 1) * 2 KB >= 4 (t + 1)
+  // bytes) and select there
+  if (lane == 0) atomicAdd(n_recomputed, 1u);
+  float* frow = reinterpret_cast<float*>(cl);
+  {
+    IW iw;
+    iw.load_single(qi + (int64_t)b * T * H * DI, t, wgt, lane & 15, lane >> 4);
+    const uint16_t* kib = ki + (int64_t)b * T * DI;
+    constexpr int U = 16;  // key tiles in flight
+    for (int kt0 = 0; kt0 * 16 <= t; kt0 += U) {
+      u32x4 bk[U][IW::KS];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        IW::load_keys(kib, min((kt0 + u) * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float sc = iw.score_single(bk[u]);
+        const int key = (kt0 + u) * 16 + (lane & 15);
+        if (lane < 16 && key <= t) frow[key] = sc;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");  // the row's stores are complete
+  // lane L owns the positions [lo_e, hi_e) (whole float4s)
+  const int seg = ((n + 63) / 64 + 3) & ~3;
+  const int lo_e = min(n, lane * seg), hi_e = min(n, lo_e + seg);
+  auto each_key = [&](auto&& f) {
+    for (int e = lo_e; e < hi_e; e += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(frow + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e + u < hi_e) f(order_key(x[u]), e + u);
+    }
+  };
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  each_key([&](uint32_t key, int) {
+    mn = min(mn, key);
+    mx = max(mx, key);
+  });
+  wave_minmax(mn, mx);
+  wave_radix_kth(mn, mx - mn, k,
+                 [&](auto&& f) { each_key([&](uint32_t key, int) { f(key); }); }, hist, lane,
+                 v, take_eq);
+  int ng = 0, ne = 0;
+  each_key([&](uint32_t key, int) {
+    ng += key > v;
+    ne += key == v;
+  });
+  int tg, te;
+  int gb = wave_excl_sum(ng, tg);
+  int eb = wave_excl_sum(ne, te);
+  each_key([&](uint32_t key, int e) {
+    if (key > v) {
+      out[gb + min(eb, take_eq)] = e;
+      ++gb;
+    } else if (key == v) {
+      if (eb < take_eq) out[gb + eb] = e;
+      ++eb;
+    }
+  });
+}
+
+// ---------------------------------------------------------------- host side
+namespace {
+
+struct IdxTopkPlan {
+  int sshift, jrank, nch;
+  int64_t ns_ld;
+  size_t off_stat, off_samp, off_thr, off_cnt, off_cand, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+IdxTopkPlan plan_indexer_topk(int B, int row_begin, int row_end, int k) {
+  IdxTopkPlan p{};
+  // sample stride 2^sshift: about kf0 .. 2 kf0 sampled scores above the k-th largest.  The
+  // candidate lists then hold about (1 + 4 / sqrt(kf0)) k entries: kf0 = 64 for k <= 2048,
+  // 256 above, so that they fit the 4096 entries held in registers up to k of about 3000
+  const int kf0 = k <= 2048 ? 64 : 256;
+  int sshift = 0;
+  while ((k >> (sshift + 1)) >= kf0) ++sshift;
+  const int kf = k >> sshift;
+  int sq = 0;
+  while (sq * sq < kf) ++sq;
+  p.sshift = sshift;
+  p.jrank = kf + 4 * sq + 4;
+  p.nch = ((row_end - 1) / kIdxChunk + 1 + 3) / 4 * 4;  // multiple of 4: 8-byte count loads
+  p.ns_ld = ((int64_t)((row_end - 1) >> sshift) + 1 + 3) / 4 * 4;
+  const int64_t rows = (int64_t)B * (row_end - row_begin);
+  size_t o = 0;
+  p.off_stat = o;  // uint32: rows recomputed in full by the last call
+  o = align256(o + sizeof(uint32_t));
+  p.off_samp = o;
+  o = align256(o + (size_t)rows * p.ns_ld * sizeof(float));
+  p.off_thr = o;
+  o = align256(o + (size_t)rows * sizeof(float));
+  p.off_cnt = o;
+  o = align256(o + (size_t)rows * p.nch * sizeof(uint16_t));
+  p.off_cand = o;
+  o = align256(o + (size_t)rows * p.nch * kIdxChunk * sizeof(u32x2));
+  p.total = o;
+  return p;
+}
+
+}  // namespace
+
+size_t indexer_topk_workspace_bytes(int B, int row_begin, int row_end, int k) {
+  return plan_indexer_topk(B, row_begin, row_end, k).total;
+}
+
+hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T,
+                               int H_I, int D_I, int row_begin, int row_end, int k,
+                               int32_t* idx, void* workspace, hipStream_t st) {
+  const IdxTopkPlan p = plan_indexer_topk(B, row_begin, row_end, k);
+  char* ws = static_cast<char*>(workspace);
+  float* samp = reinterpret_cast<float*>(ws + p.off_samp);
+  float* thr = reinterpret_cast<float*>(ws + p.off_thr);
+  uint16_t* cnt = reinterpret_cast<uint16_t*>(ws + p.off_cnt);
+  u32x2* cand = reinterpret_cast<u32x2*>(ws + p.off_cand);
+  uint32_t* stat = reinterpret_cast<uint32_t*>(ws + p.off_stat);
+  const int R = row_end - row_begin;
+
+  // the sample: slot chunks of 64 spread the short sampled rows over more workgroups
+  hipError_t e = launch_indexer_mfma(qi, ki, w, B, T, H_I, D_I, row_begin, row_end, p.sshift,
+                                     p.sshift > 0 ? 64 : kIdxChunk, samp, p.ns_ld, st);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)B * R;
+  hipLaunchKernelGGL(sample_threshold, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, samp,
+                     p.ns_ld, B, row_begin, row_end, k, p.sshift, p.jrank, thr, stat);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  const int strips = (R + kIdxStrip - 1) / kIdxStrip;
+  const dim3 g3((unsigned)(strips * kIdxGroups), (unsigned)B);
+  const dim3 g4((unsigned)((rows + 3) / 4));
+#define SA_IDXTK(HH, DD)                                                                        \
+  do {                                                                                          \
+    hipLaunchKernelGGL((indexer_cand<HH, DD>), g3, dim3(256), 0, st, (const uint16_t*)qi,       \
+                       (const uint16_t*)ki, w, T, row_begin, row_end, k, thr, cnt, cand,        \
+                       p.nch);                                                                  \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                                        \
+    hipLaunchKernelGGL((cand_topk<HH, DD>), g4, dim3(256), 0, st, (const uint16_t*)qi,          \
+                       (const uint16_t*)ki, w, B, T, row_begin, row_end, k, cnt, cand, p.nch,   \
+                       idx, stat);                                                              \
+  } while (0)
+  if (H_I == 4) {
+    if (D_I == 32) SA_IDXTK(4, 32); else if (D_I == 64) SA_IDXTK(4, 64); else SA_IDXTK(4, 128);
+  } else if (H_I == 2) {
+    if (D_I == 32) SA_IDXTK(2, 32); else if (D_I == 64) SA_IDXTK(2, 64); else SA_IDXTK(2, 128);
+  } else {
+    if (D_I == 32) SA_IDXTK(1, 32); else if (D_I == 64) SA_IDXTK(1, 64); else SA_IDXTK(1, 128);
+  }
+#undef SA_IDXTK
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,318 +1,28 @@
-// Exact per-row top-k over the causal indexer scores.
+// Exact per-row top-k over the causal indexer scores (sa_topk_select).
 //
-// [IC] IndexCache page, body paragraph 2 (the indexer selects a small subset of the
-// earlier tokens) and [HS2] HySparse2 page, "Más precisión con menos memoria" (the
-// subset is made of individual tokens).  For row t the result is the min(k, t+1)
-// positions s <= t with the largest scores, ties to the lower s, written ascending.
-//
-// One 256-thread workgroup (4 wavefronts) per row; scores become order-preserving
-// 32-bit keys (-0.0 and +0.0 share a key).  Each wavefront owns one contiguous segment
-// of the row.
-//  pass 1 (reads the row from HBM): every wavefront counts the top 11 key bits (the
-//         digit) of its segment into its own LDS histogram.  Summed, the histograms give
-//         the digit d* holding the k-th largest key and kk1, how many keys of digit d* are
-//         kept; each wavefront's own count of digits >= d* gives its offset in the hit
-//         list.
-//  pass 2 (reads the row again, now cache-resident): positions with digit >= d* ("hits")
-//         go with their keys to the hit list, in position order (ballot + mbcnt).
-//  resolve (LDS only): hits above d* are all kept; among hits at d*, two more radix
-//         digits (11 + 10 bits) find the exact k-th key a; keys above a, and the first
-//         ones equal to a (lower positions first: the tie rule), are kept.
-//  output: one order-preserving compaction of the kept hits is the ascending answer.
-// Rows with more hits than kHitCap (massive exact ties) fall back to the multi-pass
-// workgroup select of select.h reading the row from memory.  Rows are issued longest
-// first.
+// One 256-thread workgroup (4 wavefronts) per row, rows issued longest first; the
+// two-pass radix selection over the row is topk_row in topk_common.h.
 #include "sa_launch.h"
-#include "select.h"
+#include "topk_common.h"
 
 namespace sa {
-
-constexpr int kTkThreads = 256;
-constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kD1Bins = 2048;   // first digit: key bits [31:21]
-constexpr int kHitCap = 6144;   // hit list capacity
-constexpr int kLoads = 8;                // 16-byte loads per lane in flight while streaming
-constexpr int kChunk = 64 * 4 * kLoads;  // positions a wavefront streams per step
-
-struct TopkShared {
-  union {
-    uint32_t whist[kTkWaves][kD1Bins];  // pass 1: per-wave counters
-    struct {
-      uint32_t key[kHitCap];
-      int pos[kHitCap];
-    } hit;                              // pass 2 / resolve: the hit list
-    SelectShared<kTkThreads> fallback;  // rows with too many hits
-  } u;
-  uint32_t hist2[2048];  // resolve histograms
-  int run_gt[kHitCap / 64];
-  int run_eq[kHitCap / 64];
-  int whits[kTkWaves];
-  int wsum[2][kTkWaves];
-  int misc[8];
-};
-
-// Digit (top 11 bits of the order-preserving key) of a float, -0.0 counted as +0.0:
-// positive u -> (u >> 21) | 0x400, negative u -> ~(u >> 21) & 0x7ff.
-__device__ __forceinline__ uint32_t digit11(float x) {
-  const uint32_t u = __float_as_uint(x + 0.0f);
-  const uint32_t s = (uint32_t)((int32_t)u >> 31);
-  return (u >> 21) ^ ((s & 0x3ffu) | 0x400u);
-}
-
-// Finds, over nb bins (counts from cnt(d)), the digit holding the kk-th largest element:
-// writes misc[o] = digit, misc[o+1] = kk - (count above it), misc[o+2] = 1 if that is the
-// digit's whole count.  Bins are owned from the top down, bpt per thread.
-template <typename Cnt>
-__device__ __forceinline__ void find_digit(int nb, int kk, Cnt&& cnt, TopkShared& sh, int o) {
-  const int tid = threadIdx.x;
-  const int bpt = (nb + kTkThreads - 1) / kTkThreads;
-  const int top = nb - 1 - bpt * tid;
-  uint32_t c[8];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    c[i] = (i < bpt && top - i >= 0) ? cnt(top - i) : 0u;
-    local += (int)c[i];
-  }
-  int above = wg_excl_scan<kTkThreads>(local, sh.wsum[0]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i < bpt && top - i >= 0) {
-      if (above < kk && kk <= above + (int)c[i]) {
-        sh.misc[o] = top - i;
-        sh.misc[o + 1] = kk - above;
-        sh.misc[o + 2] = (kk - above) == (int)c[i];
-      }
-      above += (int)c[i];
-    }
-  }
-  __syncthreads();
-}
-
-// Streams positions [lo, hi) of the row (lo a multiple of 4, the row 16-byte aligned) in
-// groups of 4 consecutive positions per lane: f(e, x[4], valid[4]) with e the first
-// position of the group.  A wavefront's call order covers its positions in increasing
-// order, 256 per call round (lane-major inside a round); kLoads loads per lane are in
-// flight, and full chunks run without per-position guards.
-template <typename F>
-__device__ __forceinline__ void stream_segment(const float* __restrict__ row, int lo, int hi,
-                                               int lane, F&& f) {
-  int e0 = lo;
-  for (; e0 + kChunk <= hi; e0 += kChunk) {
-    f32x4 v[kLoads];
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u)
-      v[u] = *reinterpret_cast<const f32x4*>(row + e0 + u * 256 + lane * 4);
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const bool ok[4] = {true, true, true, true};
-      const float x[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
-      f(e0 + u * 256 + lane * 4, x, ok);
-    }
-  }
-  if (e0 < hi) {  // the last, partial chunk: 16-byte loads where the group is whole
-    f32x4 v[kLoads];
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = e0 + u * 256 + lane * 4;
-      if (e + 3 < hi) {
-        v[u] = *reinterpret_cast<const f32x4*>(row + e);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[u][c] = e + c < hi ? row[e + c] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = e0 + u * 256 + lane * 4;
-      const bool ok[4] = {e < hi, e + 1 < hi, e + 2 < hi, e + 3 < hi};
-      const float x[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
-      f(e, x, ok);
-    }
-  }
-}
 
 __global__ __launch_bounds__(kTkThreads) void topk_rows(const float* __restrict__ scores,
                                                         int64_t ld, int T, int row_begin,
                                                         int row_end, int k,
                                                         int32_t* __restrict__ idx) {
   __shared__ TopkShared sh;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = row_end - row_begin;
   const int b = blockIdx.x / R;
   const int r = R - 1 - (int)(blockIdx.x % R);  // longest rows first
   const int t = row_begin + r;
   const int n = t + 1;
-  const float* __restrict__ row = scores + ((int64_t)b * R + r) * ld;
   int32_t* __restrict__ out = idx + ((int64_t)b * T + t) * k;
-
   if (n <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    for (int i = threadIdx.x; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
     return;
   }
-
-  // ---- pass 1: per-wave digit histograms
-  const int seg = ((n + kTkThreads - 1) / kTkThreads) * 64;
-  const int lo = min(n, w * seg), hi = min(n, lo + seg);
-  for (int i = tid; i < kTkWaves * kD1Bins; i += kTkThreads) (&sh.u.whist[0][0])[i] = 0u;
-  __syncthreads();
-  uint32_t* wh = sh.u.whist[w];
-  stream_segment(row, lo, hi, lane, [&](int, const float* x, const bool* ok) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (ok[c]) atomicAdd(&wh[digit11(x[c])], 1u);
-  });
-  __syncthreads();
-
-  // ---- digit of the k-th largest key; per-wave counts of hits (digit >= d*)
-  find_digit(kD1Bins, k, [&](int d) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int ww = 0; ww < kTkWaves; ++ww) s += sh.u.whist[ww][d];
-    return s;
-  }, sh, 0);
-  const uint32_t dstar = (uint32_t)sh.misc[0];
-  const int kk1 = sh.misc[1];
-  {
-    int cnt = 0;
-    for (int d = (int)dstar + lane; d < kD1Bins; d += 64) cnt += (int)wh[d];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
-    if (lane == 0) sh.whits[w] = cnt;
-  }
-  __syncthreads();
-  int hit_off = 0, n_hits = 0;
-#pragma unroll
-  for (int ww = 0; ww < kTkWaves; ++ww) {
-    hit_off += ww < w ? sh.whits[ww] : 0;
-    n_hits += sh.whits[ww];
-  }
-  const int n_sure = k - kk1;  // hits above d*
-  const int n_cand = n_hits - n_sure;
-  __syncthreads();  // the histogram region becomes the hit list
-
-  if (n_hits > kHitCap) {
-    wg_topk<kTkThreads, 0>(
-        n, k, [&](int e) { return order_key(row[e]); }, [&](int pos, int e) { out[pos] = e; },
-        sh.u.fallback);
-    return;
-  }
-
-  // ---- pass 2: the hit list, in position order
-  stream_segment(row, lo, hi, lane, [&](int e, const float* x, const bool* ok) {
-    bool hit[4];
-    uint64_t m[4];
-    int before = 0;  // hits of the lower lanes in this round (lane-major order)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      hit[c] = ok[c] && digit11(x[c]) >= dstar;
-      m[c] = ballot(hit[c]);
-      before += lanes_below(m[c]);
-    }
-    if ((m[0] | m[1] | m[2] | m[3]) != 0ull) {
-      int p = hit_off + before;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (hit[c]) {
-          sh.u.hit.key[p] = order_key(x[c]);
-          sh.u.hit.pos[p] = e + c;
-          ++p;
-        }
-      }
-      hit_off += __popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]);
-    }
-  });
-  __syncthreads();
-
-  // ---- resolve: keep all hits above d*, and kk1 of the hits at d*
-  const uint32_t dlo = dstar << 21;   // smallest key of digit d*
-  const uint32_t dhi = dlo + (1u << 21);
-  uint32_t thr_gt = dlo;              // keys >= thr_gt are kept
-  uint32_t thr_eq = 0u;               // keys == thr_eq are kept while fewer than take_eq precede
-  int take_eq = 0;
-  if (kk1 < n_cand) {
-    for (int i = tid; i < 2048; i += kTkThreads) sh.hist2[i] = 0u;
-    __syncthreads();
-    for (int e = tid; e < n_hits; e += kTkThreads) {
-      const uint32_t key = sh.u.hit.key[e];
-      if (key < dhi) atomicAdd(&sh.hist2[(key >> 10) & 2047u], 1u);
-    }
-    __syncthreads();
-    find_digit(2048, kk1, [&](int d) { return sh.hist2[d]; }, sh, 3);
-    const uint32_t pre2 = dlo | ((uint32_t)sh.misc[3] << 10);
-    const int kk2 = sh.misc[4];
-    if (sh.misc[5]) {
-      thr_gt = pre2;
-    } else {
-      __syncthreads();
-      for (int i = tid; i < 1024; i += kTkThreads) sh.hist2[i] = 0u;
-      __syncthreads();
-      for (int e = tid; e < n_hits; e += kTkThreads) {
-        const uint32_t key = sh.u.hit.key[e];
-        if ((key >> 10) == (pre2 >> 10)) atomicAdd(&sh.hist2[key & 1023u], 1u);
-      }
-      __syncthreads();
-      find_digit(1024, kk2, [&](int d) { return sh.hist2[d]; }, sh, 5);  // misc[5..7]
-      const uint32_t a = pre2 | (uint32_t)sh.misc[5];
-      thr_gt = a + 1u;
-      thr_eq = a;
-      take_eq = sh.misc[6];
-    }
-  }
-
-  // ---- output: order-preserving compaction of the kept hits
-  const int runs = (n_hits + 63) / 64;
-  const int slots = (n_hits + kTkThreads - 1) / kTkThreads;
-  for (int j = 0; j < slots; ++j) {
-    const int e = j * kTkThreads + tid;
-    const bool in = e < n_hits;
-    const uint32_t key = in ? sh.u.hit.key[e] : 0u;
-    const bool gt = in && key >= thr_gt;
-    const bool eq = in && !gt && take_eq > 0 && key == thr_eq;
-    const uint64_t mg = ballot(gt), me = ballot(eq);
-    if (lane == 0 && (e >> 6) < runs) {
-      sh.run_gt[e >> 6] = __popcll(mg);
-      sh.run_eq[e >> 6] = __popcll(me);
-    }
-  }
-  __syncthreads();
-  if (w == 0) {  // exclusive scan of the runs by one wavefront
-    int gsum = 0, esum = 0;
-    for (int r0 = 0; r0 < runs; r0 += 64) {
-      const int ri = r0 + lane;
-      const int g0 = ri < runs ? sh.run_gt[ri] : 0, e0 = ri < runs ? sh.run_eq[ri] : 0;
-      int gx = g0, ex = e0;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int gy = __shfl_up(gx, o, 64), ey = __shfl_up(ex, o, 64);
-        if (lane >= o) {
-          gx += gy;
-          ex += ey;
-        }
-      }
-      if (ri < runs) {
-        sh.run_gt[ri] = gsum + gx - g0;
-        sh.run_eq[ri] = esum + ex - e0;
-      }
-      gsum += __shfl(gx, 63, 64);
-      esum += __shfl(ex, 63, 64);
-    }
-  }
-  __syncthreads();
-  for (int j = 0; j < slots; ++j) {
-    const int e = j * kTkThreads + tid;
-    const bool in = e < n_hits;
-    const uint32_t key = in ? sh.u.hit.key[e] : 0u;
-    const bool gt = in && key >= thr_gt;
-    const bool eq = in && !gt && take_eq > 0 && key == thr_eq;
-    const uint64_t mg = ballot(gt), me = ballot(eq);
-    if (in) {
-      const int gb = sh.run_gt[e >> 6] + lanes_below(mg);
-      const int eb = sh.run_eq[e >> 6] + lanes_below(me);
-      if (gt) out[gb + min(eb, take_eq)] = sh.u.hit.pos[e];
-      else if (eq && eb < take_eq) out[gb + eb] = sh.u.hit.pos[e];
-    }
-  }
+  topk_row(scores + ((int64_t)b * R + r) * ld, n, k, out, sh);
 }
 
 hipError_t launch_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,

@@ -121,6 +121,52 @@ int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
   }
 }
 
+static bool indexer_topk_sizes_ok(int B, int T, int H_I, int D_I, int row_begin, int row_end,
+                                  int k) {
+  return B >= 1 && B <= 65535 && T >= 1 && T <= 262144 && 0 <= row_begin &&
+         row_begin < row_end && row_end <= T && k >= 1 && k <= 4096 && H_I >= 1 && D_I >= 1 &&
+         (int64_t)B * (row_end - row_begin) <= 0x7fffffff;
+}
+
+size_t sa_indexer_topk_workspace(int B, int T, int H_I, int D_I, int row_begin, int row_end,
+                                 int k) {
+  if (!indexer_topk_sizes_ok(B, T, H_I, D_I, row_begin, row_end, k)) return 0;
+  return sa::indexer_topk_workspace_bytes(B, row_begin, row_end, k);
+}
+
+int sa_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T, int H_I,
+                    int D_I, int dtype, int row_begin, int row_end, int k, int32_t* idx,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    REQUIRE_PTR(qi);
+    REQUIRE_PTR(ki);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(idx);
+    REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(B <= 65535, "B must be <= 65535 (got %d)", B);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(0 <= row_begin && row_begin < row_end && row_end <= T,
+            "need 0 <= row_begin < row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
+    REQUIRE(k >= 1 && k <= 4096, "k must be in [1, 4096] (got %d)", k);
+    REQUIRE(H_I >= 1 && D_I >= 1, "H_I and D_I must be >= 1 (H_I=%d D_I=%d)", H_I, D_I);
+    REQUIRE((int64_t)B * (row_end - row_begin) <= 0x7fffffff, "too many rows in one call");
+    SUPPORT(T <= 262144, "T > 262144 is not supported (T=%d)", T);
+    SUPPORT(sa::indexer_has_mfma(dtype == SA_BF16, H_I, D_I),
+            "the fused path needs bf16, H_I in {1,2,4} and D_I in {32,64,128} "
+            "(dtype=%d H_I=%d D_I=%d)", dtype, H_I, D_I);
+    const size_t need = sa::indexer_topk_workspace_bytes(B, row_begin, row_end, k);
+    if (!workspace || ws_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "sa_indexer_topk: workspace of %zu bytes needed (got %zu)",
+                  need, workspace ? ws_bytes : (size_t)0);
+    REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    return hip_status(sa::launch_indexer_topk(qi, ki, w, B, T, H_I, D_I, row_begin, row_end, k,
+                                              idx, workspace, as_stream(stream)),
+                      "sa_indexer_topk launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_indexer_topk: unexpected exception");
+  }
+}
+
 int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
                        int T, int Hq, int Hkv, int D, int topk, int window, float scale,
                        int dtype, void* out, float* lse, void* stream) {

@@ -71,6 +71,38 @@ __device__ __forceinline__ float sum8_dpp(float v) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Inclusive scan over the 64 lanes with DPP moves (no LDS round trips): shifts by 1, 2,
+// 4, 8 inside each row of 16 lanes, then row 0's total into rows 1 and 3 (row_bcast:15)
+// and lane 31's running total into rows 2 and 3 (row_bcast:31).  op(a, b) must be
+// associative with identity id (the value shifted in at row edges and masked rows).
+template <typename Op>
+__device__ __forceinline__ int wave_incl_scan(int x, int id, Op op) {
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix sum over the 64 lanes; total = the sum over all lanes.
+__device__ __forceinline__ int wave_excl_sum(int v, int& total) {
+  const int x = wave_incl_scan(v, 0, [](int a, int b) { return a + b; });
+  total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
+// Minimum and maximum over the 64 lanes (unsigned).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  const int x = wave_incl_scan((int)v, -1, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  const int x = wave_incl_scan((int)v, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
 // Orders LDS accesses of the lanes of one wavefront (LDS executes a wavefront's
 // instructions in order; this keeps the compiler from moving accesses across).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -13,8 +13,21 @@ hipError_t launch_indexer_scores(const void* qi, const void* ki, const float* w,
                                  int H_I, int D_I, bool bf16, int row_begin, int row_end,
                                  float* scores, int64_t ld, hipStream_t st);
 
+// MFMA indexer over key slots j at positions j << sshift (sshift = 0: plain scores), slots
+// cut into chunks of `chunk` (a multiple of 64) spread over the workgroups of a strip.
+bool indexer_has_mfma(bool bf16, int H_I, int D_I);
+hipError_t launch_indexer_mfma(const void* qi, const void* ki, const float* w, int B, int T,
+                               int H_I, int D_I, int row_begin, int row_end, int sshift,
+                               int chunk, float* scores, int64_t ld, hipStream_t st);
+
 hipError_t launch_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
                               int row_end, int k, int32_t* idx, hipStream_t st);
+
+// Fused indexer -> top-k (MFMA indexer configurations only).
+size_t indexer_topk_workspace_bytes(int B, int row_begin, int row_end, int k);
+hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T,
+                               int H_I, int D_I, int row_begin, int row_end, int k,
+                               int32_t* idx, void* workspace, hipStream_t st);
 
 hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
                                   int B, int T, int Hq, int Hkv, int D, int topk, int window,

@@ -51,6 +51,30 @@ def _err(L):
     return L.sa_last_error().decode()
 
 
+def test_indexer_topk_validation_and_workspace(L):
+    f = L.sa_indexer_topk
+    ws = L.sa_indexer_topk_workspace
+    need = ws(1, 4096, 4, 64, 0, 4096, 256)
+    assert need > 0
+    assert ws(1, 4096, 4, 64, 0, 4097, 256) == 0                   # row_end > T
+    assert ws(1, 4096, 4, 64, 0, 4096, 0) == 0                     # k
+    # more rows or longer rows need more workspace
+    assert ws(1, 8192, 4, 64, 0, 8192, 256) > need
+    assert ws(2, 4096, 4, 64, 0, 4096, 256) > need
+    # every case below fails validation, so nothing reaches the GPU
+    args = (P, P, P, 1, 4096, 4, 64, 1, 0, 4096, 256, P)
+    assert f(*args, None, need, None) == 3
+    assert "workspace" in _err(L)
+    assert f(*args, P, need - 1, None) == 3
+    assert f(P, P, P, 1, 4096, 4, 64, 0, 0, 4096, 256, P, P, need, None) == 2   # f32: two-step path
+    assert f(P, P, P, 1, 4096, 3, 64, 1, 0, 4096, 256, P, P, need, None) == 2   # H_I = 3
+    assert f(P, P, P, 1, 4096, 4, 48, 1, 0, 4096, 256, P, P, need, None) == 2   # D_I = 48
+    assert f(P, P, P, 1, 4096, 4, 64, 1, 0, 4096, 5000, P, P, need, None) == 1  # k too big
+    assert f(P, P, P, 1, 4096, 4, 64, 1, 100, 100, 256, P, P, need, None) == 1  # empty rows
+    assert f(P, P, None, 1, 4096, 4, 64, 1, 0, 4096, 256, P, P, need, None) == 1
+    assert f(P, P, P, 1, 300000, 4, 64, 1, 0, 4096, 256, P, P, need, None) == 2  # T too long
+
+
 def test_attn_validation(L):
     f = L.sa_sparse_attn_fwd
     assert f(None, P, P, P, 1, 8, 4, 1, 64, 4, 4, 0.1, 1, P, None, None) == 1

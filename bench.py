@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--chunk", type=int, default=8192, help="indexer/top-k rows per chunk")
+    ap.add_argument("--chunk", type=int, default=32768, help="indexer/top-k rows per chunk")
     ap.add_argument("--indices", choices=["fused", "two-step"], default="fused",
                     help="how the step builds the indices: sa_indexer_topk, or "
                          "sa_indexer_scores + sa_topk_select")
@@ -388,7 +388,7 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         lx = sa_synth.attn_inputs(sa_synth.layer_seed(l), 1, T, p["Hq"], p["Hkv"], p["D"], "bf16")
         layers.append(tuple(to_dev(lx[n], "bf16") for n in ("q", "k", "v")))
         del lx
-    chunk = 8192
+    chunk = 32768
     ws = torch.empty(sa.sa_indexer_topk_workspace(1, T, p["H_I"], p["D_I"], T - chunk, T,
                                                   p["topk"]), dtype=torch.uint8, device=dev)
     idx = torch.full((1, T, p["topk"]), -1, dtype=torch.int32, device=dev)

@@ -127,16 +127,21 @@ __device__ __forceinline__ void wave_radix_kth(uint32_t lo, uint32_t span, int k
 }  // namespace
 
 // ---------------------------------------------------------------- 2. thresholds
-// One wavefront per row.  thr = +inf for rows that keep all their positions (t + 1 <= k),
-// -inf when the row has no more than jrank samples (every score is a candidate).
-// Block 0 also clears the recompute counter of this call.
+// One wavefront per row; the row's samples go to registers (lane L holds samples
+// 4 L + 256 i .. + 3), and thr = the jrank-th largest of them, exactly (the radix
+// select of the selection kernel).  thr = +inf for rows that keep all their positions
+// (t + 1 <= k), -inf when the row has no more than jrank samples (every score is a
+// candidate).  Block 0 also clears the recompute counter of this call.
+constexpr int kSampleVec = 16;  // float4 loads per lane: up to 4096 samples per row
+
 __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict__ samp,
                                                         int64_t lds, int B, int row_begin,
                                                         int row_end, int k, int sshift,
                                                         int jrank, float* __restrict__ thr,
                                                         uint32_t* __restrict__ n_recomputed) {
-  __shared__ uint32_t hist[4][2048];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ uint32_t hist_s[4][kRadixBins];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_recomputed = 0u;
   const int R = row_end - row_begin;
   const int64_t item = (int64_t)blockIdx.x * 4 + wv;
@@ -148,27 +153,36 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
   }
   const int ns = (t >> sshift) + 1;
   const float* __restrict__ row = samp + item * lds;
-  uint32_t* h = hist[wv];
-
-  for (int i = lane; i < 2048; i += 64) h[i] = 0u;
-  wave_lds_sync();
-  for (int e = lane; e < ns; e += 64) atomicAdd(&h[order_key(row[e]) >> 21], 1u);
-  wave_lds_sync();
-  int d1, j1;
-  bool w1;
-  wave_find_bin(h, 2048, jrank, lane, d1, j1, w1);
-  wave_lds_sync();
-  for (int i = lane; i < 2048; i += 64) h[i] = 0u;
-  wave_lds_sync();
-  for (int e = lane; e < ns; e += 64) {
-    const uint32_t key = order_key(row[e]);
-    if ((int)(key >> 21) == d1) atomicAdd(&h[(key >> 10) & 2047u], 1u);
+  uint32_t key[4 * kSampleVec];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < kSampleVec; ++i) {
+    const int e = 256 * i + 4 * lane;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (e < ns) x = *reinterpret_cast<const f32x4*>(row + e);  // (lds is a multiple of 4)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      key[4 * i + u] = order_key(x[u]);
+      if (e + u < ns) {
+        mn = min(mn, key[4 * i + u]);
+        mx = max(mx, key[4 * i + u]);
+      }
+    }
   }
-  wave_lds_sync();
-  int d2, j2;
-  bool w2;
-  wave_find_bin(h, 2048, j1, lane, d2, j2, w2);
-  if (lane == 0) thr[item] = key_to_float(((uint32_t)d1 << 21) | ((uint32_t)d2 << 10));
+  wave_minmax(mn, mx);
+  uint32_t v;
+  int take;
+  wave_radix_kth(mn, mx - mn, jrank,
+                 [&](auto&& f) {
+#pragma unroll
+                   for (int i = 0; i < kSampleVec; ++i)
+#pragma unroll
+                     for (int u = 0; u < 4; ++u)
+                       if (256 * i + 4 * lane + u < ns) f(key[4 * i + u]);
+                 },
+                 hist_s[wv], lane, v, take);
+  // v is the jrank-th largest sample, or one below the smallest key kept whole
+  if (lane == 0) thr[item] = key_to_float(take > 0 ? v : v + 1u);
 }
 
 // ---------------------------------------------------------------- 3. candidates
@@ -236,20 +250,24 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__
       float vals[IW::ROWS];
 #pragma unroll
       for (int rr = 0; rr < IW::ROWS; ++rr) vals[rr] = st[rr * SROW + lane];
+      // the chunk's list base for row 0, opaque per block so that the 32 row pointers are
+      // formed as needed instead of being kept live across blocks
+      int64_t cbo = (row0 * nch + c) * kIdxChunk;
+      int64_t rstride = (int64_t)nch * kIdxChunk;  // entries between rows' lists
+      asm volatile("" : "+s"(cbo), "+s"(rstride));
+      u32x2* cb = cand + cbo;
       auto compact = [&](auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        u32x2* rowp = cand + (row0 * nch + c) * kIdxChunk;  // list of row rr in chunk c
 #pragma unroll
         for (int rr = 0; rr < IW::ROWS; ++rr) {
           const float th = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr_v), rr));
           const bool hit = vals[rr] >= th && (!DIAG || s <= t0 + rr);
           const uint64_t m = ballot(hit);
           if (m) {
-            const uint32_t base = cnt_s[rr];
-            if (hit) rowp[base + (uint32_t)lanes_below(m)] = u32x2{__float_as_uint(vals[rr]), (uint32_t)s};
-            cnt_s[rr] = base + (uint32_t)__popcll(m);
+            u32x2* dst = cb + rr * rstride + cnt_s[rr];
+            if (hit) dst[lanes_below(m)] = u32x2{__float_as_uint(vals[rr]), (uint32_t)s};
+            cnt_s[rr] += (uint32_t)__popcll(m);
           }
-          rowp += (int64_t)nch * kIdxChunk;
         }
       };
       if (j0 + SB - 1 > t0) compact(std::true_type{});  // some key follows some row
@@ -554,7 +572,10 @@ IdxTopkPlan plan_indexer_topk(int B, int row_begin, int row_end, int k) {
   const int kf0 = k <= 2048 ? 64 : 256;
   int sshift = 0;
   while ((k >> (sshift + 1)) >= kf0) ++sshift;
-  const int kf = k >> sshift;
+  // at most 64 * 4 * kSampleVec samples per row (the threshold kernel holds them in
+  // registers): longer rows take a sparser sample and a wider margin
+  while (((row_end - 1) >> sshift) + 1 > 64 * 4 * kSampleVec) ++sshift;
+  const int kf = max(1, k >> sshift);
   int sq = 0;
   while (sq * sq < kf) ++sq;
   p.sshift = sshift;

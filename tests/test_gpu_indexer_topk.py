@@ -124,3 +124,10 @@ def test_64k_rows():
     # the 64K prefill sizes (k = 2048): the last rows of the longest chunk
     x = sa_synth.indexer_inputs(618, 1, 65536, 4, 64, "bf16")
     _case(x, 2048, 65536 - 48, 65536, max_recomputed=1)
+
+
+def test_long_rows_sparser_sample():
+    # rows of 150,000 keys: the sample is thinned to at most 4096 per row (wider margin)
+    x = sa_synth.indexer_inputs(619, 1, 150000, 4, 64, "bf16")
+    _case(x, 2048, 150000 - 16, 150000, max_recomputed=1)
+    _case(x, 256, 150000 - 16, 150000, max_recomputed=1)

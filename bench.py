@@ -314,26 +314,33 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    # ---- fixed-graph distance attention, 16K
+    # ---- fixed-graph distance attention: the 16K workload, and the same distributions
+    # at 64K and 128K (16K alone is launch/latency-bound)
     W2 = sa_synth.WORKLOADS[2]
     p = W2.params
-    log("graph attention (16K)")
-    g = sa_synth.graph_inputs(W2.seed, 1, p["T"], p["H"], p["D"], "bf16")
-    cq, ck, vg, bias = (to_dev(g["cq"], "bf16"), to_dev(g["ck"], "bf16"), to_dev(g["v"], "bf16"),
-                        to_dev(g["bias"], "f32"))
-    og = torch.empty_like(vg)
-    ms = timed(lambda: sa.sa_graph_attn_fwd(cq, ck, vg, bias, p["tau"], p["local"], p["n_pow2"],
-                                            out=og), reps)
-    T2, H2, D2 = p["T"], p["H"], p["D"]
-    edges = sum(min(t, 32) + 1 + sum(1 for j in range(6, 14) if (1 << j) <= t) for t in range(T2))
-    comp = T2 * H2 * (2 * D2 * 2 + 2 * 3 * 2)
-    rows["graph_attn_16k"] = {
-        "ms": ms, "query_tokens_per_s": T2 / (ms * 1e-3),
-        "compulsory_bytes": comp, "compulsory_GBps": comp / (ms * 1e-3) / 1e9,
-        "edge_bytes": edges * H2 * (D2 * 2 + 6), "edge_GBps": edges * H2 * (D2 * 2 + 6) / (ms * 1e-3) / 1e9,
-        "hbm_frac_compulsory": comp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-    }
-    del cq, ck, vg, bias, og
+    H2, D2 = p["H"], p["D"]
+    for T2, name in ((p["T"], "graph_attn_16k"), (65536, "graph_attn_64k"),
+                     (131072, "graph_attn_128k")):
+        log(f"graph attention ({T2} tokens)")
+        g = sa_synth.graph_inputs(W2.seed, 1, T2, H2, D2, "bf16")
+        cq, ck, vg, bias = (to_dev(g["cq"], "bf16"), to_dev(g["ck"], "bf16"),
+                            to_dev(g["v"], "bf16"), to_dev(g["bias"], "f32"))
+        del g
+        og = torch.empty_like(vg)
+        ms = timed(lambda: sa.sa_graph_attn_fwd(cq, ck, vg, bias, p["tau"], p["local"],
+                                                p["n_pow2"], out=og), reps)
+        edges = sum(min(t, p["local"]) + 1 + sum(1 for j in range(p["n_pow2"])
+                                                  if (1 << j) > p["local"] and (1 << j) <= t)
+                    for t in range(T2))
+        comp = T2 * H2 * (2 * D2 * 2 + 2 * 3 * 2)
+        rows[name] = {
+            "ms": ms, "query_tokens_per_s": T2 / (ms * 1e-3),
+            "compulsory_bytes": comp, "compulsory_GBps": comp / (ms * 1e-3) / 1e9,
+            "edge_bytes": edges * H2 * (D2 * 2 + 6),
+            "edge_GBps": edges * H2 * (D2 * 2 + 6) / (ms * 1e-3) / 1e9,
+            "hbm_frac_compulsory": comp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        del cq, ck, vg, bias, og
 
     # ---- block-sparse decode, 32 x 128K
     W5 = sa_synth.WORKLOADS[5]

@@ -36,6 +36,16 @@ def test_degenerate_graphs():
     _run(505, 1, 1, 8, 64, "bf16", 1.0, 32, 14)    # one token
 
 
+def test_block_kernel_edges():
+    # 64-token blocks: ragged last block, widest band (local = 64), far offsets beyond T,
+    # no far offsets at all, and offsets reaching back many blocks
+    _run(507, 2, 1000, 4, 64, "bf16", 1.3, 64, 30)
+    _run(508, 1, 130, 2, 64, "bf16", 0.5, 64, 6)       # every power of two <= local
+    _run(509, 1, 3000, 3, 64, "bf16", 1.0, 32, 14)
+    _run(510, 1, 777, 2, 128, "bf16", 2.0, 17, 11)
+    _run(511, 1, 64, 2, 64, "bf16", 1.0, 32, 14)        # exactly one block
+
+
 def test_wide_heads():
     _run(506, 1, 100, 16, 128, "bf16", 1.0, 32, 14)   # H*D = 2048: 4 chunk groups per token
 

@@ -11,10 +11,11 @@
 //  1. decode_block_scores: score_j = (sum_h q_h) . kbar_j for every complete block;
 //     each workgroup hands on the exact top-16 of its blocks as candidates.
 //  2. decode_split_attn: one workgroup of 4 wavefronts per (sequence, KV head, split)
-//     selects the top blocks from the candidates; each wavefront attends the group's query heads to its sub-slice of U = selected
-//     blocks' tokens before the window followed by the window, through GroupAttn (MFMA
-//     over the grouped heads); the workgroup merges its wavefronts in LDS and the last
-//     workgroup of each (sequence, KV head) merges the splits.
+//     (8 wavefronts when a single split covers everything) selects the top blocks from
+//     the candidates; each wavefront attends the group's query heads to its sub-slice of
+//     U = selected blocks' tokens before the window followed by the window, through
+//     GroupAttn (MFMA over the grouped heads); the workgroup merges its wavefronts in LDS
+//     and the last workgroup of each (sequence, KV head) merges the splits.
 // The kernel boundary makes the candidates visible to kernel 2.  Inside kernel 2 the
 // split partials travel through agent-scope atomic stores/loads and one counter per
 // (sequence, KV head), avoiding a device-wide cache flush per workgroup.  The counters
@@ -86,8 +87,9 @@ constexpr int kScoreThreads = 256;
 constexpr int kScoreChunk = 256;   // blocks scored per workgroup pass (64 per wavefront)
 constexpr int kCandMax = 64;       // most candidates a scoring workgroup hands on
 constexpr int kMaxScoreWGs = 64;   // scoring workgroups per (sequence, KV head)
-constexpr int kSplitWaves = 4;     // wavefronts per split workgroup
-constexpr int kSplitGrain = kSplitWaves * 32;  // positions of U per split step
+constexpr int kSplitWaves = 4;     // wavefronts per split workgroup (n_splits > 1)
+constexpr int kSplitGrain = kSplitWaves * 64;  // positions of U per split: 2 tiles per wave
+constexpr int kWholeWaves = 8;     // wavefronts of the one workgroup per sequence (n_splits == 1)
 
 // Scoring workgroups per (sequence, KV head) and blocks each one covers.
 static void score_grid(int nb, int& nwg, int& per_wg) {
@@ -130,7 +132,8 @@ static int decode_u_max(int Lmax, int block, int top_blocks, int window) {
 }
 
 int decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_blocks, int window) {
-  // one 32-key tile per wavefront (the step is latency-bound), up to ~8 waves per CU
+  // two 32-key tiles per wavefront of a 4-wavefront split (the step is latency-bound:
+  // more, thinner splits cost more in the merge than they save), up to ~8 waves per CU
   const int64_t umax = decode_u_max(Lmax, block, top_blocks, window);
   const int64_t steps = imax(1, (umax + kSplitGrain - 1) / kSplitGrain);
   const int64_t cap = imax(1, (2048 / kSplitWaves) / ((int64_t)B * Hkv));
@@ -172,6 +175,7 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
     uint32_t* __restrict__ cand) {
   __shared__ uint64_t scomb[kScoreChunk + kCandMax];
   __shared__ uint64_t best[kCandMax];
+  __shared__ __attribute__((aligned(16))) uint16_t qrows[16 * D];  // the group's query rows
   // a row (D floats) is read by 8 lanes, C = D/8 consecutive floats each; 8 rows per
   // group of loads, 8 groups for the wave's 64 rows; rows are reduced with DPP
   constexpr int C = D / 8;
@@ -185,33 +189,12 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
   const int nfull = L / block;
 
   const int d0 = (lane & 7) * C;
-  float qb[C];
-#pragma unroll
-  for (int i = 0; i < C; ++i) qb[i] = 0.f;
-  {
-    u32x4 w[16][C / 8];
-#pragma unroll
-    for (int hh = 0; hh < 16; ++hh)  // G <= 16: all head rows in flight at once
-#pragma unroll
-      for (int c = 0; c < C / 8; ++c)
-        w[hh][c] = hh < G ? ld16(q + ((int64_t)b * Hq + g * G + hh) * D + d0 + c * 8)
-                          : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int hh = 0; hh < 16; ++hh)
-#pragma unroll
-      for (int c = 0; c < C / 8; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qb[c * 8 + 2 * i] += bf16_lo(w[hh][c][i]);
-          qb[c * 8 + 2 * i + 1] += bf16_hi(w[hh][c][i]);
-        }
-  }
-  if (tid < cpw) best[tid] = 0ull;
   const int j_begin = blockIdx.y * per_wg;
   const int j_end = min(j_begin + per_wg, nfull);
-  for (int c0 = j_begin; c0 < j_end; c0 += kScoreChunk) {
+  // the first chunk's key means are requested before the query rows arrive
+  f32x4 a[8][NL];
+  auto load_rows = [&](int c0) {
     const int jw = c0 + wv * 64 + (lane >> 3);  // this lane's row in group 0
-    f32x4 a[8][NL];
 #pragma unroll
     for (int gi = 0; gi < 8; ++gi) {  // all of the wave's rows in flight at once
       const int j = jw + gi * 8;
@@ -220,6 +203,34 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
       for (int l = 0; l < NL; ++l)
         a[gi][l] = j < j_end ? *reinterpret_cast<const f32x4*>(rp + 4 * l) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  if (j_begin < j_end) load_rows(j_begin);
+  // the group's query rows (G x D bf16, one 16-byte piece per thread) through LDS
+  {
+    const int pieces = G * D / 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (tid < pieces) x = ld16(q + ((int64_t)b * Hq + g * G) * D + tid * 8);
+    if (tid < pieces) *reinterpret_cast<u32x4*>(&qrows[tid * 8]) = x;
+  }
+  __syncthreads();
+  float qb[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) qb[i] = 0.f;
+  for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+    for (int c = 0; c < C / 8; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&qrows[hh * D + d0 + c * 8]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qb[c * 8 + 2 * i] += bf16_lo(w[i]);
+        qb[c * 8 + 2 * i + 1] += bf16_hi(w[i]);
+      }
+    }
+  }
+  if (tid < cpw) best[tid] = 0ull;
+  for (int c0 = j_begin; c0 < j_end; c0 += kScoreChunk) {
+    const int jw = c0 + wv * 64 + (lane >> 3);  // this lane's row in group 0
+    if (c0 != j_begin) load_rows(c0);
 #pragma unroll
     for (int gi = 0; gi < 8; ++gi) {
       float part = 0.f;
@@ -250,8 +261,8 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
 // publishes the split's partial.  The last split to finish (a counter) merges all splits
 // into the output.  Partials are written and read with agent-scope atomic accesses, which
 // go straight to the memory side, so no cache flush is needed between workgroups.
-template <int D>
-__global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void decode_split_attn(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ lens, int Lmax, int Hq,
     int Hkv, int block, int top_blocks, int window, int n_splits, int n_cand, float scale_log2,
@@ -263,11 +274,11 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
   // per-wave staging area, also used for the wave's merge slot and (all of it) for the
   // candidate list
   constexpr int CAND_BYTES = kMaxScoreWGs * kCandMax * 8 + 64 * 4;
-  constexpr int STAGE = GA::LDS_BYTES * kSplitWaves >= CAND_BYTES
+  constexpr int STAGE = GA::LDS_BYTES * W >= CAND_BYTES
                             ? GA::LDS_BYTES
-                            : (CAND_BYTES + kSplitWaves - 1) / kSplitWaves;
+                            : (CAND_BYTES + W - 1) / W;
   static_assert(16 * D * 4 + 2 * 16 * 4 <= STAGE, "merge area must fit the stage");
-  __shared__ __attribute__((aligned(16))) unsigned char vl[kSplitWaves][(STAGE + 15) / 16 * 16];
+  __shared__ __attribute__((aligned(16))) unsigned char vl[W][(STAGE + 15) / 16 * 16];
   __shared__ int pre[65];   // token offsets of the selected blocks inside U
   __shared__ int blk[64];   // selected blocks, ascending
   __shared__ int last;
@@ -291,9 +302,9 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
     uint64_t* cc = reinterpret_cast<uint64_t*>(&vl[0][0]);
     int* rsel = reinterpret_cast<int*>(cc + n_cand);  // blocks in score order
     const uint64_t* cb = reinterpret_cast<const uint64_t*>(cand) + (int64_t)bg * n_cand;
-    for (int i = tid; i < n_cand; i += 64 * kSplitWaves) cc[i] = cb[i];
+    for (int i = tid; i < n_cand; i += 64 * W) cc[i] = cb[i];
     __syncthreads();
-    rank_select<64 * kSplitWaves>(cc, n_cand, nsel_blocks,
+    rank_select<64 * W>(cc, n_cand, nsel_blocks,
                                   [&](int rank, uint64_t c) { rsel[rank] = unpack_pos(c); });
     __syncthreads();
     if (tid < nsel_blocks) {  // ascending block order
@@ -322,8 +333,8 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
   }
   const int nsel = pre[64];
   const int U = nsel + (L - wstart);
-  const int per = ((U + n_splits - 1) / n_splits + kSplitGrain - 1) / kSplitGrain * kSplitGrain;
-  const int wper = per / kSplitWaves;
+  const int per = ((U + n_splits - 1) / n_splits + 32 * W - 1) / (32 * W) * (32 * W);
+  const int wper = per / W;
   const int u_lo = min(U, split * per + wv * wper);
   const int u_hi = min(U, u_lo + wper);
 
@@ -368,17 +379,17 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
   }
   __syncthreads();
   const int64_t pbase = ((int64_t)bg * n_splits + split) * G * PS;
-  for (int it = tid; it < G * (D / 8); it += 64 * kSplitWaves) {
+  for (int it = tid; it < G * (D / 8); it += 64 * W) {
     const int hh = it / (D / 8), dd = (it % (D / 8)) * 8;
     float M = -INFINITY;
 #pragma unroll
-    for (int w2 = 0; w2 < kSplitWaves; ++w2)
+    for (int w2 = 0; w2 < W; ++w2)
       M = fmaxf(M, reinterpret_cast<const float*>(vl[w2])[16 * D + hh]);
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float lt = 0.f;
     if (M > -INFINITY) {
 #pragma unroll
-      for (int w2 = 0; w2 < kSplitWaves; ++w2) {
+      for (int w2 = 0; w2 < W; ++w2) {
         const float* mo = reinterpret_cast<const float*>(vl[w2]);
         const float f = exp2f(mo[16 * D + hh] - M);
         lt += f * mo[16 * D + 16 + hh];
@@ -391,6 +402,15 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
         }
       }
     }
+    if (n_splits == 1) {  // the whole of U was here: write the output
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* orow = out + ((int64_t)b * Hq + g * G + hh) * D + dd;
+      st16(orow, u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)});
+      if (lse && dd == 0)
+        lse[(int64_t)b * Hq + g * G + hh] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
+      continue;
+    }
     float* pp = partials + pbase + (int64_t)hh * PS;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -401,6 +421,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
     }
   }
 
+  if (n_splits == 1) return;
   // ---- the last split of this (sequence, KV head) merges all splits
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
@@ -413,7 +434,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_attn(
   auto ald = [](const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  for (int it = tid; it < G * (D / 4); it += 64 * kSplitWaves) {
+  for (int it = tid; it < G * (D / 4); it += 64 * W) {
     const int hh = it / (D / 4), dd = (it % (D / 4)) * 4;
     float M = -INFINITY, lt = 0.f;
     float o[4] = {0.f, 0.f, 0.f, 0.f};
@@ -472,10 +493,16 @@ static void launch_decode_d(const void* q, const void* kcache, const void* vcach
   const dim3 g2((unsigned)(B * Hkv), (unsigned)n_splits);
   hipLaunchKernelGGL(decode_block_scores<D>, g1, dim3(kScoreThreads), 0, st, (const uint16_t*)q,
                      kbar, lens, Lmax, Hq, Hkv, block, per_wg, cpw, ws.cand);
-  hipLaunchKernelGGL(decode_split_attn<D>, g2, dim3(64 * kSplitWaves), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)kcache, (const uint16_t*)vcache, lens, Lmax, Hq, Hkv, block,
-                     top_blocks, window, n_splits, nwg * cpw, sl2, ws.cand, ws.partials,
-                     ws.counters, sel_out, (uint16_t*)out, lse);
+  if (n_splits == 1)
+    hipLaunchKernelGGL((decode_split_attn<D, kWholeWaves>), g2, dim3(64 * kWholeWaves), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)kcache, (const uint16_t*)vcache, lens,
+                       Lmax, Hq, Hkv, block, top_blocks, window, n_splits, nwg * cpw, sl2,
+                       ws.cand, ws.partials, ws.counters, sel_out, (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL((decode_split_attn<D, kSplitWaves>), g2, dim3(64 * kSplitWaves), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)kcache, (const uint16_t*)vcache, lens,
+                       Lmax, Hq, Hkv, block, top_blocks, window, n_splits, nwg * cpw, sl2,
+                       ws.cand, ws.partials, ws.counters, sel_out, (uint16_t*)out, lse);
 }
 
 hipError_t launch_sparse_decode(const void* q, const void* kcache, const void* vcache,

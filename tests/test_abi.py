@@ -129,10 +129,10 @@ def test_graph_meanpool_decode_validation(L):
 
 
 def test_decode_auto_splits(L):
-    # one 32-key tile per wavefront: |U| = 16*64 + 512 = 1536 keys -> 12 splits of 4
-    # wavefronts; a tiny U or a huge batch caps the splits
-    assert L.sa_sparse_decode_auto_splits(32, 131072, 1, 64, 16, 512) == 12
+    # two 32-key tiles per wavefront of 4-wavefront splits: |U| = 16*64 + 512 = 1536 keys
+    # -> 6 splits; a tiny U or a huge batch caps the splits
+    assert L.sa_sparse_decode_auto_splits(32, 131072, 1, 64, 16, 512) == 6
     assert L.sa_sparse_decode_auto_splits(1, 64, 1, 64, 1, 0) == 1
-    assert L.sa_sparse_decode_auto_splits(1, 131072, 1, 64, 64, 4096) == 64
+    assert L.sa_sparse_decode_auto_splits(1, 131072, 1, 64, 64, 4096) == 32
     assert L.sa_sparse_decode_auto_splits(1024, 131072, 1, 64, 16, 512) == 1
     assert L.sa_sparse_decode_auto_splits(1024, 131072, 1, 64, 16, 512) == 1

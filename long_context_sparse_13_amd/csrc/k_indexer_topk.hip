@@ -250,12 +250,16 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__
       float vals[IW::ROWS];
 #pragma unroll
       for (int rr = 0; rr < IW::ROWS; ++rr) vals[rr] = st[rr * SROW + lane];
-      // the chunk's list base for row 0, opaque per block so that the 32 row pointers are
-      // formed as needed instead of being kept live across blocks
+      // the lists of this chunk for the wavefront's 32 rows as one buffer resource: a
+      // lane's store goes to byte offset 8 (rr * rstride + entry); lanes without a
+      // candidate get an offset past the range, and the hardware drops those stores, so
+      // the compaction needs no exec-mask changes or branches.  The base is opaque per
+      // block so the compiler forms it here instead of keeping it live across blocks.
       int64_t cbo = (row0 * nch + c) * kIdxChunk;
-      int64_t rstride = (int64_t)nch * kIdxChunk;  // entries between rows' lists
-      asm volatile("" : "+s"(cbo), "+s"(rstride));
-      u32x2* cb = cand + cbo;
+      asm volatile("" : "+s"(cbo));
+      const uint32_t rstride8 = (uint32_t)nch * kIdxChunk * 8u;  // bytes between rows' lists
+      const __amdgpu_buffer_rsrc_t lists = __builtin_amdgcn_make_buffer_rsrc(
+          cand + cbo, 0, (int)(rstride8 * IW::ROWS), 0x00020000);
       auto compact = [&](auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
 #pragma unroll
@@ -263,11 +267,10 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__
           const float th = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr_v), rr));
           const bool hit = vals[rr] >= th && (!DIAG || s <= t0 + rr);
           const uint64_t m = ballot(hit);
-          if (m) {
-            u32x2* dst = cb + rr * rstride + cnt_s[rr];
-            if (hit) dst[lanes_below(m)] = u32x2{__float_as_uint(vals[rr]), (uint32_t)s};
-            cnt_s[rr] += (uint32_t)__popcll(m);
-          }
+          const uint32_t at = (uint32_t)rr * rstride8 + (cnt_s[rr] + (uint32_t)lanes_below(m)) * 8u;
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(vals[rr]), (uint32_t)s}, lists,
+                                               hit ? at : 0xffffffffu, 0, 0);
+          cnt_s[rr] += (uint32_t)__popcll(m);
         }
       };
       if (j0 + SB - 1 > t0) compact(std::true_type{});  // some key follows some row

@@ -31,6 +31,7 @@
 #include "sa_launch.h"
 #include "sa_device.h"
 
+#include <climits>
 #include <type_traits>
 
 namespace sa {
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
   // per wavefront: the list-start marks (during the gather) or the radix histogram
   __shared__ uint32_t work_s[4][kMarkCap / 2 > kRadixBins ? kMarkCap / 2 : kRadixBins];
   __shared__ uint32_t nz_s[4][1028];  // (chunk << 16) | list offset, non-empty lists only
+  __shared__ uint32_t sbin_s[4][64];  // lists starting in each 64-entry slot
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = row_end - row_begin;
@@ -327,6 +329,7 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
   uint32_t* hist = work_s[wv];
   uint16_t* mark = reinterpret_cast<uint16_t*>(work_s[wv]);
   uint32_t* nz = nz_s[wv];
+  uint32_t* sbin = sbin_s[wv];
   const int nc = t / kIdxChunk + 1;  // chunks of this row (<= 1024)
 
   // ---- list lengths: lane L holds chunks 256 g + 4 L + i (g < 4, i < 4) in registers
@@ -362,9 +365,11 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
   uint32_t v;
   int take_eq;
   if (n_hits >= k && n_hits <= 64 * J) {
-    // ---- the non-empty lists (chunk, offset), and a mark where each one starts
+    // ---- the non-empty lists (chunk, offset), a mark where each one starts, and how
+    // many start in each 64-entry slot
     const int nw = (n_hits + 1) / 2;
     for (int i = lane; i < nw; i += 64) work_s[wv][i] = 0xffffffffu;  // no mark
+    sbin[lane] = 0u;
     wave_lds_sync();
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -375,26 +380,35 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
         if (x > 0) {
           nz[zo] = ((uint32_t)(256 * g + 4 * lane + i) << 16) | (uint32_t)o;
           mark[o] = (uint16_t)zo;
+          atomicAdd(&sbin[o >> 6], 1u);
           ++zo;
         }
         o += x;
       }
     }
     wave_lds_sync();
-    // ---- gather: slot j holds entry 64 j + lane
+    // lane j: the list holding the entry just before slot j (lists that start in earlier
+    // slots, minus one); slot 0 starts with list 0
+    int n_lists;
+    const int before_v = wave_excl_sum((int)sbin[lane], n_lists) - 1;
+    // ---- gather: slot j holds entry 64 j + lane.  The list of an entry is the last one
+    // starting at or before it: the running maximum of the marks within the slot, or
+    // the list carried into the slot.  Slots are independent, eight per straight-line
+    // group; lanes past the last entry load the last entry again and are ignored.
     uint32_t key[J];
     int pos[J];
-    int carry = 0;  // list of the previous slot's last entry
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (64 * j < n_hits) {
-        const int e = 64 * j + lane;
-        const int mk = e < n_hits ? (mark[e] == 0xffffu ? -1 : (int)mark[e]) : -1;
-        const int m = max(carry, wave_incl_scan(mk, -1, [](int x, int y) { return max(x, y); }));
-        carry = __builtin_amdgcn_readlane(m, 63);
-        if (e < n_hits) {
+    for (int j0 = 0; j0 < J; j0 += 8) {
+      if (64 * j0 < n_hits) {
+#pragma unroll
+        for (int j = j0; j < j0 + 8; ++j) {
+          const int e = min(64 * j + lane, n_hits - 1);
+          const int mr = (int)mark[e];
+          const int m = max(__builtin_amdgcn_readlane(before_v, j),
+                            wave_incl_scan(mr != 0xffff ? mr : INT_MIN, INT_MIN,
+                                           [](int x, int y) { return max(x, y); }));
           const uint32_t info = nz[m];
-          const u32x2 ent = cl[(int64_t)(info >> 16) * kIdxChunk + (e - (int)(info & 0xffffu))];
+          const u32x2 ent = cl[(int)(info >> 16) * kIdxChunk + (e - (int)(info & 0xffffu))];
           key[j] = ent[0];
           pos[j] = (int)ent[1];
         }
@@ -419,19 +433,30 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
                        if (j < jn && 64 * j + lane < n_hits) f(key[j]);
                    },
                    hist, lane, v, take_eq);
-    // ---- output: per slot, ranks from ballots (keys > v; the first take_eq keys == v)
-    int gr = 0, er = 0;  // kept keys > v and keys == v in the slots before
+    // ---- output: per slot, the kept entries (keys > v, and the first take_eq keys == v)
+    // ranked by ballots and written through a buffer store that drops the other lanes
+    const uint64_t ob = reinterpret_cast<uint64_t>(out);  // uniform: keep it in SGPRs
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<int32_t*>(
+            ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ob >> 32)) << 32) |
+            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ob)),
+        0, k * 4, 0x00020000);
+    int kr = 0, er = 0;  // kept entries and keys == v in the slots before
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (j < jn) {
         const bool in = 64 * j + lane < n_hits;
-        const bool g = in && key[j] > v, e = in && key[j] == v;
-        const uint64_t mg = ballot(g), me = ballot(e);
-        const int gb = gr + lanes_below(mg), eb = er + lanes_below(me);
-        if (g) out[gb + min(eb, take_eq)] = pos[j];
-        else if (e && eb < take_eq) out[gb + eb] = pos[j];
-        gr += __popcll(mg);
-        er += __popcll(me);
+        bool keep = in && key[j] > v;
+        const bool eq = in && key[j] == v;
+        const uint64_t me = ballot(eq);
+        if (me) {
+          keep = keep || (eq && er + lanes_below(me) < take_eq);
+          er += __popcll(me);
+        }
+        const uint64_t mk = ballot(keep);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            (uint32_t)pos[j], orsrc, keep ? (uint32_t)(kr + lanes_below(mk)) * 4u : 0xffffffffu, 0, 0);
+        kr += __popcll(mk);
       }
     }
     return;

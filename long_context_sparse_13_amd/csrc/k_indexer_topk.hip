@@ -84,14 +84,15 @@ __device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
 constexpr int kRadixBins = 1024;
 
 // One wavefront: the kk-th largest key v among the keys its lanes enumerate with
-// for_each(f) (all within [lo, lo + span]) and take = how many keys equal to v are kept
-// (keys > v are all kept).  Radix digits of up to 10 bits over the remaining range
-// (bins hold (key - lo) >> shift); stops early when the digit holding the kk-th key is
-// kept whole.
+// for_each(f) (keys outside [lo, lo + span] are skipped) and take = how many keys equal
+// to v are kept (keys > v are all kept).  Radix digits of up to 10 bits over the
+// remaining range (bins hold (key - lo) >> shift); stops early when the digit holding
+// the kk-th key is kept whole.  whole: every key equal to v is kept too when take > 0
+// (the kept set is then the keys > v - 1; when take == 0 it is the keys > v).
 template <typename ForEach>
 __device__ __forceinline__ void wave_radix_kth(uint32_t lo, uint32_t span, int kk,
                                                ForEach&& for_each, uint32_t* hist, int lane,
-                                               uint32_t& v, int& take) {
+                                               uint32_t& v, int& take, bool& whole) {
   for (;;) {
     const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
     const int shift = bits > 10 ? bits - 10 : 0;
@@ -112,11 +113,13 @@ __device__ __forceinline__ void wave_radix_kth(uint32_t lo, uint32_t span, int k
     if (shift == 0) {
       v = blo;
       take = rem;
+      whole = wh;
       return;
     }
     if (wh) {  // every key of the bin is kept: keep keys >= blo
       v = blo - 1u;
       take = 0;
+      whole = true;
       return;
     }
     lo = blo;
@@ -173,6 +176,7 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
   wave_minmax(mn, mx);
   uint32_t v;
   int take;
+  bool whole;
   wave_radix_kth(mn, mx - mn, jrank,
                  [&](auto&& f) {
 #pragma unroll
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
                      for (int u = 0; u < 4; ++u)
                        if (256 * i + 4 * lane + u < ns) f(key[4 * i + u]);
                  },
-                 hist_s[wv], lane, v, take);
+                 hist_s[wv], lane, v, take, whole);
   // v is the jrank-th largest sample, or one below the smallest key kept whole
   if (lane == 0) thr[item] = key_to_float(take > 0 ? v : v + 1u);
 }
@@ -299,6 +303,7 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
                                                   const uint16_t* __restrict__ ki,
                                                   const float* __restrict__ wgt, int B, int T,
                                                   int row_begin, int row_end, int k,
+                                                  const float* __restrict__ thr,
                                                   const uint16_t* __restrict__ counts,
                                                   u32x2* __restrict__ cand, int nch,
                                                   int32_t* __restrict__ idx,
@@ -349,21 +354,26 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
   int n_hits = 0, n_nz = 0, run[4], zrun[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    int l = 0, z = 0;
+    run[g] = n_hits;
+    zrun[g] = n_nz;
+    if (256 * g < nc) {
+      int l = 0, z = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      l += len_of(g, i);
-      z += len_of(g, i) > 0;
+      for (int i = 0; i < 4; ++i) {
+        l += len_of(g, i);
+        z += len_of(g, i) > 0;
+      }
+      int tl, tz;
+      run[g] += wave_excl_sum(l, tl);
+      zrun[g] += wave_excl_sum(z, tz);
+      n_hits += tl;
+      n_nz += tz;
     }
-    int tl, tz;
-    run[g] = n_hits + wave_excl_sum(l, tl);
-    zrun[g] = n_nz + wave_excl_sum(z, tz);
-    n_hits += tl;
-    n_nz += tz;
   }
 
   uint32_t v;
   int take_eq;
+  bool whole;
   if (n_hits >= k && n_hits <= 64 * J) {
     // ---- the non-empty lists (chunk, offset), a mark where each one starts, and how
     // many start in each 64-entry slot
@@ -415,48 +425,64 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
       }
     }
     const int jn = (n_hits + 63) / 64;  // slots in use (the last one partly)
-    uint32_t mn = 0xffffffffu, mx = 0u;
+    // ordered keys; lanes past the last entry take key 0, below every finite score's key
+    // (so they are never kept and the radix skips them)
+    uint32_t mx = 0u;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (j < jn && 64 * j + lane < n_hits) {
-        key[j] = order_key(__uint_as_float(key[j]));
-        mn = min(mn, key[j]);
+      if (j < jn) {
+        key[j] = 64 * j + lane < n_hits ? order_key(__uint_as_float(key[j])) : 0u;
         mx = max(mx, key[j]);
       }
     }
-    wave_minmax(mn, mx);
+    mx = wave_max_u32(mx);
+    // every candidate scored at least the row's threshold
+    const uint32_t lo = order_key(thr[rowi]);
     wave_lds_sync();  // the marks are dead: the histogram takes their place
-    wave_radix_kth(mn, mx - mn, k,
+    wave_radix_kth(lo, mx - lo, k,
                    [&](auto&& f) {
 #pragma unroll
                      for (int j = 0; j < J; ++j)
-                       if (j < jn && 64 * j + lane < n_hits) f(key[j]);
+                       if (j < jn) f(key[j]);
                    },
-                   hist, lane, v, take_eq);
-    // ---- output: per slot, the kept entries (keys > v, and the first take_eq keys == v)
-    // ranked by ballots and written through a buffer store that drops the other lanes
+                   hist, lane, v, take_eq, whole);
+    // ---- output: per slot, the kept entries ranked by a ballot and written through a
+    // buffer store that drops the other lanes
     const uint64_t ob = reinterpret_cast<uint64_t>(out);  // uniform: keep it in SGPRs
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<int32_t*>(
             ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ob >> 32)) << 32) |
             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ob)),
         0, k * 4, 0x00020000);
-    int kr = 0, er = 0;  // kept entries and keys == v in the slots before
+    int kr = 0;  // kept entries in the slots before
+    int jn_e = jn;
+    asm volatile("" : "+s"(jn_e));  // a fresh scalar compare per slot, not a kept mask
+    if (whole) {  // the kept set is the keys above one value
+      const uint32_t vk = take_eq == 0 ? v : v - 1u;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (j < jn) {
-        const bool in = 64 * j + lane < n_hits;
-        bool keep = in && key[j] > v;
-        const bool eq = in && key[j] == v;
-        const uint64_t me = ballot(eq);
-        if (me) {
-          keep = keep || (eq && er + lanes_below(me) < take_eq);
-          er += __popcll(me);
+      for (int j = 0; j < J; ++j) {
+        if (j < jn_e) {
+          const bool keep = key[j] > vk;
+          const uint64_t mk = ballot(keep);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              (uint32_t)pos[j], orsrc, keep ? (uint32_t)(kr + lanes_below(mk)) * 4u : 0xffffffffu, 0, 0);
+          kr += __popcll(mk);
         }
-        const uint64_t mk = ballot(keep);
-        __builtin_amdgcn_raw_buffer_store_b32(
-            (uint32_t)pos[j], orsrc, keep ? (uint32_t)(kr + lanes_below(mk)) * 4u : 0xffffffffu, 0, 0);
-        kr += __popcll(mk);
+      }
+    } else {  // keys > v, and the first take_eq keys == v in position order
+      int er = 0;  // keys == v in the slots before
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (j < jn_e) {
+          const bool eq = key[j] == v;
+          const int eb = er + lanes_below(ballot(eq));
+          const bool keep = key[j] > v || (eq && eb < take_eq);
+          const uint64_t mk = ballot(keep);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              (uint32_t)pos[j], orsrc, keep ? (uint32_t)(kr + lanes_below(mk)) * 4u : 0xffffffffu, 0, 0);
+          kr += __popcll(mk);
+          er += __popcll(ballot(eq));
+        }
       }
     }
     return;
@@ -490,7 +516,7 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
                      for (int c = lane; c < nc; c += 64)
                        each_entry(c, [&](uint32_t key, int) { f(key); });
                    },
-                   hist, lane, v, take_eq);
+                   hist, lane, v, take_eq, whole);
     // output in chunk order: 64 consecutive chunks per round, one per lane
     int gsum = 0, esum = 0;
     for (int c0 = 0; c0 < nc; c0 += 64) {
@@ -561,7 +587,7 @@ __global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi
   wave_minmax(mn, mx);
   wave_radix_kth(mn, mx - mn, k,
                  [&](auto&& f) { each_key([&](uint32_t key, int) { f(key); }); }, hist, lane,
-                 v, take_eq);
+                 v, take_eq, whole);
   int ng = 0, ne = 0;
   each_key([&](uint32_t key, int) {
     ng += key > v;
@@ -663,8 +689,8 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
                        p.nch);                                                                  \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                        \
     hipLaunchKernelGGL((cand_topk<HH, DD>), g4, dim3(256), 0, st, (const uint16_t*)qi,          \
-                       (const uint16_t*)ki, w, B, T, row_begin, row_end, k, cnt, cand, p.nch,   \
-                       idx, stat);                                                              \
+                       (const uint16_t*)ki, w, B, T, row_begin, row_end, k, thr, cnt, cand,     \
+                       p.nch, idx, stat);                                                       \
   } while (0)
   if (H_I == 4) {
     if (D_I == 32) SA_IDXTK(4, 32); else if (D_I == 64) SA_IDXTK(4, 64); else SA_IDXTK(4, 128);

@@ -299,7 +299,7 @@ constexpr int kCandPerLane = 64;
 constexpr int kMarkCap = 64 * kCandPerLane;  // entries the mark table covers
 
 template <int H, int DI>
-__global__ __launch_bounds__(256) void cand_topk(const uint16_t* __restrict__ qi,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cand_topk(const uint16_t* __restrict__ qi,
                                                   const uint16_t* __restrict__ ki,
                                                   const float* __restrict__ wgt, int B, int T,
                                                   int row_begin, int row_end, int k,

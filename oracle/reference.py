@@ -74,6 +74,28 @@ def indexer_scores_row(qi, ki, w, b: int, t: int) -> np.ndarray:
     return np.matmul(_f64(w), relu)         # Σ_h w_h · ReLU(.)
 
 
+def decode_e4m3(codes) -> np.ndarray:
+    """The value of each 8-bit E4M3 code (an array of uint8), in float64.
+
+    Reading: the pages name no 8-bit format.  The indexer's 8-bit inputs are taken to
+    be E4M3 codes as the OCP 8-bit floating point specification defines them (its "fn"
+    variant): a sign bit, 4 exponent bits with bias 7 and 3 mantissa bits; exponent
+    field 0 holds zero and the subnormals m/8 * 2^-6; there are no infinities, and the
+    two codes with every exponent and mantissa bit set are NaN.  No scale factor comes
+    with them: a positive factor shared by a whole row (a per-tensor or per-query scale)
+    leaves that row's top-k unchanged, because ReLU commutes with it.  The 8-bit indexer
+    is then ``indexer_scores_row`` over these values.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    negative = (c >> 7) == 1
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    magnitude = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = np.where(negative, -magnitude, magnitude)
+    out[(e == 15) & ((c & 7) == 7)] = np.nan
+    return out
+
+
 def indexer_scores(qi, ki, w, rows=None):
     """All requested rows as a dict ``{(b, t): row}``; rows default to every (b, t)."""
     B, T = qi.shape[0], qi.shape[1]

@@ -29,6 +29,7 @@ import numpy as np
 __all__ = [
     "rng",
     "round_bf16",
+    "encode_e4m3",
     "normal",
     "prefill_inputs",
     "indexer_inputs",
@@ -59,6 +60,18 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out.view(np.float32).reshape(x.shape)
 
 
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    """The nearest 8-bit E4M3 code (OCP "fn" variant, ties to even) of each float32
+    value, as uint8.  Values must lie within +-448 (every draw here does).  The rounding
+    is torch's float32 -> float8_e4m3fn conversion."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.size and float(np.max(np.abs(x))) > 448.0:
+        raise ValueError("E4M3 inputs must lie within +-448")
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().reshape(x.shape)
+
+
 def normal(g: np.random.Generator, shape, dtype: str, std: float = 1.0) -> np.ndarray:
     x = g.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
@@ -84,10 +97,16 @@ def _normal_big(g: np.random.Generator, shape, dtype: str, chunk: int = 1 << 26)
 
 
 def indexer_inputs(seed: int, B: int, T: int, H_I: int, D_I: int, dtype: str, g=None):
-    """qi[B,T,H_I,D_I], ki[B,T,D_I] ~ N(0,1) and per-head weights w[H_I] ~ U(0,1)."""
+    """qi[B,T,H_I,D_I], ki[B,T,D_I] ~ N(0,1) and per-head weights w[H_I] ~ U(0,1).
+
+    ``dtype="fp8"``: the same float32 draws as "f32", returned as E4M3 codes (uint8)."""
     g = g if g is not None else rng(seed)
-    qi = normal(g, (B, T, H_I, D_I), dtype)
-    ki = normal(g, (B, T, D_I), dtype)
+    if dtype == "fp8":
+        qi = encode_e4m3(normal(g, (B, T, H_I, D_I), "f32"))
+        ki = encode_e4m3(normal(g, (B, T, D_I), "f32"))
+    else:
+        qi = normal(g, (B, T, H_I, D_I), dtype)
+        ki = normal(g, (B, T, D_I), dtype)
     w = g.uniform(0.0, 1.0, size=H_I).astype(np.float32)
     return {"qi": qi, "ki": ki, "w": w}
 

@@ -417,4 +417,67 @@ def pin_indexcache(orc):
         assert np.array_equal(O, want)
 
 
+def pin_e4m3_closed_forms(orc):
+    """Codes whose values the OCP E4M3 definition fixes directly: zeros of both signs, the
+    smallest subnormal 2^-9, the largest subnormal 7*2^-9, the smallest normal 2^-6, 1,
+    1.125, 2, the largest finite 448, 240 and 256 at the top of the exponent range, and
+    the two NaN codes."""
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+            0x39: 1.125, 0x40: 2.0, 0xC0: -2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+            0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    codes = np.array(sorted(want), dtype=np.uint8)
+    got = orc.decode_e4m3(codes)
+    for c, g in zip(codes, got):
+        assert g == want[int(c)], (hex(int(c)), g)
+    z = orc.decode_e4m3(np.array([0x00, 0x80], dtype=np.uint8))
+    assert z[0] == 0.0 and not math.copysign(1.0, z[0]) < 0
+    assert z[1] == 0.0 and math.copysign(1.0, z[1]) < 0
+    nan = orc.decode_e4m3(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.isnan(nan).all()
+
+
+def pin_e4m3_every_code_vs_torch(orc):
+    """All 256 codes against torch's float8_e4m3fn -> float32 conversion (an independent
+    implementation of the same format); also strictly increasing over 0x00..0x7E, and
+    code c | 0x80 is the negative of code c."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.decode_e4m3(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~fin)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert np.all(np.diff(got[:0x7F]) > 0)
+    assert np.array_equal(got[0x80:0xFF], -got[:0x7F])
+
+
+def pin_indexer_e4m3_exact(orc):
+    """The 8-bit indexer: scores over decoded E4M3 inputs equal exact rational arithmetic
+    on the same codes (each decoded by hand from sign, exponent and mantissa)."""
+    g = sa_synth.rng(71)
+    T, H, D = 7, 2, 5
+    qc = g.integers(0, 256, size=(1, T, H, D)).astype(np.uint8)
+    kc = g.integers(0, 256, size=(1, T, D)).astype(np.uint8)
+    qc[(qc & 0x7F) == 0x7F] = 0x38   # no NaN inputs
+    kc[(kc & 0x7F) == 0x7F] = 0x40
+    w = np.array([0.75, 0.5], dtype=np.float32)
+
+    def frac(c):
+        c = int(c)
+        e, m = (c >> 3) & 15, c & 7
+        v = Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        return -v if c >> 7 else v
+
+    qd, kd = orc.decode_e4m3(qc), orc.decode_e4m3(kc)
+    for t in range(T):
+        row = orc.indexer_scores_row(qd, kd, w, 0, t)
+        for s in range(t + 1):
+            tot = Fraction(0)
+            for h in range(H):
+                dot = sum(frac(qc[0, t, h, d]) * frac(kc[0, s, d]) for d in range(D))
+                tot += Fraction(float(w[h])) * max(dot, Fraction(0))
+            assert abs(row[s] - float(tot)) <= 1e-12 * max(1.0, abs(float(tot))), (t, s)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -52,6 +52,11 @@ MUTANTS = [
     ("decode_partial_block_scored", "nfull = int(lens[b]) // block\n        for g in range(Hkv):",
      "nfull = min(kbar.shape[1], (int(lens[b]) + block - 1) // block)\n        for g in range(Hkv):"),
     ("indexcache_indexes_every_layer", 'if kind == "F":', "if True:"),
+    ("e4m3_bias_8", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    ("e4m3_subnormal_scale", "(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7"),
+    ("e4m3_mantissa_sixteenths", "(1.0 + m / 8.0) * np.exp2", "(1.0 + m / 16.0) * np.exp2"),
+    ("e4m3_no_nan", "out[(e == 15) & ((c & 7) == 7)] = np.nan", "pass"),
+    ("e4m3_sign_dropped", "out = np.where(negative, -magnitude, magnitude)", "out = magnitude"),
 ]
 
 

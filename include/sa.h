@@ -41,8 +41,11 @@ extern "C" {
 
 #define SA_VERSION 100 /* 1.0.0 */
 
-/* Element types of the input/output tensors. */
-typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+/* Element types of the input/output tensors.  SA_FP8_E4M3: 8-bit floats as the OCP 8-bit
+ * floating point specification defines E4M3 ("fn": bias 7, subnormals, no infinities,
+ * 0x7F/0xFF NaN), one byte per element, no scale factor; accepted by the indexer entry
+ * points only (sa_indexer_scores, sa_indexer_topk), SA_ERR_UNSUPPORTED elsewhere. */
+typedef enum { SA_F32 = 0, SA_BF16 = 1, SA_FP8_E4M3 = 2 } sa_dtype;
 
 /* Status codes. */
 enum {
@@ -69,6 +72,11 @@ enum {
  *        consecutive [row_begin, row_end) ranges.
  * Requires 0 <= row_begin < row_end <= T, ld >= row_end, ld % 4 == 0, 1 <= H_I <= 64,
  * D_I % 8 == 0 and D_I <= 256.  bf16 with H_I in {1,2,4} and D_I % 32 == 0 runs on MFMA.
+ * SA_FP8_E4M3 (qi and ki as E4M3 codes) requires H_I in {1,2,4} and D_I in {32,64,128}
+ * (else SA_ERR_UNSUPPORTED); the codes are widened exactly to bf16 inside the kernel and
+ * contracted on the bf16 MFMA, so the scores are those of the decoded values with the
+ * same float32 accumulation as bf16 inputs.  A positive per-tensor or per-query scale
+ * leaves every row's top-k unchanged; fold it into w if the scores themselves matter.
  */
 int sa_indexer_scores(const void* qi, const void* ki, const float* w, int B, int T, int H_I,
                       int D_I, int dtype, int row_begin, int row_end, float* scores,
@@ -102,7 +110,8 @@ int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
  * recomputed in full inside the call; the result never depends on the inputs'
  * distribution, only the time does.
  *
- * qi [B, T, H_I, D_I] bf16; ki [B, T, D_I] bf16; w [H_I] float32; idx [B, T, k] int32.
+ * qi [B, T, H_I, D_I] and ki [B, T, D_I] bf16 or E4M3 (dtype); w [H_I] float32;
+ * idx [B, T, k] int32.
  * workspace: device memory of at least sa_indexer_topk_workspace(...) bytes, no
  * initialisation needed; it holds per-row samples, thresholds and candidate lists
  * (about (row_end / 256) * 2 KB per row), so long rows are best processed in row chunks.
@@ -110,8 +119,8 @@ int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
  * number of rows that were recomputed in full (a diagnostic; 0 in the usual case).  The
  * kept set is about 1.3-1.6 k entries; beyond k of about 3000 most rows are selected by
  * list passes, which is slower (the two-step path may be faster there).
- * Requires bf16, H_I in {1, 2, 4}, D_I in {32, 64, 128} (else SA_ERR_UNSUPPORTED: use the
- * two-step path), 1 <= k <= 4096, 0 <= row_begin < row_end <= T <= 262144.
+ * Requires bf16 or E4M3, H_I in {1, 2, 4}, D_I in {32, 64, 128} (else SA_ERR_UNSUPPORTED:
+ * use the two-step path), 1 <= k <= 4096, 0 <= row_begin < row_end <= T <= 262144.
  */
 int sa_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T, int H_I,
                     int D_I, int dtype, int row_begin, int row_end, int k, int32_t* idx,

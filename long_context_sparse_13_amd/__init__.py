@@ -25,7 +25,7 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "sa.h")
-SA_F32, SA_BF16 = 0, 1
+SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
 
 _c_void_p, _c_int, _c_int64, _c_float, _c_size_t = (
     ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t)
@@ -122,7 +122,9 @@ def _dtype_code(t) -> int:
         return SA_BF16
     if t.dtype == torch.float32:
         return SA_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    if t.dtype == torch.float8_e4m3fn:
+        return SA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float32 or float8_e4m3fn)")
 
 
 def _dev(t, name: str, dtype=None):
@@ -152,7 +154,7 @@ def sa_indexer_scores(qi, ki, w, row_begin: int = 0, row_end: int | None = None,
                       scores=None, ld: int | None = None):
     """scores[b, r, s] = Σ_h w[h]·ReLU(qi[b,t,h]·ki[b,s]) for t = row_begin + r, s ≤ t.
 
-    qi [B,T,H_I,D_I], ki [B,T,D_I] (bf16 or f32), w [H_I] f32.  Returns scores
+    qi [B,T,H_I,D_I], ki [B,T,D_I] (bf16, f32 or float8_e4m3fn), w [H_I] f32.  Returns scores
     [B, row_end-row_begin, ld] f32 (entries s > t untouched / uninitialised)."""
     torch = _torch()
     _dev(qi, "qi"); _dev(ki, "ki", qi.dtype); _dev(w, "w", torch.float32)

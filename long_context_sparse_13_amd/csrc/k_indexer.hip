@@ -22,15 +22,14 @@ namespace sa {
 // Scores of the key slots j = 0, 1, ... at positions j << sshift (sshift = 0: every key;
 // sshift > 0: the strided sample used by the fused selection) into scores[row, j] for the
 // slots with j << sshift <= t.  Slots are cut into chunks of `chunk` (a multiple of 64).
-template <int H, int DI>
-__global__ __launch_bounds__(256) void indexer_mfma(const uint16_t* __restrict__ qi,
-                                                     const uint16_t* __restrict__ ki,
+template <int H, int DI, bool F8>
+__global__ __launch_bounds__(256) void indexer_mfma(const uint8_t* __restrict__ qi,
+                                                     const uint8_t* __restrict__ ki,
                                                      const float* __restrict__ wgt, int T,
                                                      int row_begin, int row_end, int sshift,
                                                      int chunk, float* __restrict__ scores,
                                                      int64_t ld) {
-  using IW = IdxWave<H, DI>;
-  constexpr int KS = IW::KS;
+  using IW = IdxWave<H, DI, F8>;
   constexpr int SB = 64;        // key slots per staged block (4 tiles)
   constexpr int SROW = SB + 4;  // padded LDS row (floats)
   __shared__ __attribute__((aligned(16))) float stage[kIdxWaves][IW::ROWS * SROW];
@@ -49,28 +48,27 @@ __global__ __launch_bounds__(256) void indexer_mfma(const uint16_t* __restrict__
   float* st = stage[wv];
 
   IW iw;
-  iw.load(qi + (int64_t)b * T * H * DI, t0, row_end, wgt, n, grp);
-  const uint16_t* kib = ki + (int64_t)b * T * DI;
+  iw.load(qi + (int64_t)b * T * H * DI * IW::EB, t0, row_end, wgt, n, grp);
+  const uint8_t* kib = ki + (int64_t)b * T * DI * IW::EB;
   float* sb = scores + (int64_t)b * R * ld;
 
   for (int c = group; c < wave_chunks; c += kIdxGroups) {
     const int j_lo = c * chunk;
     const int j_hi = min(j_lo + chunk, j_last + 1);
-    u32x4 bk[KS];
+    typename IW::Keys bk;
     IW::load_keys(kib, min((j_lo + n) << sshift, T - 1), grp, bk);
     for (int j0 = j_lo; j0 < j_hi; j0 += SB) {
       // ---- 32 rows x 64 slots of scores into this wave's LDS stage; the next tile's
       // keys are in flight while a tile is scored
 #pragma unroll
       for (int nt = 0; nt < SB / 16; ++nt) {
-        u32x4 bn[KS];
+        typename IW::Keys bn;
         IW::load_keys(kib, min((j0 + nt * 16 + 16 + n) << sshift, T - 1), grp, bn);
         float sc[IW::NSC];
         iw.scores(bk, sc);
 #pragma unroll
         for (int i = 0; i < IW::NSC; ++i) st[IW::token(i, grp) * SROW + nt * 16 + n] = sc[i];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bk[ks] = bn[ks];
+        bk = bn;
       }
       wave_lds_sync();
       // ---- 16 B per lane: 4 rows x 64 slots per instruction
@@ -146,40 +144,34 @@ __global__ __launch_bounds__(256) void indexer_valu(const void* __restrict__ qi,
 }
 
 hipError_t launch_indexer_mfma(const void* qi, const void* ki, const float* w, int B, int T,
-                               int H_I, int D_I, int row_begin, int row_end, int sshift,
+                               int H_I, int D_I, bool f8, int row_begin, int row_end, int sshift,
                                int chunk, float* scores, int64_t ld, hipStream_t st) {
   const int R = row_end - row_begin;
   const int strips = (R + kIdxStrip - 1) / kIdxStrip;
   const dim3 grid((unsigned)(strips * kIdxGroups), (unsigned)B);
-#define SA_IDX(HH, DD)                                                                        \
-  hipLaunchKernelGGL((indexer_mfma<HH, DD>), grid, dim3(256), 0, st, (const uint16_t*)qi,     \
-                     (const uint16_t*)ki, w, T, row_begin, row_end, sshift, chunk, scores, \
-                     ld)
-  if (H_I == 4) {
-    if (D_I == 32) SA_IDX(4, 32); else if (D_I == 64) SA_IDX(4, 64); else SA_IDX(4, 128);
-  } else if (H_I == 2) {
-    if (D_I == 32) SA_IDX(2, 32); else if (D_I == 64) SA_IDX(2, 64); else SA_IDX(2, 128);
-  } else {
-    if (D_I == 32) SA_IDX(1, 32); else if (D_I == 64) SA_IDX(1, 64); else SA_IDX(1, 128);
-  }
-#undef SA_IDX
-  return hipGetLastError();
+  return dispatch_indexer(H_I, D_I, f8, [&](auto h, auto d, auto f) {
+    hipLaunchKernelGGL((indexer_mfma<decltype(h)::value, decltype(d)::value, decltype(f)::value>),
+                       grid, dim3(256), 0, st, (const uint8_t*)qi, (const uint8_t*)ki, w, T,
+                       row_begin, row_end, sshift, chunk, scores, ld);
+    return hipGetLastError();
+  });
 }
 
-bool indexer_has_mfma(bool bf16, int H_I, int D_I) {
-  return bf16 && (H_I == 1 || H_I == 2 || H_I == 4) && (D_I == 32 || D_I == 64 || D_I == 128);
+bool indexer_has_mfma(int elem, int H_I, int D_I) {
+  return (elem == kBF16 || elem == kE4M3) && (H_I == 1 || H_I == 2 || H_I == 4) &&
+         (D_I == 32 || D_I == 64 || D_I == 128);
 }
 
 hipError_t launch_indexer_scores(const void* qi, const void* ki, const float* w, int B, int T,
-                                 int H_I, int D_I, bool bf16, int row_begin, int row_end,
+                                 int H_I, int D_I, int elem, int row_begin, int row_end,
                                  float* scores, int64_t ld, hipStream_t st) {
   const int R = row_end - row_begin;
-  if (indexer_has_mfma(bf16, H_I, D_I)) {
-    return launch_indexer_mfma(qi, ki, w, B, T, H_I, D_I, row_begin, row_end, 0, kIdxChunk,
-                               scores, ld, st);
+  if (indexer_has_mfma(elem, H_I, D_I)) {
+    return launch_indexer_mfma(qi, ki, w, B, T, H_I, D_I, elem == kE4M3, row_begin, row_end, 0,
+                               kIdxChunk, scores, ld, st);
   } else {
     const dim3 grid((unsigned)((R + 3) / 4), (unsigned)((row_end + 255) / 256), (unsigned)B);
-    if (bf16)
+    if (elem == kBF16)
       hipLaunchKernelGGL(indexer_valu<true>, grid, dim3(256), 0, st, qi, ki, w, T, H_I, D_I,
                          row_begin, row_end, scores, ld);
     else

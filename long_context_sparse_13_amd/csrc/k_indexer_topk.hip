@@ -191,16 +191,15 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- 3. candidates
-template <int H, int DI>
-__global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__ qi,
-                                                     const uint16_t* __restrict__ ki,
+template <int H, int DI, bool F8>
+__global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ qi,
+                                                     const uint8_t* __restrict__ ki,
                                                      const float* __restrict__ wgt, int T,
                                                      int row_begin, int row_end, int k,
                                                      const float* __restrict__ thr,
                                                      uint16_t* __restrict__ counts,
                                                      u32x2* __restrict__ cand, int nch) {
-  using IW = IdxWave<H, DI>;
-  constexpr int KS = IW::KS;
+  using IW = IdxWave<H, DI, F8>;
   constexpr int SB = 64;        // keys per staged block (4 tiles)
   constexpr int SROW = SB + 4;  // padded LDS row (floats)
   __shared__ __attribute__((aligned(16))) float stage[kIdxWaves][IW::ROWS * SROW];
@@ -219,8 +218,8 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__
   const int wave_chunks = t_last / kIdxChunk + 1;
 
   IW iw;
-  iw.load(qi + (int64_t)b * T * H * DI, t0, row_end, wgt, n, grp);
-  const uint16_t* kib = ki + (int64_t)b * T * DI;
+  iw.load(qi + (int64_t)b * T * H * DI * IW::EB, t0, row_end, wgt, n, grp);
+  const uint8_t* kib = ki + (int64_t)b * T * DI * IW::EB;
   float* st = stage[wv];
 
   // row rr of the wavefront is kept by lane rr: its threshold (+inf: no candidates)
@@ -235,19 +234,18 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__
     uint32_t cnt_s[IW::ROWS];  // list length of row rr in this chunk so far (uniform)
 #pragma unroll
     for (int rr = 0; rr < IW::ROWS; ++rr) cnt_s[rr] = 0u;
-    u32x4 bk[KS];
+    typename IW::Keys bk;
     IW::load_keys(kib, min(s_lo + n, T - 1), grp, bk);
     for (int j0 = s_lo; j0 < s_hi; j0 += SB) {
 #pragma unroll
       for (int nt = 0; nt < SB / 16; ++nt) {
-        u32x4 bn[KS];
+        typename IW::Keys bn;
         IW::load_keys(kib, min(j0 + nt * 16 + 16 + n, T - 1), grp, bn);
         float sc[IW::NSC];
         iw.scores(bk, sc);
 #pragma unroll
         for (int i = 0; i < IW::NSC; ++i) st[IW::token(i, grp) * SROW + nt * 16 + n] = sc[i];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bk[ks] = bn[ks];
+        bk = bn;
       }
       wave_lds_sync();
       // ---- row by row: one lane per key of the block
@@ -298,9 +296,9 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint16_t* __restrict__
 constexpr int kCandPerLane = 64;
 constexpr int kMarkCap = 64 * kCandPerLane;  // entries the mark table covers
 
-template <int H, int DI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cand_topk(const uint16_t* __restrict__ qi,
-                                                  const uint16_t* __restrict__ ki,
+template <int H, int DI, bool F8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cand_topk(const uint8_t* __restrict__ qi,
+                                                  const uint8_t* __restrict__ ki,
                                                   const float* __restrict__ wgt, int B, int T,
                                                   int row_begin, int row_end, int k,
                                                   const float* __restrict__ thr,
@@ -308,7 +306,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
                                                   u32x2* __restrict__ cand, int nch,
                                                   int32_t* __restrict__ idx,
                                                   uint32_t* __restrict__ n_recomputed) {
-  using IW = IdxWave<H, DI>;
+  using IW = IdxWave<H, DI, F8>;
   constexpr int J = kCandPerLane;
   // per wavefront: the list-start marks (during the gather) or the radix histogram
   __shared__ uint32_t work_s[4][kMarkCap / 2 > kRadixBins ? kMarkCap / 2 : kRadixBins];
@@ -551,11 +549,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   float* frow = reinterpret_cast<float*>(cl);
   {
     IW iw;
-    iw.load_single(qi + (int64_t)b * T * H * DI, t, wgt, lane & 15, lane >> 4);
-    const uint16_t* kib = ki + (int64_t)b * T * DI;
+    iw.load_single(qi + (int64_t)b * T * H * DI * IW::EB, t, wgt, lane & 15, lane >> 4);
+    const uint8_t* kib = ki + (int64_t)b * T * DI * IW::EB;
     constexpr int U = 16;  // key tiles in flight
     for (int kt0 = 0; kt0 * 16 <= t; kt0 += U) {
-      u32x4 bk[U][IW::KS];
+      typename IW::Keys bk[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
         IW::load_keys(kib, min((kt0 + u) * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
@@ -659,7 +657,7 @@ size_t indexer_topk_workspace_bytes(int B, int row_begin, int row_end, int k) {
 }
 
 hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T,
-                               int H_I, int D_I, int row_begin, int row_end, int k,
+                               int H_I, int D_I, bool f8, int row_begin, int row_end, int k,
                                int32_t* idx, void* workspace, hipStream_t st) {
   const IdxTopkPlan p = plan_indexer_topk(B, row_begin, row_end, k);
   char* ws = static_cast<char*>(workspace);
@@ -671,8 +669,8 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
   const int R = row_end - row_begin;
 
   // the sample: slot chunks of 64 spread the short sampled rows over more workgroups
-  hipError_t e = launch_indexer_mfma(qi, ki, w, B, T, H_I, D_I, row_begin, row_end, p.sshift,
-                                     p.sshift > 0 ? 64 : kIdxChunk, samp, p.ns_ld, st);
+  hipError_t e = launch_indexer_mfma(qi, ki, w, B, T, H_I, D_I, f8, row_begin, row_end,
+                                     p.sshift, p.sshift > 0 ? 64 : kIdxChunk, samp, p.ns_ld, st);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)B * R;
   hipLaunchKernelGGL(sample_threshold, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, samp,
@@ -682,25 +680,18 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
   const int strips = (R + kIdxStrip - 1) / kIdxStrip;
   const dim3 g3((unsigned)(strips * kIdxGroups), (unsigned)B);
   const dim3 g4((unsigned)((rows + 3) / 4));
-#define SA_IDXTK(HH, DD)                                                                        \
-  do {                                                                                          \
-    hipLaunchKernelGGL((indexer_cand<HH, DD>), g3, dim3(256), 0, st, (const uint16_t*)qi,       \
-                       (const uint16_t*)ki, w, T, row_begin, row_end, k, thr, cnt, cand,        \
-                       p.nch);                                                                  \
-    if ((e = hipGetLastError()) != hipSuccess) return e;                                        \
-    hipLaunchKernelGGL((cand_topk<HH, DD>), g4, dim3(256), 0, st, (const uint16_t*)qi,          \
-                       (const uint16_t*)ki, w, B, T, row_begin, row_end, k, thr, cnt, cand,     \
-                       p.nch, idx, stat);                                                       \
-  } while (0)
-  if (H_I == 4) {
-    if (D_I == 32) SA_IDXTK(4, 32); else if (D_I == 64) SA_IDXTK(4, 64); else SA_IDXTK(4, 128);
-  } else if (H_I == 2) {
-    if (D_I == 32) SA_IDXTK(2, 32); else if (D_I == 64) SA_IDXTK(2, 64); else SA_IDXTK(2, 128);
-  } else {
-    if (D_I == 32) SA_IDXTK(1, 32); else if (D_I == 64) SA_IDXTK(1, 64); else SA_IDXTK(1, 128);
-  }
-#undef SA_IDXTK
-  return hipGetLastError();
+  return dispatch_indexer(H_I, D_I, f8, [&](auto h, auto d, auto f) {
+    constexpr int HH = decltype(h)::value, DD = decltype(d)::value;
+    constexpr bool FF = decltype(f)::value;
+    hipLaunchKernelGGL((indexer_cand<HH, DD, FF>), g3, dim3(256), 0, st, (const uint8_t*)qi,
+                       (const uint8_t*)ki, w, T, row_begin, row_end, k, thr, cnt, cand, p.nch);
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL((cand_topk<HH, DD, FF>), g4, dim3(256), 0, st, (const uint8_t*)qi,
+                       (const uint8_t*)ki, w, B, T, row_begin, row_end, k, thr, cnt, cand,
+                       p.nch, idx, stat);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace sa

@@ -84,7 +84,8 @@ int sa_indexer_scores(const void* qi, const void* ki, const float* w, int B, int
     REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
     REQUIRE(H_I >= 1 && H_I <= 64, "H_I must be in [1, 64] (got %d)", H_I);
     REQUIRE(D_I >= 8 && D_I <= 256 && D_I % 8 == 0, "D_I must be a multiple of 8 in [8, 256] (got %d)", D_I);
-    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+            dtype);
     REQUIRE(0 <= row_begin && row_begin < row_end && row_end <= T,
             "need 0 <= row_begin < row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
     REQUIRE(ld >= row_end && ld % 4 == 0, "ld must be >= row_end and a multiple of 4 (got %lld)",
@@ -92,7 +93,9 @@ int sa_indexer_scores(const void* qi, const void* ki, const float* w, int B, int
     REQUIRE((int64_t)B * (row_end - row_begin) * ld <= kMaxElems, "scores buffer too large");
     REQUIRE(B <= 65535, "B must be <= 65535 (got %d)", B);
     SUPPORT(H_I * D_I <= 4096, "H_I * D_I must be <= 4096 (got %d)", H_I * D_I);
-    return hip_status(sa::launch_indexer_scores(qi, ki, w, B, T, H_I, D_I, dtype == SA_BF16,
+    SUPPORT(dtype != SA_FP8_E4M3 || sa::indexer_has_mfma(dtype, H_I, D_I),
+            "E4M3 inputs need H_I in {1,2,4} and D_I in {32,64,128} (H_I=%d D_I=%d)", H_I, D_I);
+    return hip_status(sa::launch_indexer_scores(qi, ki, w, B, T, H_I, D_I, dtype,
                                                 row_begin, row_end, scores, ld, as_stream(stream)),
                       "sa_indexer_scores launch");
   } catch (...) {
@@ -144,23 +147,25 @@ int sa_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T
     REQUIRE_PTR(idx);
     REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
     REQUIRE(B <= 65535, "B must be <= 65535 (got %d)", B);
-    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+            dtype);
     REQUIRE(0 <= row_begin && row_begin < row_end && row_end <= T,
             "need 0 <= row_begin < row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
     REQUIRE(k >= 1 && k <= 4096, "k must be in [1, 4096] (got %d)", k);
     REQUIRE(H_I >= 1 && D_I >= 1, "H_I and D_I must be >= 1 (H_I=%d D_I=%d)", H_I, D_I);
     REQUIRE((int64_t)B * (row_end - row_begin) <= 0x7fffffff, "too many rows in one call");
     SUPPORT(T <= 262144, "T > 262144 is not supported (T=%d)", T);
-    SUPPORT(sa::indexer_has_mfma(dtype == SA_BF16, H_I, D_I),
-            "the fused path needs bf16, H_I in {1,2,4} and D_I in {32,64,128} "
+    SUPPORT(sa::indexer_has_mfma(dtype, H_I, D_I),
+            "the fused path needs bf16 or E4M3, H_I in {1,2,4} and D_I in {32,64,128} "
             "(dtype=%d H_I=%d D_I=%d)", dtype, H_I, D_I);
     const size_t need = sa::indexer_topk_workspace_bytes(B, row_begin, row_end, k);
     if (!workspace || ws_bytes < need)
       return fail(SA_ERR_WORKSPACE, "sa_indexer_topk: workspace of %zu bytes needed (got %zu)",
                   need, workspace ? ws_bytes : (size_t)0);
     REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
-    return hip_status(sa::launch_indexer_topk(qi, ki, w, B, T, H_I, D_I, row_begin, row_end, k,
-                                              idx, workspace, as_stream(stream)),
+    return hip_status(sa::launch_indexer_topk(qi, ki, w, B, T, H_I, D_I, dtype == SA_FP8_E4M3,
+                                              row_begin, row_end, k, idx, workspace,
+                                              as_stream(stream)),
                       "sa_indexer_topk launch");
   } catch (...) {
     return fail(SA_ERR_INTERNAL, "sa_indexer_topk: unexpected exception");
@@ -180,7 +185,9 @@ int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_
     REQUIRE(topk >= 0 && window >= 0 && topk + window >= 1,
             "need topk >= 0, window >= 0 and topk + window >= 1 (topk=%d window=%d)", topk, window);
     REQUIRE(topk == 0 || idx, "idx is NULL with topk=%d", topk);
-    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+            dtype);
+    SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
     REQUIRE((int64_t)B * T * Hq * D <= kMaxElems, "tensors too large");
     REQUIRE(((int64_t)B * T * Hkv + 7) / 8 * 8 <= 0x7fffffffLL, "too many (token, KV head) items");
     SUPPORT(D == 64 || D == 128, "head dim D=%d is not supported (64, 128)", D);
@@ -209,7 +216,9 @@ int sa_graph_attn_fwd(const void* cq, const void* ck, const void* v, const float
     REQUIRE(D >= 8 && D % 8 == 0, "D must be a positive multiple of 8 (got %d)", D);
     REQUIRE(local >= 0 && local <= 64, "local must be in [0, 64] (got %d)", local);
     REQUIRE(n_pow2 >= 0 && n_pow2 <= 30, "n_pow2 must be in [0, 30] (got %d)", n_pow2);
-    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+            dtype);
+    SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
     REQUIRE((int64_t)B * T * H * D <= kMaxElems, "tensors too large");
     SUPPORT(H * D <= 4096, "H * D must be <= 4096 (got %d)", H * D);
     REQUIRE(((int64_t)B * T * ((H * D / 8 + 63) / 64) + 7) / 8 * 8 <= 0x7fffffffLL, "too many tokens");
@@ -231,7 +240,9 @@ int sa_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, 
     REQUIRE(D >= 4 && D % 4 == 0, "D must be a positive multiple of 4 (got %d)", D);
     REQUIRE(block == 16 || block == 32 || block == 64 || block == 128,
             "block must be 16, 32, 64 or 128 (got %d)", block);
-    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+            dtype);
+    SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
     REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
     return hip_status(sa::launch_block_meanpool(kcache, lens, B, Lmax, Hkv, D, block,
                                                 dtype == SA_BF16, kbar, as_stream(stream)),
@@ -282,7 +293,9 @@ int sa_sparse_decode(const void* q, const void* kcache, const void* vcache, cons
     REQUIRE_PTR(kbar);
     REQUIRE(lens, "lens is NULL");
     REQUIRE_PTR(out);
-    REQUIRE(dtype == SA_F32 || dtype == SA_BF16, "unknown dtype %d", dtype);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+            dtype);
+    SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
     const int rc = decode_check_sizes(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits);
     if (rc != SA_OK) return rc;
     SUPPORT(dtype == SA_BF16, "sa_sparse_decode supports bf16 only");

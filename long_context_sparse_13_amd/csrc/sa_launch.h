@@ -9,15 +9,19 @@
 
 namespace sa {
 
+// Stored element types (the values of the public dtype codes).
+enum Elem { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
+
 hipError_t launch_indexer_scores(const void* qi, const void* ki, const float* w, int B, int T,
-                                 int H_I, int D_I, bool bf16, int row_begin, int row_end,
+                                 int H_I, int D_I, int elem, int row_begin, int row_end,
                                  float* scores, int64_t ld, hipStream_t st);
 
 // MFMA indexer over key slots j at positions j << sshift (sshift = 0: plain scores), slots
 // cut into chunks of `chunk` (a multiple of 64) spread over the workgroups of a strip.
-bool indexer_has_mfma(bool bf16, int H_I, int D_I);
+// f8: qi and ki hold E4M3 codes (else bf16).
+bool indexer_has_mfma(int elem, int H_I, int D_I);
 hipError_t launch_indexer_mfma(const void* qi, const void* ki, const float* w, int B, int T,
-                               int H_I, int D_I, int row_begin, int row_end, int sshift,
+                               int H_I, int D_I, bool f8, int row_begin, int row_end, int sshift,
                                int chunk, float* scores, int64_t ld, hipStream_t st);
 
 hipError_t launch_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
@@ -26,7 +30,7 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, int B, int T, int
 // Fused indexer -> top-k (MFMA indexer configurations only).
 size_t indexer_topk_workspace_bytes(int B, int row_begin, int row_end, int k);
 hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T,
-                               int H_I, int D_I, int row_begin, int row_end, int k,
+                               int H_I, int D_I, bool f8, int row_begin, int row_end, int k,
                                int32_t* idx, void* workspace, hipStream_t st);
 
 hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,

@@ -29,6 +29,9 @@ def dev(x: np.ndarray, dtype: str):
         t = t.to(torch.float32)
     elif dtype == "i32":
         t = t.to(torch.int32)
+    elif dtype == "fp8":  # E4M3 codes (uint8) viewed as float8_e4m3fn
+        assert x.dtype == np.uint8
+        t = t.view(torch.float8_e4m3fn)
     return t.cuda()
 
 

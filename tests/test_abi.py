@@ -73,6 +73,23 @@ def test_indexer_topk_validation_and_workspace(L):
     assert f(P, P, P, 1, 4096, 4, 64, 1, 100, 100, 256, P, P, need, None) == 1  # empty rows
     assert f(P, P, None, 1, 4096, 4, 64, 1, 0, 4096, 256, P, P, need, None) == 1
     assert f(P, P, P, 1, 300000, 4, 64, 1, 0, 4096, 256, P, P, need, None) == 2  # T too long
+    # E4M3 inputs (dtype 2) take the same MFMA configurations
+    assert f(P, P, P, 1, 4096, 3, 64, 2, 0, 4096, 256, P, P, need, None) == 2   # H_I = 3
+    assert f(P, P, P, 1, 4096, 4, 64, 2, 0, 4096, 5000, P, P, need, None) == 1  # k too big
+    assert f(P, P, P, 1, 4096, 4, 64, 2, 0, 4096, 256, P, None, need, None) == 3
+    assert f(P, P, P, 1, 4096, 4, 64, 3, 0, 4096, 256, P, P, need, None) == 1   # dtype
+
+
+def test_e4m3_accepted_by_the_indexer_only(L):
+    # every call fails validation before any launch
+    g = L.sa_indexer_scores
+    assert g(P, P, P, 1, 64, 3, 64, 2, 0, 64, P, 64, None) == 2    # E4M3 needs MFMA shapes
+    assert g(P, P, P, 1, 64, 4, 48, 2, 0, 64, P, 64, None) == 2
+    assert g(P, P, P, 1, 64, 4, 64, 2, 0, 64, P, 60, None) == 1    # ld < row_end
+    assert "E4M3" in (g(P, P, P, 1, 64, 3, 64, 2, 0, 64, P, 64, None) and _err(L))
+    assert L.sa_sparse_attn_fwd(P, P, P, P, 1, 8, 4, 1, 64, 4, 4, 0.1, 2, P, None, None) == 2
+    assert "indexer" in _err(L)
+    assert L.sa_graph_attn_fwd(P, P, P, P, 1.0, 1, 8, 2, 64, 4, 4, 2, P, None, None) == 2
 
 
 def test_attn_validation(L):

@@ -314,6 +314,39 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # ---- the 64K fused index path with 8-bit (E4M3) indexer inputs: the same draws as the
+    # bf16 step, encoded to E4M3; bf16 timed beside on the same sizes
+    W3 = sa_synth.WORKLOADS[3]
+    p = W3.params
+    T3, topk3 = p["T"], p["topk"]
+    log("fused indices with E4M3 inputs (64K)")
+    x8 = sa_synth.indexer_inputs(W3.seed, 1, T3, p["H_I"], p["D_I"], "fp8")
+    qi8 = torch.from_numpy(x8["qi"]).view(torch.float8_e4m3fn).to(dev)
+    ki8 = torch.from_numpy(x8["ki"]).view(torch.float8_e4m3fn).to(dev)
+    w8 = to_dev(x8["w"], "f32")
+    xb = sa_synth.indexer_inputs(W3.seed, 1, T3, p["H_I"], p["D_I"], "bf16")
+    qib, kib, wb = to_dev(xb["qi"], "bf16"), to_dev(xb["ki"], "bf16"), to_dev(xb["w"], "f32")
+    del x8, xb
+    chunk3 = 32768
+    ws3 = torch.empty(sa.sa_indexer_topk_workspace(1, T3, p["H_I"], p["D_I"], T3 - chunk3, T3,
+                                                   topk3), dtype=torch.uint8, device=dev)
+    idx3 = torch.full((1, T3, topk3), -1, dtype=torch.int32, device=dev)
+
+    def fused(qq, kk, ww):
+        for r0 in range(0, T3, chunk3):
+            sa.sa_indexer_topk(qq, kk, ww, topk3, r0, min(T3, r0 + chunk3), idx3, ws3)
+
+    t8 = timed(lambda: fused(qi8, ki8, w8), 5)
+    tb = timed(lambda: fused(qib, kib, wb), 5)
+    flops3 = 2.0 * p["H_I"] * p["D_I"] * T3 * (T3 + 1) / 2
+    rows["indexer_topk_e4m3_64k"] = {
+        "ms_per_step": t8, "bf16_ms_per_step": tb, "speedup_vs_bf16": tb / t8,
+        "effective_tflops": flops3 / (t8 * 1e-3) / 1e12,
+        "input_bytes": qi8.numel() + ki8.numel(), "bf16_input_bytes": 2 * (qib.numel() + kib.numel()),
+    }
+    del qi8, ki8, w8, qib, kib, wb, ws3, idx3
+    torch.cuda.empty_cache()
+
     # ---- fixed-graph distance attention: the 16K workload, and the same distributions
     # at 64K and 128K (16K alone is launch/latency-bound)
     W2 = sa_synth.WORKLOADS[2]

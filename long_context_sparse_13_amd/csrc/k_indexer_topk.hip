@@ -30,6 +30,7 @@
 #include "indexer_tile.h"
 #include "sa_launch.h"
 #include "sa_device.h"
+#include "topk_common.h"
 
 #include <climits>
 #include <type_traits>
@@ -296,17 +297,10 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
 constexpr int kCandPerLane = 64;
 constexpr int kMarkCap = 64 * kCandPerLane;  // entries the mark table covers
 
-template <int H, int DI, bool F8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cand_topk(const uint8_t* __restrict__ qi,
-                                                  const uint8_t* __restrict__ ki,
-                                                  const float* __restrict__ wgt, int B, int T,
-                                                  int row_begin, int row_end, int k,
-                                                  const float* __restrict__ thr,
-                                                  const uint16_t* __restrict__ counts,
-                                                  u32x2* __restrict__ cand, int nch,
-                                                  int32_t* __restrict__ idx,
-                                                  uint32_t* __restrict__ n_recomputed) {
-  using IW = IdxWave<H, DI, F8>;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cand_topk(
+    int B, int T, int row_begin, int row_end, int k, const float* __restrict__ thr,
+    const uint16_t* __restrict__ counts, const u32x2* __restrict__ cand, int nch,
+    int32_t* __restrict__ idx, uint32_t* __restrict__ n_recomputed, int* __restrict__ fix_rows) {
   constexpr int J = kCandPerLane;
   // per wavefront: the list-start marks (during the gather) or the radix histogram
   __shared__ uint32_t work_s[4][kMarkCap / 2 > kRadixBins ? kMarkCap / 2 : kRadixBins];
@@ -328,7 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   }
   const int64_t rowi = (int64_t)b * R + r;
   const uint16_t* __restrict__ cr = counts + rowi * nch;
-  u32x2* __restrict__ cl = cand + rowi * nch * kIdxChunk;
+  const u32x2* __restrict__ cl = cand + rowi * nch * kIdxChunk;
   uint32_t* hist = work_s[wv];
   uint16_t* mark = reinterpret_cast<uint16_t*>(work_s[wv]);
   uint32_t* nz = nz_s[wv];
@@ -542,67 +536,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     return;
   }
 
-  // ---- fewer entries than k (the threshold was above the k-th score): recompute the
-  // row in full into its own list area (16-byte aligned, (t/256 + 1) * 2 KB >= 4 (t + 1)
-  // bytes) and select there
-  if (lane == 0) atomicAdd(n_recomputed, 1u);
-  float* frow = reinterpret_cast<float*>(cl);
-  {
+  // ---- fewer entries than k (the threshold was above the k-th score): the row is listed,
+  // and fix_score / fix_select recompute and select it over the whole grid
+  if (lane == 0) fix_rows[atomicAdd(n_recomputed, 1u)] = (int)rowi;
+}
+
+// ---------------------------------------------------------------- 5. listed rows
+// fix_score scores each row listed by cand_topk in full into the row's own list area
+// (16-byte aligned, (t/256 + 1) * 2 KB >= 4 (t + 1) bytes), one wavefront per 256-key
+// chunk of a row, spread over the whole grid, with the same MFMA arithmetic as every
+// other indexer kernel; fix_select then runs the two-step path's two-pass radix selection
+// (topk_row) over each listed row.  With no listed row both return at once.
+template <int H, int DI, bool F8>
+__global__ __launch_bounds__(256) void fix_score(const uint8_t* __restrict__ qi,
+                                                 const uint8_t* __restrict__ ki,
+                                                 const float* __restrict__ wgt, int T,
+                                                 int row_begin, int row_end,
+                                                 u32x2* __restrict__ cand, int nch,
+                                                 const uint32_t* __restrict__ n_fix,
+                                                 const int* __restrict__ fix_rows) {
+  using IW = IdxWave<H, DI, F8>;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = row_end - row_begin;
+  const int maxch = (row_end - 1) / kIdxChunk + 1;
+  const int64_t items = (int64_t)__builtin_amdgcn_readfirstlane((int)*n_fix) * maxch;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wv; it < items; it += (int64_t)gridDim.x * 4) {
+    const int i = (int)(it / maxch), c = (int)(it % maxch);
+    const int rowi = fix_rows[i];
+    const int b = rowi / R, t = row_begin + rowi % R;
+    if (c * kIdxChunk > t) continue;
+    float* frow = reinterpret_cast<float*>(cand + (int64_t)rowi * nch * kIdxChunk);
     IW iw;
     iw.load_single(qi + (int64_t)b * T * H * DI * IW::EB, t, wgt, lane & 15, lane >> 4);
     const uint8_t* kib = ki + (int64_t)b * T * DI * IW::EB;
-    constexpr int U = 16;  // key tiles in flight
-    for (int kt0 = 0; kt0 * 16 <= t; kt0 += U) {
-      typename IW::Keys bk[U];
+    constexpr int U = kIdxChunk / 16;  // the chunk's key tiles, all in flight
+    typename IW::Keys bk[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        IW::load_keys(kib, min((kt0 + u) * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
+    for (int u = 0; u < U; ++u)
+      IW::load_keys(kib, min(c * kIdxChunk + u * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float sc = iw.score_single(bk[u]);
-        const int key = (kt0 + u) * 16 + (lane & 15);
-        if (lane < 16 && key <= t) frow[key] = sc;
-      }
+    for (int u = 0; u < U; ++u) {
+      const float sc = iw.score_single(bk[u]);
+      const int key = c * kIdxChunk + u * 16 + (lane & 15);
+      if (lane < 16 && key <= t) frow[key] = sc;
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");  // the row's stores are complete
-  // lane L owns the positions [lo_e, hi_e) (whole float4s)
-  const int seg = ((n + 63) / 64 + 3) & ~3;
-  const int lo_e = min(n, lane * seg), hi_e = min(n, lo_e + seg);
-  auto each_key = [&](auto&& f) {
-    for (int e = lo_e; e < hi_e; e += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(frow + e);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (e + u < hi_e) f(order_key(x[u]), e + u);
-    }
-  };
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  each_key([&](uint32_t key, int) {
-    mn = min(mn, key);
-    mx = max(mx, key);
-  });
-  wave_minmax(mn, mx);
-  wave_radix_kth(mn, mx - mn, k,
-                 [&](auto&& f) { each_key([&](uint32_t key, int) { f(key); }); }, hist, lane,
-                 v, take_eq, whole);
-  int ng = 0, ne = 0;
-  each_key([&](uint32_t key, int) {
-    ng += key > v;
-    ne += key == v;
-  });
-  int tg, te;
-  int gb = wave_excl_sum(ng, tg);
-  int eb = wave_excl_sum(ne, te);
-  each_key([&](uint32_t key, int e) {
-    if (key > v) {
-      out[gb + min(eb, take_eq)] = e;
-      ++gb;
-    } else if (key == v) {
-      if (eb < take_eq) out[gb + eb] = e;
-      ++eb;
-    }
-  });
+}
+
+__global__ __launch_bounds__(kTkThreads) void fix_select(int T, int row_begin, int row_end, int k,
+                                                         const u32x2* __restrict__ cand, int nch,
+                                                         int32_t* __restrict__ idx,
+                                                         const uint32_t* __restrict__ n_fix,
+                                                         const int* __restrict__ fix_rows) {
+  __shared__ TopkShared sh;
+  const int R = row_end - row_begin;
+  const int cnt = (int)*n_fix;
+  for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
+    const int rowi = fix_rows[i];
+    const int b = rowi / R, t = row_begin + rowi % R;
+    const float* frow = reinterpret_cast<const float*>(cand + (int64_t)rowi * nch * kIdxChunk);
+    topk_row(frow, t + 1, k, idx + ((int64_t)b * T + t) * k, sh);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -611,7 +607,7 @@ namespace {
 struct IdxTopkPlan {
   int sshift, jrank, nch;
   int64_t ns_ld;
-  size_t off_stat, off_samp, off_thr, off_cnt, off_cand, total;
+  size_t off_stat, off_samp, off_thr, off_cnt, off_fix, off_cand, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -644,6 +640,8 @@ IdxTopkPlan plan_indexer_topk(int B, int row_begin, int row_end, int k) {
   o = align256(o + (size_t)rows * sizeof(float));
   p.off_cnt = o;
   o = align256(o + (size_t)rows * p.nch * sizeof(uint16_t));
+  p.off_fix = o;  // int32: rows listed for recomputation
+  o = align256(o + (size_t)rows * sizeof(int));
   p.off_cand = o;
   o = align256(o + (size_t)rows * p.nch * kIdxChunk * sizeof(u32x2));
   p.total = o;
@@ -666,6 +664,7 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
   uint16_t* cnt = reinterpret_cast<uint16_t*>(ws + p.off_cnt);
   u32x2* cand = reinterpret_cast<u32x2*>(ws + p.off_cand);
   uint32_t* stat = reinterpret_cast<uint32_t*>(ws + p.off_stat);
+  int* fix = reinterpret_cast<int*>(ws + p.off_fix);
   const int R = row_end - row_begin;
 
   // the sample: slot chunks of 64 spread the short sampled rows over more workgroups
@@ -687,9 +686,14 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
                        (const uint8_t*)ki, w, T, row_begin, row_end, k, thr, cnt, cand, p.nch);
     hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL((cand_topk<HH, DD, FF>), g4, dim3(256), 0, st, (const uint8_t*)qi,
-                       (const uint8_t*)ki, w, B, T, row_begin, row_end, k, thr, cnt, cand,
-                       p.nch, idx, stat);
+    hipLaunchKernelGGL(cand_topk, g4, dim3(256), 0, st, B, T, row_begin, row_end, k, thr, cnt,
+                       cand, p.nch, idx, stat, fix);
+    if ((e2 = hipGetLastError()) != hipSuccess) return e2;
+    hipLaunchKernelGGL((fix_score<HH, DD, FF>), dim3(512), dim3(256), 0, st, (const uint8_t*)qi,
+                       (const uint8_t*)ki, w, T, row_begin, row_end, cand, p.nch, stat, fix);
+    if ((e2 = hipGetLastError()) != hipSuccess) return e2;
+    hipLaunchKernelGGL(fix_select, dim3(256), dim3(kTkThreads), 0, st, T, row_begin, row_end, k,
+                       cand, p.nch, idx, stat, fix);
     return hipGetLastError();
   });
 }

@@ -346,6 +346,141 @@ def sparse_decode(q, kcache, vcache, lens, block: int, top_blocks: int, window: 
 
 
 # ----------------------------------------------------------------------------------------
+# NSA's three branches  [NSA] "Puntos Clave" (hierarchical sparsity: coarse token
+# compression, fine-grained selection, sliding window) and "Análisis Profundo"
+# (compression and selection combined; one KV fetch per GQA group)
+# ----------------------------------------------------------------------------------------
+
+def cmp_attn(q, kbar, vbar, block: int, scale: float, rows=None):
+    """Compressed branch: O[b,t,h] = Σ_j softmax_j(scale·q[b,t,h]·kbar[b,j,g]) · vbar[b,j,g]
+    over the complete blocks whose last token is at or before t, j < (t+1) // block.
+
+    Returns (O [B,R,Hq,D], LSE [B,Hq,R]); a row with no complete block gets O = 0 and
+    LSE = -inf.  Reading: the compressed keys and values are the block means of K and V
+    (the decode path's pooling, ``block_meanpool``), and a block joins once it is complete.
+    """
+    B, T, Hq, D = q.shape
+    Hkv = kbar.shape[2]
+    G = Hq // Hkv
+    rows = list(range(T)) if rows is None else list(rows)
+    O = np.zeros((B, len(rows), Hq, D))
+    LSE = np.zeros((B, Hq, len(rows)))
+    for b in range(B):
+        for r, t in enumerate(rows):
+            nfull = (t + 1) // block
+            for g in range(Hkv):
+                qh = _f64(q[b, t, g * G:(g + 1) * G])
+                kb = _f64(kbar[b, :nfull, g])
+                logits = scale * np.matmul(qh, kb.T)                       # [G, nfull]
+                o, lse = _masked_softmax_attend(logits, np.ones(nfull, dtype=bool),
+                                                _f64(vbar[b, :nfull, g]))
+                O[b, r, g * G:(g + 1) * G] = o
+                LSE[b, g * G:(g + 1) * G, r] = lse
+    return O, LSE
+
+
+def block_select_rows(q, kbar, block: int, top_blocks: int, rows=None) -> np.ndarray:
+    """sel[b, r, :]: for query row t = rows[r], the top ``top_blocks`` complete blocks
+    (j < (t+1) // block) by score_j = Σ_h q[b,t,h] · kbar[b,j,g(h)] over every query head,
+    ties to the lower j, ascending, padded with -1.  Reading: one selection per query row
+    shared by all heads, as the token-level path shares its top-k (for one KV head this
+    is the per-group rule of the decode path); raw dot products, no scale."""
+    B, T, Hq, D = q.shape
+    Hkv = kbar.shape[2]
+    G = Hq // Hkv
+    rows = list(range(T)) if rows is None else list(rows)
+    sel = np.full((B, len(rows), top_blocks), -1, dtype=np.int32)
+    for b in range(B):
+        for r, t in enumerate(rows):
+            nfull = (t + 1) // block
+            scores = np.zeros(nfull)
+            for g in range(Hkv):
+                qg = _f64(q[b, t, g * G:(g + 1) * G])
+                scores += np.matmul(qg, _f64(kbar[b, :nfull, g]).T).sum(axis=0)
+            sel[b, r] = topk_select_row(scores, top_blocks)
+    return sel
+
+
+def block_tokens(sel_row, block: int) -> np.ndarray:
+    """The token positions of the listed blocks (-1 entries skipped), ascending, padded
+    with -1 to len(sel_row) * block entries."""
+    out = np.full(len(sel_row) * block, -1, dtype=np.int32)
+    toks = sorted(int(j) * block + i for j in np.asarray(sel_row) if j >= 0 for i in range(block))
+    out[: len(toks)] = toks
+    return out
+
+
+def nsa_combine(gates, o_cmp, o_slc, o_win) -> np.ndarray:
+    """O = g0·O_cmp + g1·O_slc + g2·O_win per (token, head); gates [..., Hq, 3].
+    Reading: the page names the three branches but not how they are joined; NSA gates
+    them, and the gates (learned from the query in NSA) are inputs here."""
+    g = _f64(gates)
+    return g[..., 0:1] * o_cmp + g[..., 1:2] * o_slc + g[..., 2:3] * o_win
+
+
+def nsa_prefill(q, k, v, gates, block: int, top_blocks: int, window: int, scale: float,
+                rows=None):
+    """The three branches for every requested row, each its own softmax: compressed
+    (``cmp_attn``), selected (the tokens of the row's ``block_select_rows`` blocks, all
+    before or at t since the blocks are complete; no window), window (the last
+    ``window`` tokens, self included); then ``nsa_combine``.
+    Returns (O [B,R,Hq,D], (O_cmp, O_slc, O_win), sel [B,R,top_blocks])."""
+    B, T, Hq, D = q.shape
+    rows = list(range(T)) if rows is None else list(rows)
+    lens = np.full(B, T)
+    kbar = block_meanpool(k, lens, block)
+    vbar = block_meanpool(v, lens, block)
+    o_cmp, _ = cmp_attn(q, kbar, vbar, block, scale, rows)
+    sel = block_select_rows(q, kbar, block, top_blocks, rows)
+    idx = np.full((B, T, top_blocks * block), -1, dtype=np.int32)
+    for b in range(B):
+        for r, t in enumerate(rows):
+            idx[b, t] = block_tokens(sel[b, r], block)
+    o_slc, _ = sparse_attn(q, k, v, idx, 0, scale, rows)
+    o_win, _ = sparse_attn(q, k, v, np.full((B, T, 1), -1, dtype=np.int32), window, scale, rows)
+    g = np.stack([_f64(gates[:, t]) for t in rows], axis=1)
+    return nsa_combine(g, o_cmp, o_slc, o_win), (o_cmp, o_slc, o_win), sel
+
+
+def nsa_decode(q, kcache, vcache, lens, gates, block: int, top_blocks: int, window: int,
+               scale: float, kbar=None, vbar=None):
+    """One decode step per sequence with the three branches of the query at position
+    lens[b]-1: compressed (every complete block j < lens[b] // block), selected (all tokens
+    of the ``decode_select`` blocks of the query's KV group), window ([L-window, L)); each
+    its own softmax, then ``nsa_combine`` with gates [B,Hq,3].
+    Returns (O [B,Hq,D], (O_cmp, O_slc, O_win), sel [B,Hkv,top_blocks])."""
+    B, Hq, D = q.shape
+    Hkv = kcache.shape[2]
+    G = Hq // Hkv
+    if kbar is None:
+        kbar = block_meanpool(kcache, lens, block)
+    if vbar is None:
+        vbar = block_meanpool(vcache, lens, block)
+    sel = decode_select(q, kbar, lens, top_blocks, block)
+    outs = [np.zeros((B, Hq, D)) for _ in range(3)]
+    for b in range(B):
+        L = int(lens[b])
+        nfull = L // block
+        for g in range(Hkv):
+            qg = _f64(q[b, g * G:(g + 1) * G])
+            hs = slice(g * G, (g + 1) * G)
+            lc = scale * np.matmul(qg, _f64(kbar[b, :nfull, g]).T)
+            outs[0][b, hs], _ = _masked_softmax_attend(lc, np.ones(nfull, dtype=bool),
+                                                       _f64(vbar[b, :nfull, g]))
+            kb, vb = _f64(kcache[b, :L, g]), _f64(vcache[b, :L, g])
+            logits = scale * np.matmul(qg, kb.T)                              # dense [G, L]
+            m_slc = np.zeros(L, dtype=bool)
+            for j in sel[b, g]:
+                if j >= 0:
+                    m_slc[int(j) * block: int(j) * block + block] = True
+            m_win = np.zeros(L, dtype=bool)
+            m_win[max(0, L - window): L] = True
+            outs[1][b, hs], _ = _masked_softmax_attend(logits, m_slc, vb)
+            outs[2][b, hs], _ = _masked_softmax_attend(logits, m_win, vb)
+    return nsa_combine(gates, *outs), tuple(outs), sel
+
+
+# ----------------------------------------------------------------------------------------
 # Cross-layer index reuse  [IC] paragraph 4 (F layers index and cache, S layers reuse)
 # ----------------------------------------------------------------------------------------
 

@@ -480,4 +480,127 @@ def pin_indexer_e4m3_exact(orc):
             assert abs(row[s] - float(tot)) <= 1e-12 * max(1.0, abs(float(tot))), (t, s)
 
 
+# ------------------------------------------------------------------------------ NSA branches
+
+def _mask_attend64(q, k, v, scale, mask):
+    """[H,D] queries over [n,D] keys/values under a bool mask [n], via float64 SDPA."""
+    H = q.shape[0]
+    if not mask.any():
+        return np.zeros((H, v.shape[1]))
+    kk = np.repeat(np.asarray(k, np.float64)[mask][None], H, axis=0)
+    vv = np.repeat(np.asarray(v, np.float64)[mask][None], H, axis=0)
+    return _sdpa64(np.asarray(q, np.float64)[:, None, :] * scale, kk, vv)[:, 0]
+
+
+def pin_cmp_attn_block1_is_causal_attention(orc):
+    """block = 1: the block means are K and V themselves and every earlier token is a
+    complete block, so the compressed branch is full causal attention (SDPA, causal)."""
+    x = sa_synth.attn_inputs(81, 1, 37, 4, 2, 8, "f32")
+    kbar = orc.block_meanpool(x["k"], np.array([37]), 1)
+    vbar = orc.block_meanpool(x["v"], np.array([37]), 1)
+    O, L = orc.cmp_attn(x["q"], kbar, vbar, 1, 0.3)
+    for g in range(2):
+        qg = np.transpose(x["q"][0, :, 2 * g: 2 * g + 2].astype(np.float64), (1, 0, 2)) * 0.3
+        kg = np.repeat(x["k"][0, :, g][None], 2, axis=0)
+        vg = np.repeat(x["v"][0, :, g][None], 2, axis=0)
+        want = _sdpa64(qg, kg, vg, causal=True)
+        assert np.abs(np.transpose(O[0, :, 2 * g: 2 * g + 2], (1, 0, 2)) - want).max() < 1e-12
+
+
+def pin_cmp_attn_and_selection_brute(orc):
+    """Tiny case by pure-Python loops: block means, the compressed softmax (math.exp) over
+    the complete blocks at or before t, and the block ranking Σ_h q_h·kbar_j over both KV
+    groups with ties to the lower block."""
+    T, Hq, Hkv, D, blk = 23, 4, 2, 3, 4
+    x = sa_synth.attn_inputs(82, 1, T, Hq, Hkv, D, "f32")
+    q, k, v = (x[n].astype(np.float64) for n in ("q", "k", "v"))
+    kbar = orc.block_meanpool(x["k"], np.array([T]), blk)
+    vbar = orc.block_meanpool(x["v"], np.array([T]), blk)
+    O, _ = orc.cmp_attn(x["q"], kbar, vbar, blk, 0.5)
+    sel = orc.block_select_rows(x["q"], kbar, blk, 2)
+    for t in range(T):
+        nfull = (t + 1) // blk
+        mean = lambda arr, j, g, d: sum(arr[0, j * blk + i, g, d] for i in range(blk)) / blk
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            if nfull == 0:
+                assert not O[0, t, h].any()
+                continue
+            lg = [0.5 * sum(q[0, t, h, d] * mean(k, j, g, d) for d in range(D)) for j in range(nfull)]
+            mx = max(lg)
+            e = [math.exp(a - mx) for a in lg]
+            for d in range(D):
+                want = sum(e[j] * mean(v, j, g, d) for j in range(nfull)) / sum(e)
+                assert abs(O[0, t, h, d] - want) < 1e-12
+        sc = [sum(q[0, t, h, d] * mean(k, j, h // 2, d) for h in range(Hq) for d in range(D))
+              for j in range(nfull)]
+        order = sorted(range(nfull), key=lambda j: (-sc[j], j))[:2]
+        want_sel = sorted(order) + [-1] * (2 - len(order))
+        assert list(sel[0, t]) == want_sel, (t, list(sel[0, t]), want_sel)
+
+
+def pin_nsa_prefill_branches_vs_sdpa(orc):
+    """Each branch against SDPA with its own mask: with every complete block selected the
+    selected branch attends to [0, (t+1)//block·block); the window branch to the last W
+    tokens; block = 1 makes the compressed branch causal attention.  One-hot gates give the
+    branches, random gates their weighted sum."""
+    T, Hq, D, blk, W = 40, 2, 8, 1, 5
+    x = sa_synth.attn_inputs(83, 1, T, Hq, 1, D, "f32")
+    gates = sa_synth.rng(84).uniform(0, 1, size=(1, T, Hq, 3))
+    O, (oc, osl, ow), sel = orc.nsa_prefill(x["q"], x["k"], x["v"], gates, blk, T, W, 0.4)
+    k0, v0 = x["k"][0, :, 0], x["v"][0, :, 0]
+    for t in range(T):
+        q = x["q"][0, t]
+        full = np.arange(T) <= t
+        want_c = _mask_attend64(q, k0, v0, 0.4, full)                 # block = 1
+        want_s = _mask_attend64(q, k0, v0, 0.4, np.arange(T) < (t + 1) // blk * blk)
+        want_w = _mask_attend64(q, k0, v0, 0.4, (np.arange(T) <= t) & (np.arange(T) > t - W))
+        assert np.abs(oc[0, t] - want_c).max() < 1e-12
+        assert np.abs(osl[0, t] - want_s).max() < 1e-12
+        assert np.abs(ow[0, t] - want_w).max() < 1e-12
+        g = gates[0, t]
+        want = g[:, 0:1] * want_c + g[:, 1:2] * want_s + g[:, 2:3] * want_w
+        assert np.abs(O[0, t] - want).max() < 1e-12
+    # block 4, two blocks chosen: the selected branch attends to exactly those tokens
+    O2, (_, osl2, _), sel2 = orc.nsa_prefill(x["q"], x["k"], x["v"], gates, 4, 2, W, 0.4, rows=[33])
+    m = np.zeros(T, dtype=bool)
+    for j in sel2[0, 0]:
+        m[j * 4: j * 4 + 4] = True
+    assert m.sum() == 8 and not m[32:].any()
+    assert np.abs(osl2[0, 0] - _mask_attend64(x["q"][0, 33], k0, v0, 0.4, m)).max() < 1e-12
+
+
+def pin_nsa_decode_branches_vs_sdpa(orc):
+    """Decode: the window branch over [L-W, L) and the selected branch over every token of
+    the chosen blocks (window overlap kept: the branches are separate), each against SDPA;
+    the compressed branch with block = 1 is full attention over the cache."""
+    x = sa_synth.decode_inputs(85, 2, 90, 4, 2, 8, "f32", lens=[90, 37])
+    gates = sa_synth.rng(86).uniform(0, 1, size=(2, 4, 3))
+    O, (oc, osl, ow), sel = orc.nsa_decode(x["q"], x["kcache"], x["vcache"], x["lens"], gates,
+                                           8, 3, 20, 0.3)
+    O1, (oc1, _, _), _ = orc.nsa_decode(x["q"], x["kcache"], x["vcache"], x["lens"], gates,
+                                        1, 3, 20, 0.3)
+    for b in range(2):
+        L = int(x["lens"][b])
+        for g in range(2):
+            q = x["q"][b, 2 * g: 2 * g + 2]
+            kb, vb = x["kcache"][b, :L, g], x["vcache"][b, :L, g]
+            m = np.zeros(L, dtype=bool)
+            for j in sel[b, g]:
+                if j >= 0:
+                    m[j * 8: j * 8 + 8] = True
+            assert m.sum() == 8 * min(3, L // 8)
+            win = np.arange(L) >= L - 20
+            ws = _mask_attend64(q, kb, vb, 0.3, m)
+            ww = _mask_attend64(q, kb, vb, 0.3, win)
+            wc1 = _mask_attend64(q, kb, vb, 0.3, np.ones(L, dtype=bool))
+            hs = slice(2 * g, 2 * g + 2)
+            assert np.abs(osl[b, hs] - ws).max() < 1e-12
+            assert np.abs(ow[b, hs] - ww).max() < 1e-12
+            assert np.abs(oc1[b, hs] - wc1).max() < 1e-12
+            gg = gates[b, hs]
+            want = gg[:, 0:1] * oc[b, hs] + gg[:, 1:2] * ws + gg[:, 2:3] * ww
+            assert np.abs(O[b, hs] - want).max() < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

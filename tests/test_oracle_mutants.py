@@ -57,6 +57,20 @@ MUTANTS = [
     ("e4m3_mantissa_sixteenths", "(1.0 + m / 8.0) * np.exp2", "(1.0 + m / 16.0) * np.exp2"),
     ("e4m3_no_nan", "out[(e == 15) & ((c & 7) == 7)] = np.nan", "pass"),
     ("e4m3_sign_dropped", "out = np.where(negative, -magnitude, magnitude)", "out = magnitude"),
+    ("cmp_partial_block_joins", "            nfull = (t + 1) // block\n            for g in range(Hkv):\n                qh",
+     "            nfull = min(kbar.shape[1], (t + block) // block)\n            for g in range(Hkv):\n                qh"),
+    ("cmp_scale_dropped", "logits = scale * np.matmul(qh, kb.T)                       # [G, nfull]",
+     "logits = np.matmul(qh, kb.T)"),
+    ("select_last_group_only", "scores += np.matmul(qg, _f64(kbar[b, :nfull, g]).T).sum(axis=0)",
+     "scores = np.matmul(qg, _f64(kbar[b, :nfull, g]).T).sum(axis=0)"),
+    ("block_tokens_shifted", "int(j) * block + i for j", "int(j) * block + i + 1 for j"),
+    ("combine_gates_swapped", "g[..., 1:2] * o_slc + g[..., 2:3] * o_win",
+     "g[..., 2:3] * o_slc + g[..., 1:2] * o_win"),
+    ("nsa_decode_selected_before_window",
+     "m_slc[int(j) * block: int(j) * block + block] = True",
+     "m_slc[int(j) * block: min(int(j) * block + block, L - window)] = True"),
+    ("nsa_decode_window_without_self", "m_win[max(0, L - window): L] = True",
+     "m_win[max(0, L - window): L - 1] = True"),
 ]
 
 

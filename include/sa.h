@@ -224,6 +224,59 @@ size_t sa_sparse_decode_workspace(int B, int Lmax, int Hq, int Hkv, int D, int b
 int sa_sparse_decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_blocks,
                                  int window);
 
+/*
+ * NSA compressed branch (prefill).  [NSA] "Puntos Clave": coarse token compression keeps
+ * the global context with fewer tokens.  The compressed tokens are the block means of K
+ * and V (sa_block_meanpool of each, lens = T), and a query attends to the blocks that are
+ * complete at or before it:
+ *
+ *   out[b, t, h, :] = sum_{j < (t+1)/block} softmax_j(scale * q[b,t,h,:] . kbar[b,j,g,:])
+ *                                            * vbar[b,j,g,:],   g = h / (Hq/Hkv)
+ *   lse[b, h, t]    = log sum_j exp(scale * q . kbar)   (natural log; -inf, out = 0 when
+ *                                                         no block is complete)
+ *
+ * q, out [B, T, Hq, D] bf16; kbar, vbar [B, T/block, Hkv, D] float32 (rounded to bf16 once
+ * per call into the workspace); lse [B, Hq, T] float32 or NULL.
+ * workspace: at least sa_cmp_attn_workspace(B, T, Hkv, D, block) bytes, any contents.
+ * Requires bf16, D in {64, 128}, Hq/Hkv <= 16, block in {16, 32, 64, 128}.
+ */
+int sa_cmp_attn_fwd(const void* q, const float* kbar, const float* vbar, int B, int T, int Hq,
+                    int Hkv, int D, int block, float scale, int dtype, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream);
+size_t sa_cmp_attn_workspace(int B, int T, int Hkv, int D, int block);
+
+/*
+ * NSA block selection (prefill).  [NSA] "Puntos Clave": fine-grained selection in blocks
+ * ("Utiliza la selección de tokens por bloques").  For each row t in [row_begin, row_end):
+ *
+ *   score_j = sum_h q[b,t,h,:] . kbar[b,j,g(h),:]   (float32; every query head)
+ *
+ * over the complete blocks j < (t+1)/block; the top_blocks best (ties to the lower j; all
+ * of them when fewer are complete), ascending, are written as their tokens:
+ * idx[b, t, i*block + e] = j_i*block + e, -1 padded, so idx [B, T, top_blocks*block] int32
+ * feeds sa_sparse_attn_fwd (window 0) as the selected branch.  One selection per query
+ * row, shared by all heads, as for the token-level top-k.
+ * q [B, T, Hq, D] bf16 or float32; kbar as for sa_cmp_attn_fwd.
+ * workspace: at least sa_block_select_workspace(...) bytes (scores and summed queries).
+ * Requires 1 <= top_blocks <= 64, block in {16, 32, 64, 128}, T/block <= 4096.
+ */
+int sa_block_select(const void* q, const float* kbar, int B, int T, int Hq, int Hkv, int D,
+                    int block, int top_blocks, int dtype, int row_begin, int row_end,
+                    int32_t* idx, void* workspace, size_t ws_bytes, void* stream);
+size_t sa_block_select_workspace(int B, int T, int Hkv, int D, int block, int row_begin,
+                                 int row_end);
+
+/*
+ * NSA gated combine.  [NSA] "Puntos Clave" (three branches) -- the page does not say how
+ * they are joined; NSA gates them per head with weights it learns from the query, which
+ * are an input here:
+ *   out = gates[..., 0] * o_cmp + gates[..., 1] * o_slc + gates[..., 2] * o_win
+ * o_cmp, o_slc, o_win, out [B, T, Hq, D] bf16 (out may alias an input); gates
+ * [B, T, Hq, 3] float32.  Requires D % 8 == 0.
+ */
+int sa_nsa_combine(const void* o_cmp, const void* o_slc, const void* o_win, const float* gates,
+                   int B, int T, int Hq, int D, int dtype, void* out, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* sa_status_str(int status);
 

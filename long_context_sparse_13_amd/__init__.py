@@ -53,6 +53,16 @@ _SIGS = {
                                   _c_size_t, _c_void_p]),
     "sa_sparse_decode_workspace": (_c_size_t, [_c_int] * 9),
     "sa_sparse_decode_auto_splits": (_c_int, [_c_int] * 6),
+    "sa_cmp_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _c_float, _c_int, _c_void_p, _c_void_p,
+                                 _c_void_p, _c_size_t, _c_void_p]),
+    "sa_cmp_attn_workspace": (_c_size_t, [_c_int] * 5),
+    "sa_block_select": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                 _c_size_t, _c_void_p]),
+    "sa_block_select_workspace": (_c_size_t, [_c_int] * 7),
+    "sa_nsa_combine": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "sa_status_str": (ctypes.c_char_p, [_c_int]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_version": (_c_int, []),
@@ -312,3 +322,72 @@ def sa_sparse_decode(q, kcache, vcache, kbar, lens, block: int, top_blocks: int,
     if return_sel:
         res.append(sel)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+# ------------------------------------------------------------------------ NSA branches
+def sa_cmp_attn_workspace(B, T, Hkv, D, block) -> int:
+    return int(lib().sa_cmp_attn_workspace(B, T, Hkv, D, block))
+
+
+def sa_cmp_attn_fwd(q, kbar, vbar, block: int, scale: float, out=None, lse=None,
+                    workspace=None, want_lse: bool = False):
+    """Compressed branch: q [B,T,Hq,D] bf16 over the complete-block means kbar, vbar
+    [B,T/block,Hkv,D] f32.  Returns out (and lse [B,Hq,T] f32 when asked)."""
+    torch = _torch()
+    _dev(q, "q"); _dev(kbar, "kbar", torch.float32); _dev(vbar, "vbar", torch.float32)
+    B, T, Hq, D = q.shape
+    Hkv = kbar.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(sa_cmp_attn_workspace(B, T, Hkv, D, block), 256),
+                                dtype=torch.uint8, device=q.device)
+    rc = lib().sa_cmp_attn_fwd(_p(q), _p(kbar), _p(vbar), B, T, Hq, Hkv, D, block, float(scale),
+                               _dtype_code(q), _p(out), _p(lse), _p(workspace),
+                               workspace.numel(), _stream(q.device))
+    _check("sa_cmp_attn_fwd", rc)
+    return (out, lse) if want_lse else out
+
+
+def sa_block_select_workspace(B, T, Hkv, D, block, row_begin, row_end) -> int:
+    return int(lib().sa_block_select_workspace(B, T, Hkv, D, block, row_begin, row_end))
+
+
+def sa_block_select(q, kbar, block: int, top_blocks: int, row_begin: int = 0,
+                    row_end: int | None = None, idx=None, workspace=None):
+    """Top blocks per query row by sum_h q_h . kbar_j, written as token lists
+    idx [B, T, top_blocks*block] int32 (rows [row_begin, row_end))."""
+    torch = _torch()
+    _dev(q, "q"); _dev(kbar, "kbar", torch.float32)
+    B, T, Hq, D = q.shape
+    Hkv = kbar.shape[2]
+    row_end = T if row_end is None else row_end
+    if idx is None:
+        idx = torch.full((B, T, top_blocks * block), -1, dtype=torch.int32, device=q.device)
+    _dev(idx, "idx", torch.int32)
+    if workspace is None:
+        workspace = torch.empty(max(sa_block_select_workspace(B, T, Hkv, D, block, row_begin,
+                                                              row_end), 256),
+                                dtype=torch.uint8, device=q.device)
+    rc = lib().sa_block_select(_p(q), _p(kbar), B, T, Hq, Hkv, D, block, top_blocks,
+                               _dtype_code(q), row_begin, row_end, _p(idx), _p(workspace),
+                               workspace.numel(), _stream(q.device))
+    _check("sa_block_select", rc)
+    return idx
+
+
+def sa_nsa_combine(o_cmp, o_slc, o_win, gates, out=None):
+    """out = g0*o_cmp + g1*o_slc + g2*o_win; gates [B,T,Hq,3] f32."""
+    torch = _torch()
+    _dev(o_cmp, "o_cmp"); _dev(o_slc, "o_slc", o_cmp.dtype); _dev(o_win, "o_win", o_cmp.dtype)
+    _dev(gates, "gates", torch.float32)
+    B, T, Hq, D = o_cmp.shape
+    if out is None:
+        out = torch.empty_like(o_cmp)
+    rc = lib().sa_nsa_combine(_p(o_cmp), _p(o_slc), _p(o_win), _p(gates), B, T, Hq, D,
+                              _dtype_code(o_cmp), _p(out), _stream(o_cmp.device))
+    _check("sa_nsa_combine", rc)
+    return out

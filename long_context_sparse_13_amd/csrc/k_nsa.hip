@@ -1,0 +1,361 @@
+// NSA's compressed and selected branches for prefill, and the gated combine of the three
+// branches.
+//
+// [NSA] Native Sparse Attention page, "Puntos Clave": a hierarchical sparse strategy of
+// coarse token compression (global context with fewer tokens), fine-grained selection
+// (the most important details, chosen in blocks) and a sliding window (local
+// dependencies); "Análisis Profundo": compression and selection combined, one K/V fetch
+// shared by the query heads of a GQA group.
+//
+//  * round_bf16: the float32 block means (sa_block_meanpool of K and of V) rounded once
+//    per call to bf16 rows for the MFMA tiles.
+//  * cmp_attn_mfma<D>: the compressed branch.  One wavefront per (batch, token, KV head)
+//    runs GroupAttn (attn_tile.h) over the compressed keys j < (t+1)/block, 32 per step;
+//    consecutive tokens go to one XCD, so the few compressed rows they all read stay in
+//    that XCD's L2.
+//  * head_sum + block_scores: score[t, j] = sum_h q[t,h] . kbar[j, g(h)] in float32 for the
+//    complete blocks of each row (the queries of each KV group summed first); a workgroup
+//    owns 64 rows x 64 blocks with the summed queries and the pooled keys staged in LDS,
+//    each thread a 4 x 4 register tile.
+//  * block_topk_expand: one wavefront per row picks the top_blocks blocks (ties to the lower
+//    block; every block when fewer are complete), sorts them and writes their tokens as
+//    the row's index list (ascending, -1 padded) for sa_sparse_attn_fwd.
+//  * nsa_combine: O = g0 * O_cmp + g1 * O_slc + g2 * O_win, 8 elements per thread.
+#include "attn_tile.h"
+#include "sa_launch.h"
+
+#include <climits>
+
+namespace sa {
+
+__global__ __launch_bounds__(256) void round_bf16(const float* __restrict__ src,
+                                                  uint16_t* __restrict__ dst, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * i);
+  st8(dst + 4 * i, u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
+}
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void cmp_attn_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
+    const uint16_t* __restrict__ vb, int B, int T, int Hq, int Hkv, int nb, int block,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  using GA = GroupAttn<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char vl[GA::LDS_BYTES];
+  const int lane = threadIdx.x;
+  const int n = lane & 15, grp = lane >> 4;
+  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * T * Hkv);
+  if (item < 0) return;
+  const int g = (int)(item % Hkv);
+  const int t = (int)((item / Hkv) % T);
+  const int b = (int)(item / ((int64_t)Hkv * T));
+  const int G = Hq / Hkv;
+  const int h = g * G + n;
+  const bool hv = n < G;
+
+  GA ga;
+  ga.init(hv ? q + (((int64_t)b * T + t) * Hq + h) * D : nullptr, grp);
+  const int nfull = (t + 1) / block;  // complete blocks at or before t
+  const int64_t stride = (int64_t)Hkv * D;
+  const uint16_t* kbase = kb + ((int64_t)b * nb * Hkv + g) * D;
+  const uint16_t* vbase = vb + ((int64_t)b * nb * Hkv + g) * D;
+  const int slot = lane & 31;
+  auto fetch = [&](int tile) -> int { return tile * 32 + slot; };
+  auto finish = [&](int, int raw, int& key, uint32_t& vm) {
+    const bool ok = raw < nfull;
+    vm = (uint32_t)ballot(ok);
+    key = ok ? raw : 0;
+  };
+  ga.template run<false>((nfull + 31) / 32, fetch, finish, kbase, vbase, stride, vl, scale_log2,
+                         lane);
+
+  const float l = ga.total_l();
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (hv) {
+    uint16_t* orow = out + (((int64_t)b * T + t) * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < GA::DT; ++dt) {
+      const f32x4 a = ga.acc[dt] * inv;
+      st8(orow + dt * 16 + grp * 4, u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+    }
+    if (lse && grp == 0)
+      lse[((int64_t)b * Hq + h) * T + t] = l > 0.f ? (ga.m_run + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- block selection
+constexpr int kBsRows = 64;    // rows per workgroup
+constexpr int kBsBlks = 64;    // blocks per workgroup
+constexpr int kBsDim = 128;    // feature slice staged at a time
+constexpr int kBsPad = kBsDim + 4;
+
+// qs[b, r, g*D + d] = sum over the query heads h of KV group g of q[b, t, h, d] (float32,
+// heads in increasing order), t = row_begin + r; 4 features per thread.
+template <bool BF>
+__global__ __launch_bounds__(256) void head_sum(const void* __restrict__ q, int T, int Hq,
+                                                int Hkv, int D, int row_begin, int row_end,
+                                                int B, float* __restrict__ qs) {
+  const int E = Hkv * D, G = Hq / Hkv, R = row_end - row_begin;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 features each
+  if (i * 4 >= (int64_t)B * R * E) return;
+  const int64_t f = i * 4;
+  const int64_t br = f / E;
+  const int e = (int)(f % E);
+  const int b = (int)(br / R), r = (int)(br % R);
+  const int g = e / D, d = e % D;
+  const int64_t base = (((int64_t)b * T + row_begin + r) * Hq + g * G) * D + d;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < G; ++hh) {
+    if constexpr (BF) {
+      const u32x2 w = ld8(reinterpret_cast<const uint16_t*>(q) + base + (int64_t)hh * D);
+      s += f32x4{bf16_to_f32((uint16_t)w[0]), bf16_hi(w[0]), bf16_to_f32((uint16_t)w[1]), bf16_hi(w[1])};
+    } else {
+      s += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + base + (int64_t)hh * D);
+    }
+  }
+  *reinterpret_cast<f32x4*>(qs + f) = s;
+}
+
+// sc[b, r, j] = qs[b, r, :] . kbar[b, j, :] (float32) for rows t = row_begin + r and
+// complete blocks j < (t+1)/block; other entries untouched.
+__global__ __launch_bounds__(256) void block_scores(const float* __restrict__ qsum,
+                                                    const float* __restrict__ kbar, int E,
+                                                    int nb, int block, int row_begin,
+                                                    int row_end, float* __restrict__ sc,
+                                                    int64_t ldsc) {
+  __shared__ __attribute__((aligned(16))) float qs[kBsRows][kBsPad];
+  __shared__ __attribute__((aligned(16))) float ks[kBsBlks][kBsPad];
+  const int tid = threadIdx.x;
+  const int R = row_end - row_begin;
+  const int r0 = blockIdx.x * kBsRows;
+  const int j0 = blockIdx.y * kBsBlks;
+  const int b = blockIdx.z;
+  const int t_hi = row_begin + min(r0 + kBsRows, R) - 1;
+  if (j0 >= (t_hi + 1) / block) return;  // every block of the tile is past every row
+  const int tr = tid >> 4, tc = tid & 15;  // 4 rows x 4 blocks per thread
+  float acc[4][4] = {};
+  for (int e0 = 0; e0 < E; e0 += kBsDim) {
+    for (int i = tid; i < kBsRows * kBsDim / 4; i += 256) {
+      const int rr = i / (kBsDim / 4), c = (i % (kBsDim / 4)) * 4;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (r0 + rr < R && e0 + c < E)
+        x = *reinterpret_cast<const f32x4*>(qsum + ((int64_t)b * R + r0 + rr) * E + e0 + c);
+      *reinterpret_cast<f32x4*>(&qs[rr][c]) = x;
+    }
+    for (int i = tid; i < kBsBlks * kBsDim / 4; i += 256) {
+      const int jj = i / (kBsDim / 4), c = (i % (kBsDim / 4)) * 4;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (j0 + jj < nb && e0 + c < E)
+        x = *reinterpret_cast<const f32x4*>(kbar + ((int64_t)b * nb + j0 + jj) * E + e0 + c);
+      *reinterpret_cast<f32x4*>(&ks[jj][c]) = x;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < kBsDim; c += 4) {
+      f32x4 a[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const f32x4*>(&qs[tr * 4 + i][c]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const f32x4*>(&ks[tc * 4 + i][c]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jx = 0; jx < 4; ++jx)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[i][jx] = fmaf(a[i][u], w[jx][u], acc[i][jx]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + tr * 4 + i;
+    if (r >= R) continue;
+    const int nfull = (row_begin + r + 1) / block;
+#pragma unroll
+    for (int jx = 0; jx < 4; ++jx) {
+      const int j = j0 + tc * 4 + jx;
+      if (j < nfull) sc[((int64_t)b * R + r) * ldsc + j] = acc[i][jx];
+    }
+  }
+}
+
+// One wavefront per row: the top `nsel` (<= 64) complete blocks by score, ties to the
+// lower block (every complete block when there are no more than nsel), ascending, written
+// as their tokens to idx[b, t, 0 : nsel*block], -1 padded.  Scores in registers: lane L
+// holds blocks L + 64 m, m < PER.
+template <int PER>
+__global__ __launch_bounds__(256) void block_topk_expand(const float* __restrict__ sc,
+                                                         int64_t ldsc, int B, int T,
+                                                         int row_begin, int row_end, int block,
+                                                         int nsel, int32_t* __restrict__ idx) {
+  __shared__ int sorted_s[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int R = row_end - row_begin;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+  if (item >= (int64_t)B * R) return;
+  const int b = (int)(item / R), r = (int)(item % R);
+  const int t = row_begin + r;
+  const int nfull = (t + 1) / block;
+  const float* row = sc + ((int64_t)b * R + r) * ldsc;
+  int32_t* out = idx + ((int64_t)b * T + t) * ((int64_t)nsel * block);
+  const int take = min(nsel, nfull);
+  int mine = INT_MAX;  // lane i: the block chosen in round i
+  if (take == nfull) {
+    mine = lane < nfull ? lane : INT_MAX;
+  } else {
+    float v[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) v[m] = lane + 64 * m < nfull ? row[lane + 64 * m] : -INFINITY;
+    for (int i = 0; i < take; ++i) {
+      float bv = -INFINITY;
+      int bj = INT_MAX;
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const int j = lane + 64 * m;
+        if (j < nfull && (v[m] > bv || (v[m] == bv && j < bj))) {
+          bv = v[m];
+          bj = j;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {  // the largest score, then the lowest block
+        const float ov = __shfl_xor(bv, off);
+        const int oj = __shfl_xor(bj, off);
+        if (ov > bv || (ov == bv && oj < bj)) {
+          bv = ov;
+          bj = oj;
+        }
+      }
+      if (lane == i) mine = bj;
+      if ((bj & 63) == lane) {  // a chosen block drops out of later rounds
+#pragma unroll
+        for (int m = 0; m < PER; ++m)
+          if (m == (bj >> 6)) v[m] = -INFINITY;
+      }
+    }
+  }
+  // ascending: lane i's rank among the chosen blocks, through LDS
+  int rank = 0;
+  for (int i = 0; i < take; ++i) rank += __shfl(mine, i) < mine;
+  if (lane < take) sorted_s[wv][rank] = mine;
+  wave_lds_sync();
+  for (int i = 0; i < nsel; ++i) {
+    const int blk = i < take ? sorted_s[wv][i] : -1;
+    for (int e = lane; e < block; e += 64)
+      out[(int64_t)i * block + e] = blk >= 0 ? blk * block + e : -1;
+  }
+}
+
+__global__ __launch_bounds__(256) void nsa_combine_k(const uint16_t* __restrict__ oc,
+                                                     const uint16_t* __restrict__ os,
+                                                     const uint16_t* __restrict__ ow,
+                                                     const float* __restrict__ gates, int D,
+                                                     int64_t n8, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t row = (i * 8) / D;  // (token, head)
+  const float g0 = gates[row * 3], g1 = gates[row * 3 + 1], g2 = gates[row * 3 + 2];
+  const u32x4 a = ld16(oc + 8 * i), s = ld16(os + 8 * i), w = ld16(ow + 8 * i);
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float lo = g0 * bf16_to_f32((uint16_t)a[c]) + g1 * bf16_to_f32((uint16_t)s[c]) +
+                     g2 * bf16_to_f32((uint16_t)w[c]);
+    const float hi = g0 * bf16_hi(a[c]) + g1 * bf16_hi(s[c]) + g2 * bf16_hi(w[c]);
+    r[c] = pack_bf16x2(lo, hi);
+  }
+  st16(out + 8 * i, r);
+}
+
+// ---------------------------------------------------------------- host side
+size_t cmp_attn_workspace_bytes(int B, int T, int Hkv, int D, int block) {
+  const int64_t nb = T / block;
+  const size_t one = ((size_t)B * nb * Hkv * D * 2 + 255) / 256 * 256;
+  return 2 * one + 256;
+}
+
+hipError_t launch_cmp_attn(const void* q, const float* kbar, const float* vbar, int B, int T,
+                           int Hq, int Hkv, int D, int block, float scale, void* out, float* lse,
+                           void* workspace, hipStream_t st) {
+  const int nb = T / block;
+  const int64_t n = (int64_t)B * nb * Hkv * D;
+  const size_t one = ((size_t)n * 2 + 255) / 256 * 256;
+  uint16_t* kb = reinterpret_cast<uint16_t*>(workspace);
+  uint16_t* vb = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + one);
+  if (n > 0) {
+    const unsigned g = (unsigned)((n / 4 + 255) / 256);
+    hipLaunchKernelGGL(round_bf16, dim3(g), dim3(256), 0, st, kbar, kb, n / 4);
+    hipLaunchKernelGGL(round_bf16, dim3(g), dim3(256), 0, st, vbar, vb, n / 4);
+  }
+  const int64_t items = (int64_t)B * T * Hkv;
+  const dim3 grid((unsigned)((items + 7) / 8 * 8));
+  const float sl2 = scale * 1.4426950408889634f;
+  if (D == 128)
+    hipLaunchKernelGGL(cmp_attn_mfma<128>, grid, dim3(64), 0, st, (const uint16_t*)q, kb, vb, B,
+                       T, Hq, Hkv, nb, block, sl2, (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL(cmp_attn_mfma<64>, grid, dim3(64), 0, st, (const uint16_t*)q, kb, vb, B,
+                       T, Hq, Hkv, nb, block, sl2, (uint16_t*)out, lse);
+  return hipGetLastError();
+}
+
+size_t block_select_workspace_bytes(int B, int T, int Hkv, int D, int block, int row_begin,
+                                    int row_end) {
+  const int64_t ld = ((int64_t)(T / block) + 3) / 4 * 4;
+  const int64_t rows = (int64_t)B * (row_end - row_begin);
+  const size_t sc = ((size_t)rows * ld * sizeof(float) + 255) / 256 * 256;
+  return sc + (size_t)rows * Hkv * D * sizeof(float) + 256;
+}
+
+hipError_t launch_block_select(const void* q, const float* kbar, int B, int T, int Hq, int Hkv,
+                               int D, bool bf16, int block, int top_blocks, int row_begin,
+                               int row_end, int32_t* idx, void* workspace, hipStream_t st) {
+  const int nb = T / block;
+  const int64_t ld = ((int64_t)nb + 3) / 4 * 4;
+  const int R = row_end - row_begin;
+  const int64_t rows = (int64_t)B * R;
+  const int E = Hkv * D;
+  float* sc = reinterpret_cast<float*>(workspace);
+  float* qs = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       ((size_t)rows * ld * sizeof(float) + 255) / 256 * 256);
+  hipError_t e;
+  if (nb > 0) {
+    const unsigned g0 = (unsigned)((rows * E / 4 + 255) / 256);
+    if (bf16)
+      hipLaunchKernelGGL(head_sum<true>, dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D, row_begin,
+                         row_end, B, qs);
+    else
+      hipLaunchKernelGGL(head_sum<false>, dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D, row_begin,
+                         row_end, B, qs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 g1((unsigned)((R + kBsRows - 1) / kBsRows), (unsigned)((nb + kBsBlks - 1) / kBsBlks),
+                  (unsigned)B);
+    hipLaunchKernelGGL(block_scores, g1, dim3(256), 0, st, qs, kbar, E, nb, block, row_begin,
+                       row_end, sc, ld);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const dim3 g2((unsigned)((rows + 3) / 4));
+  const int per = (nb + 63) / 64;
+  if (per <= 4)
+    hipLaunchKernelGGL(block_topk_expand<4>, g2, dim3(256), 0, st, sc, ld, B, T, row_begin, row_end,
+                       block, top_blocks, idx);
+  else if (per <= 16)
+    hipLaunchKernelGGL(block_topk_expand<16>, g2, dim3(256), 0, st, sc, ld, B, T, row_begin,
+                       row_end, block, top_blocks, idx);
+  else
+    hipLaunchKernelGGL(block_topk_expand<64>, g2, dim3(256), 0, st, sc, ld, B, T, row_begin,
+                       row_end, block, top_blocks, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_nsa_combine(const void* oc, const void* os, const void* ow, const float* gates,
+                              int B, int T, int Hq, int D, void* out, hipStream_t st) {
+  const int64_t n8 = (int64_t)B * T * Hq * D / 8;
+  hipLaunchKernelGGL(nsa_combine_k, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)oc, (const uint16_t*)os, (const uint16_t*)ow, gates, D, n8,
+                     (uint16_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -249,6 +250,107 @@ int sa_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, 
                       "sa_block_meanpool launch");
   } catch (...) {
     return fail(SA_ERR_INTERNAL, "sa_block_meanpool: unexpected exception");
+  }
+}
+
+// ---------------------------------------------------------------- NSA branches (prefill)
+static bool nsa_block_ok(int block) { return block == 16 || block == 32 || block == 64 || block == 128; }
+
+size_t sa_cmp_attn_workspace(int B, int T, int Hkv, int D, int block) {
+  if (B < 1 || T < 1 || Hkv < 1 || D < 1 || !nsa_block_ok(block)) return 0;
+  return sa::cmp_attn_workspace_bytes(B, T, Hkv, D, block);
+}
+
+int sa_cmp_attn_fwd(const void* q, const float* kbar, const float* vbar, int B, int T, int Hq,
+                    int Hkv, int D, int block, float scale, int dtype, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(kbar);
+    REQUIRE_PTR(vbar);
+    REQUIRE_PTR(out);
+    REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
+    REQUIRE(nsa_block_ok(block), "block must be 16, 32, 64 or 128 (got %d)", block);
+    REQUIRE(std::isfinite(scale), "scale must be finite");
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * T * Hq * D <= kMaxElems, "tensors too large");
+    REQUIRE(lse == nullptr || aligned16(lse), "lse is not 16-byte aligned");
+    SUPPORT(dtype == SA_BF16, "the compressed branch takes bf16 queries (dtype=%d)", dtype);
+    SUPPORT(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+    SUPPORT(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+    const size_t need = sa::cmp_attn_workspace_bytes(B, T, Hkv, D, block);
+    if (!workspace || ws_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "sa_cmp_attn_fwd: workspace of %zu bytes needed (got %zu)",
+                  need, workspace ? ws_bytes : (size_t)0);
+    REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    return hip_status(sa::launch_cmp_attn(q, kbar, vbar, B, T, Hq, Hkv, D, block, scale, out, lse,
+                                          workspace, as_stream(stream)),
+                      "sa_cmp_attn_fwd launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_cmp_attn_fwd: unexpected exception");
+  }
+}
+
+size_t sa_block_select_workspace(int B, int T, int Hkv, int D, int block, int row_begin,
+                                 int row_end) {
+  if (B < 1 || T < 1 || Hkv < 1 || D < 1 || !nsa_block_ok(block) || row_begin < 0 ||
+      row_begin >= row_end || row_end > T)
+    return 0;
+  return sa::block_select_workspace_bytes(B, T, Hkv, D, block, row_begin, row_end);
+}
+
+int sa_block_select(const void* q, const float* kbar, int B, int T, int Hq, int Hkv, int D,
+                    int block, int top_blocks, int dtype, int row_begin, int row_end,
+                    int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(kbar);
+    REQUIRE_PTR(idx);
+    REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(B <= 65535, "B must be <= 65535 (got %d)", B);
+    REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
+    REQUIRE(D >= 4 && D % 4 == 0, "D must be a positive multiple of 4 (got %d)", D);
+    REQUIRE(nsa_block_ok(block), "block must be 16, 32, 64 or 128 (got %d)", block);
+    REQUIRE(top_blocks >= 1 && top_blocks <= 64, "top_blocks must be in [1, 64] (got %d)", top_blocks);
+    REQUIRE(0 <= row_begin && row_begin < row_end && row_end <= T,
+            "need 0 <= row_begin < row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * T * top_blocks * block <= kMaxElems, "index buffer too large");
+    SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
+    SUPPORT(T / block <= 4096, "at most 4096 blocks per row (T=%d block=%d)", T, block);
+    const size_t need = sa::block_select_workspace_bytes(B, T, Hkv, D, block, row_begin, row_end);
+    if (!workspace || ws_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "sa_block_select: workspace of %zu bytes needed (got %zu)",
+                  need, workspace ? ws_bytes : (size_t)0);
+    REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    return hip_status(sa::launch_block_select(q, kbar, B, T, Hq, Hkv, D, dtype == SA_BF16, block,
+                                              top_blocks, row_begin, row_end, idx, workspace,
+                                              as_stream(stream)),
+                      "sa_block_select launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_block_select: unexpected exception");
+  }
+}
+
+int sa_nsa_combine(const void* o_cmp, const void* o_slc, const void* o_win, const float* gates,
+                   int B, int T, int Hq, int D, int dtype, void* out, void* stream) {
+  try {
+    REQUIRE_PTR(o_cmp);
+    REQUIRE_PTR(o_slc);
+    REQUIRE_PTR(o_win);
+    REQUIRE_PTR(gates);
+    REQUIRE_PTR(out);
+    REQUIRE(B >= 1 && T >= 1 && Hq >= 1, "B, T and Hq must be >= 1");
+    REQUIRE(D >= 8 && D % 8 == 0, "D must be a positive multiple of 8 (got %d)", D);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * T * Hq * D <= kMaxElems, "tensors too large");
+    SUPPORT(dtype == SA_BF16, "the combine takes bf16 branch outputs (dtype=%d)", dtype);
+    return hip_status(sa::launch_nsa_combine(o_cmp, o_slc, o_win, gates, B, T, Hq, D, out,
+                                             as_stream(stream)),
+                      "sa_nsa_combine launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_nsa_combine: unexpected exception");
   }
 }
 

@@ -61,4 +61,17 @@ hipError_t launch_sparse_decode(const void* q, const void* kcache, const void* v
                                 int n_splits, float scale, void* out, float* lse,
                                 int32_t* sel_out, const DecodeWs& ws, hipStream_t st);
 
+// NSA branches (prefill) and the gated combine.
+size_t cmp_attn_workspace_bytes(int B, int T, int Hkv, int D, int block);
+hipError_t launch_cmp_attn(const void* q, const float* kbar, const float* vbar, int B, int T,
+                           int Hq, int Hkv, int D, int block, float scale, void* out, float* lse,
+                           void* workspace, hipStream_t st);
+size_t block_select_workspace_bytes(int B, int T, int Hkv, int D, int block, int row_begin,
+                                    int row_end);
+hipError_t launch_block_select(const void* q, const float* kbar, int B, int T, int Hq, int Hkv,
+                               int D, bool bf16, int block, int top_blocks, int row_begin,
+                               int row_end, int32_t* idx, void* workspace, hipStream_t st);
+hipError_t launch_nsa_combine(const void* oc, const void* os, const void* ow, const float* gates,
+                              int B, int T, int Hq, int D, void* out, hipStream_t st);
+
 }  // namespace sa

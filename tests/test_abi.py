@@ -153,3 +153,30 @@ def test_decode_auto_splits(L):
     assert L.sa_sparse_decode_auto_splits(1, 131072, 1, 64, 64, 4096) == 32
     assert L.sa_sparse_decode_auto_splits(1024, 131072, 1, 64, 16, 512) == 1
     assert L.sa_sparse_decode_auto_splits(1024, 131072, 1, 64, 16, 512) == 1
+
+
+def test_nsa_validation(L):
+    # every call fails validation, so nothing reaches the GPU
+    ws = L.sa_cmp_attn_workspace(1, 1024, 1, 128, 64)
+    assert ws > 0 and L.sa_cmp_attn_workspace(1, 1024, 1, 128, 48) == 0
+    c = L.sa_cmp_attn_fwd
+    assert c(P, P, P, 1, 1024, 16, 1, 128, 64, 0.1, 0, P, None, P, ws, None) == 2   # f32
+    assert c(P, P, P, 1, 1024, 16, 1, 96, 64, 0.1, 1, P, None, P, ws, None) == 2    # D
+    assert c(P, P, P, 1, 1024, 16, 1, 128, 48, 0.1, 1, P, None, P, ws, None) == 1   # block
+    assert c(P, P, P, 1, 1024, 16, 3, 128, 64, 0.1, 1, P, None, P, ws, None) == 1   # Hq % Hkv
+    assert c(P, P, P, 1, 1024, 16, 1, 128, 64, 0.1, 1, P, None, None, ws, None) == 3
+    assert c(P, P, P, 1, 1024, 16, 1, 128, 64, 0.1, 1, P, None, P, ws - 1, None) == 3
+    assert c(P, P, P, 1, 1024, 32, 1, 128, 64, 0.1, 1, P, None, P, ws, None) == 2   # 32 heads/group
+    s = L.sa_block_select
+    w2 = L.sa_block_select_workspace(1, 1024, 1, 128, 64, 0, 1024)
+    assert w2 > 0 and L.sa_block_select_workspace(1, 1024, 1, 128, 64, 0, 1025) == 0
+    assert s(P, P, 1, 1024, 16, 1, 128, 64, 65, 1, 0, 1024, P, P, w2, None) == 1    # top_blocks
+    assert s(P, P, 1, 1024, 16, 1, 128, 64, 16, 1, 5, 5, P, P, w2, None) == 1       # rows
+    assert s(P, P, 1, 1024, 16, 1, 128, 64, 16, 2, 0, 1024, P, P, w2, None) == 2    # E4M3
+    assert s(P, P, 1, 1024, 16, 1, 128, 64, 16, 1, 0, 1024, P, None, w2, None) == 3
+    big = L.sa_block_select_workspace(1, 300000, 1, 128, 64, 0, 64)
+    assert s(P, P, 1, 300000, 16, 1, 128, 64, 16, 1, 0, 64, P, P, big, None) == 2   # > 4096 blocks
+    m = L.sa_nsa_combine
+    assert m(P, P, P, P, 1, 64, 16, 128, 0, P, None) == 2                          # f32
+    assert m(P, P, P, P, 1, 64, 16, 12, 1, P, None) == 1                           # D % 8
+    assert m(P, P, None, P, 1, 64, 16, 128, 1, P, None) == 1

@@ -347,6 +347,45 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
     del qi8, ki8, w8, qib, kib, wb, ws3, idx3
     torch.cuda.empty_cache()
 
+    # ---- NSA's three branches over the 64K prefill tensors: compressed attention over the
+    # 64-token block means, the top-16 blocks per row, a 512-token window (the block-sparse
+    # decode workload's parameters), gated combine
+    log("NSA three-branch prefill (64K)")
+    T3, Hq3, D3 = q64.shape[1], q64.shape[2], q64.shape[3]
+    nblk, ntop, nwin = 64, 16, 512
+    scale3 = D3 ** -0.5
+    lens3 = torch.full((1,), T3, dtype=torch.int32, device=dev)
+    kbar3 = sa.sa_block_meanpool(k64, lens3, nblk)
+    vbar3 = sa.sa_block_meanpool(v64, lens3, nblk)
+    ws_c = torch.empty(sa.sa_cmp_attn_workspace(1, T3, k64.shape[2], D3, nblk), dtype=torch.uint8,
+                       device=dev)
+    ws_s = torch.empty(sa.sa_block_select_workspace(1, T3, k64.shape[2], D3, nblk, 0, T3),
+                       dtype=torch.uint8, device=dev)
+    idx_n = torch.full((1, T3, ntop * nblk), -1, dtype=torch.int32, device=dev)
+    oc3, os3, ow3, on3 = (torch.empty_like(q64) for _ in range(4))
+    gates3 = torch.rand((1, T3, Hq3, 3), generator=torch.Generator(device=dev).manual_seed(1003),
+                        device=dev, dtype=torch.float32)
+    parts = {
+        "meanpool_k_v": lambda: (sa.sa_block_meanpool(k64, lens3, nblk, kbar3),
+                                 sa.sa_block_meanpool(v64, lens3, nblk, vbar3)),
+        "compressed": lambda: sa.sa_cmp_attn_fwd(q64, kbar3, vbar3, nblk, scale3, out=oc3,
+                                                 workspace=ws_c),
+        "block_select": lambda: sa.sa_block_select(q64, kbar3, nblk, ntop, idx=idx_n,
+                                                   workspace=ws_s),
+        "selected": lambda: sa.sa_sparse_attn_fwd(q64, k64, v64, idx_n, 0, scale3, out=os3),
+        "window": lambda: sa.sa_sparse_attn_fwd(q64, k64, v64, None, nwin, scale3, out=ow3),
+        "combine": lambda: sa.sa_nsa_combine(oc3, os3, ow3, gates3, out=on3),
+    }
+    part_ms = {name: timed(fn, 3) for name, fn in parts.items()}
+    t_nsa = timed(lambda: [fn() for fn in parts.values()], 3)
+    rows["nsa_prefill_64k"] = {
+        "ms_per_step": t_nsa, "query_tokens_per_s": T3 / (t_nsa * 1e-3), "parts_ms": part_ms,
+        "block": nblk, "top_blocks": ntop, "window": nwin,
+        "selected_keys_per_query": ntop * nblk,
+    }
+    del kbar3, vbar3, ws_c, ws_s, idx_n, oc3, os3, ow3, on3, gates3
+    torch.cuda.empty_cache()
+
     # ---- fixed-graph distance attention: the 16K workload, and the same distributions
     # at 64K and 128K (16K alone is launch/latency-bound)
     W2 = sa_synth.WORKLOADS[2]

@@ -11,8 +11,8 @@
 //    per call to bf16 rows for the MFMA tiles.
 //  * cmp_attn_mfma<D>: the compressed branch.  One wavefront per (batch, token, KV head)
 //    runs GroupAttn (attn_tile.h) over the compressed keys j < (t+1)/block, 32 per step;
-//    consecutive tokens go to one XCD, so the few compressed rows they all read stay in
-//    that XCD's L2.
+//    tokens are dealt round-robin over the XCDs, longest first (the work grows with t, and
+//    the compressed rows are few enough for every XCD's L2).
 //  * head_sum + block_scores: score[t, j] = sum_h q[t,h] . kbar[j, g(h)] in float32 for the
 //    complete blocks of each row (the queries of each KV group summed first); a workgroup
 //    owns 64 rows x 64 blocks with the summed queries and the pooled keys staged in LDS,
@@ -45,11 +45,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void cm
   __shared__ __attribute__((aligned(16))) unsigned char vl[GA::LDS_BYTES];
   const int lane = threadIdx.x;
   const int n = lane & 15, grp = lane >> 4;
-  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * T * Hkv);
-  if (item < 0) return;
+  // the work of a token grows with t: tokens are dealt round-robin over the XCDs (every
+  // XCD keeps all the compressed rows in its L2), longest first
+  const int64_t items = (int64_t)B * T * Hkv;
+  if ((int64_t)blockIdx.x >= items) return;
+  const int64_t item = items - 1 - (int64_t)blockIdx.x;
   const int g = (int)(item % Hkv);
-  const int t = (int)((item / Hkv) % T);
-  const int b = (int)(item / ((int64_t)Hkv * T));
+  const int b = (int)((item / Hkv) % B);
+  const int t = (int)(item / ((int64_t)Hkv * B));
   const int G = Hq / Hkv;
   const int h = g * G + n;
   const bool hv = n < G;
@@ -289,7 +292,7 @@ hipError_t launch_cmp_attn(const void* q, const float* kbar, const float* vbar, 
     hipLaunchKernelGGL(round_bf16, dim3(g), dim3(256), 0, st, vbar, vb, n / 4);
   }
   const int64_t items = (int64_t)B * T * Hkv;
-  const dim3 grid((unsigned)((items + 7) / 8 * 8));
+  const dim3 grid((unsigned)items);
   const float sl2 = scale * 1.4426950408889634f;
   if (D == 128)
     hipLaunchKernelGGL(cmp_attn_mfma<128>, grid, dim3(64), 0, st, (const uint16_t*)q, kb, vb, B,

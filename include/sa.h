@@ -267,6 +267,33 @@ size_t sa_block_select_workspace(int B, int T, int Hkv, int D, int block, int ro
                                  int row_end);
 
 /*
+ * Block means rounded to bf16: the same means as sa_block_meanpool (float32 sums of the
+ * block's rows divided by block), written as bf16 (nearest even) for the attention kernels
+ * that read pooled rows as MFMA operands (the compressed branch of decode).
+ * kbar [B, Lmax/block, Hkv, D] bf16, complete blocks only (other rows untouched).
+ */
+int sa_block_meanpool_bf16(const void* kcache, const int32_t* lens, int B, int Lmax, int Hkv,
+                           int D, int block, int dtype, void* kbar, void* stream);
+
+/*
+ * NSA decode branches over one contiguous row range.  [NSA] "Puntos Clave" (compression,
+ * sliding window).  For each sequence b with L = lens[b]:
+ *   kind 0 (window):     rows [max(0, L - window), L) of keys/vals = the K/V caches
+ *                        [B, Lrows = Lmax, Hkv, D];
+ *   kind 1 (compressed): rows [0, L / block) of keys/vals = the bf16 block means
+ *                        (sa_block_meanpool_bf16 of K and of V) [B, Lrows = Lmax/block, Hkv, D];
+ *   out[b, h, :] = sum_{s in range} softmax_s(scale * q[b,h,:] . keys[b,s,g,:]) vals[b,s,g,:]
+ *   lse[b, h]    = log sum exp (natural log; -inf and out = 0 for an empty range)
+ * The selected branch is sa_sparse_decode with window 0 (all tokens of the chosen blocks).
+ * q, out [B, Hq, D] bf16; lens [B] int32 on the device; lse [B, Hq] float32 or NULL.
+ * Requires bf16, D in {64, 128}, Hq/Hkv <= 16, block in {16, 32, 64, 128}.
+ */
+int sa_nsa_decode_branch(const void* q, const void* keys, const void* vals,
+                         const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D, int kind,
+                         int block, int window, float scale, int dtype, void* out, float* lse,
+                         void* stream);
+
+/*
  * NSA gated combine.  [NSA] "Puntos Clave" (three branches) -- the page does not say how
  * they are joined; NSA gates them per head with weights it learns from the query, which
  * are an input here:

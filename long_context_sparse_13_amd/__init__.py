@@ -61,6 +61,11 @@ _SIGS = {
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                  _c_size_t, _c_void_p]),
     "sa_block_select_workspace": (_c_size_t, [_c_int] * 7),
+    "sa_block_meanpool_bf16": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_int, _c_void_p, _c_void_p]),
+    "sa_nsa_decode_branch": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                      _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "sa_nsa_combine": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                 _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "sa_status_str": (ctypes.c_char_p, [_c_int]),
@@ -391,3 +396,37 @@ def sa_nsa_combine(o_cmp, o_slc, o_win, gates, out=None):
                               _dtype_code(o_cmp), _p(out), _stream(o_cmp.device))
     _check("sa_nsa_combine", rc)
     return out
+
+
+def sa_block_meanpool_bf16(kcache, lens, block: int, kbar=None):
+    """Block means rounded to bf16: [B, Lmax//block, Hkv, D] (complete blocks only)."""
+    torch = _torch()
+    _dev(kcache, "kcache"); _dev(lens, "lens", torch.int32)
+    B, Lmax, Hkv, D = kcache.shape
+    if kbar is None:
+        kbar = torch.zeros((B, Lmax // block, Hkv, D), dtype=torch.bfloat16, device=kcache.device)
+    _dev(kbar, "kbar", torch.bfloat16)
+    rc = lib().sa_block_meanpool_bf16(_p(kcache), _p(lens), B, Lmax, Hkv, D, block,
+                                      _dtype_code(kcache), _p(kbar), _stream(kcache.device))
+    _check("sa_block_meanpool_bf16", rc)
+    return kbar
+
+
+def sa_nsa_decode_branch(q, keys, vals, lens, kind: int, block: int, window: int, scale: float,
+                         out=None, lse=None, want_lse: bool = False):
+    """kind 0: q [B,Hq,D] over the window of the caches keys/vals [B,Lmax,Hkv,D];
+    kind 1: over the complete blocks of the bf16 block means [B,Lmax/block,Hkv,D]."""
+    torch = _torch()
+    _dev(q, "q"); _dev(keys, "keys", q.dtype); _dev(vals, "vals", q.dtype)
+    _dev(lens, "lens", torch.int32)
+    B, Hq, D = q.shape
+    _, Lrows, Hkv, _ = keys.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    rc = lib().sa_nsa_decode_branch(_p(q), _p(keys), _p(vals), _p(lens), B, Lrows, Hq, Hkv, D,
+                                    kind, block, window, float(scale), _dtype_code(q), _p(out),
+                                    _p(lse), _stream(q.device))
+    _check("sa_nsa_decode_branch", rc)
+    return (out, lse) if want_lse else out

@@ -24,14 +24,17 @@
 #include "sa_launch.h"
 #include "select.h"
 
+#include <type_traits>
+
 namespace sa {
 
 // ------------------------------------------------------------------------ mean-pool
-template <bool BF>
+// OUT16: the means are written rounded to bf16 (for MFMA operands) instead of float32.
+template <bool BF, bool OUT16>
 __global__ __launch_bounds__(256) void block_meanpool_k(const void* __restrict__ kc,
                                                          const int32_t* __restrict__ lens, int B,
                                                          int Lmax, int Hkv, int D, int block,
-                                                         float* __restrict__ kbar) {
+                                                         void* __restrict__ kbar) {
   const int nb = Lmax / block;
   const int D4 = D / 4;
   const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -61,20 +64,29 @@ __global__ __launch_bounds__(256) void block_meanpool_k(const void* __restrict__
     }
   }
   const float inv = 1.f / (float)block;
-  *reinterpret_cast<f32x4*>(kbar + (((int64_t)b * nb + j) * Hkv + g) * D + dq * 4) =
-      f32x4{s0 * inv, s1 * inv, s2 * inv, s3 * inv};
+  const int64_t o = (((int64_t)b * nb + j) * Hkv + g) * D + dq * 4;
+  if constexpr (OUT16)
+    st8(reinterpret_cast<uint16_t*>(kbar) + o,
+        u32x2{pack_bf16x2(s0 * inv, s1 * inv), pack_bf16x2(s2 * inv, s3 * inv)});
+  else
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(kbar) + o) =
+        f32x4{s0 * inv, s1 * inv, s2 * inv, s3 * inv};
 }
 
 hipError_t launch_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, int Hkv,
-                                 int D, int block, bool bf16, float* kbar, hipStream_t st) {
+                                 int D, int block, bool bf16, void* kbar, bool out16,
+                                 hipStream_t st) {
   const int64_t total = (int64_t)B * (Lmax / block) * Hkv * (D / 4);
   const dim3 grid((unsigned)((total + 255) / 256));
-  if (bf16)
-    hipLaunchKernelGGL(block_meanpool_k<true>, grid, dim3(256), 0, st, kcache, lens, B, Lmax, Hkv,
-                       D, block, kbar);
-  else
-    hipLaunchKernelGGL(block_meanpool_k<false>, grid, dim3(256), 0, st, kcache, lens, B, Lmax, Hkv,
-                       D, block, kbar);
+  auto go = [&](auto bf, auto o16) {
+    hipLaunchKernelGGL((block_meanpool_k<decltype(bf)::value, decltype(o16)::value>), grid,
+                       dim3(256), 0, st, kcache, lens, B, Lmax, Hkv, D, block, kbar);
+  };
+  if (bf16) {
+    if (out16) go(std::true_type{}, std::true_type{}); else go(std::true_type{}, std::false_type{});
+  } else {
+    if (out16) go(std::false_type{}, std::true_type{}); else go(std::false_type{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 

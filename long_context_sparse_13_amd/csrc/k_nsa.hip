@@ -20,6 +20,10 @@
 //  * block_topk_expand: one wavefront per row picks the top_blocks blocks (ties to the lower
 //    block; every block when fewer are complete), sorts them and writes their tokens as
 //    the row's index list (ascending, -1 padded) for sa_sparse_attn_fwd.
+//  * nsa_decode_range<D>: decode attention of each sequence's query over one contiguous
+//    row range of a bf16 cache: the window of the token cache, or the complete blocks of
+//    the pooled cache (the compressed branch); 8 wavefronts per (sequence, KV head), merged
+//    by log-sum-exp in LDS.  The selected branch of decode is sa_sparse_decode with window 0.
 //  * nsa_combine: O = g0 * O_cmp + g1 * O_slc + g2 * O_win, 8 elements per thread.
 #include "attn_tile.h"
 #include "sa_launch.h"
@@ -248,6 +252,99 @@ __global__ __launch_bounds__(256) void block_topk_expand(const float* __restrict
     for (int e = lane; e < block; e += 64)
       out[(int64_t)i * block + e] = blk >= 0 ? blk * block + e : -1;
   }
+}
+
+// ---------------------------------------------------------------- decode: one row range
+// One workgroup of kRangeWaves wavefronts per (sequence, KV head): the wavefronts take
+// consecutive slices of the range (32-row tiles) through GroupAttn, then their partial
+// softmax states are merged by log-sum-exp through LDS.
+constexpr int kRangeWaves = 8;
+
+template <int D>
+__global__ __launch_bounds__(64 * kRangeWaves) void nsa_decode_range(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ keys,
+    const uint16_t* __restrict__ vals, const int32_t* __restrict__ lens, int B, int Lrows,
+    int Hq, int Hkv, int kind, int block, int window, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  using GA = GroupAttn<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char vl[kRangeWaves][GA::LDS_BYTES];
+  __shared__ float pacc[kRangeWaves][16][D];  // unnormalised O per wave and head
+  __shared__ float pm[kRangeWaves][16], pl[kRangeWaves][16];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, grp = lane >> 4;
+  const int b = (int)blockIdx.x / Hkv, g = (int)blockIdx.x % Hkv;
+  const int G = Hq / Hkv;
+  const int h = g * G + n;
+  const bool hv = n < G;
+  const int L = lens[b];
+  const int lo = kind == 0 ? max(0, L - window) : 0;
+  const int hi = kind == 0 ? L : L / block;
+  const int ntiles = (hi - lo + 31) / 32;
+  const int per = (ntiles + kRangeWaves - 1) / kRangeWaves;
+  const int tb = min(ntiles, wv * per), te = min(ntiles, tb + per);
+
+  GA ga;
+  ga.init(hv ? q + ((int64_t)b * Hq + h) * D : nullptr, grp);
+  const int64_t stride = (int64_t)Hkv * D;
+  const uint16_t* kbase = keys + ((int64_t)b * Lrows * Hkv + g) * D;
+  const uint16_t* vbase = vals + ((int64_t)b * Lrows * Hkv + g) * D;
+  const int slot = lane & 31;
+  auto fetch = [&](int tile) -> int { return lo + (tb + tile) * 32 + slot; };
+  auto finish = [&](int, int raw, int& key, uint32_t& vm) {
+    const bool ok = raw < hi;
+    vm = (uint32_t)ballot(ok);
+    key = ok ? raw : lo;
+  };
+  ga.template run<false>(te - tb, fetch, finish, kbase, vbase, stride, vl[wv], scale_log2, lane);
+
+  const float lt = ga.total_l();
+  if (grp == 0) {
+    pm[wv][n] = ga.m_run;
+    pl[wv][n] = lt;
+  }
+#pragma unroll
+  for (int dt = 0; dt < GA::DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pacc[wv][n][dt * 16 + grp * 4 + i] = ga.acc[dt][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += 64 * kRangeWaves) {
+    const int hh = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kRangeWaves; ++w) M = fmaxf(M, pm[w][hh]);
+    float lsum = 0.f, o = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kRangeWaves; ++w) {
+        if (pm[w][hh] > -INFINITY) {
+          const float f = exp2f(pm[w][hh] - M);
+          lsum += f * pl[w][hh];
+          o += f * pacc[w][hh][d];
+        }
+      }
+    }
+    const int64_t oh = (int64_t)b * Hq + g * G + hh;
+    out[oh * D + d] = (uint16_t)f32_to_bf16_bits(lsum > 0.f ? o / lsum : 0.f);
+    if (lse && d == 0) lse[oh] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+hipError_t launch_nsa_decode_range(const void* q, const void* keys, const void* vals,
+                                   const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D,
+                                   int kind, int block, int window, float scale, void* out,
+                                   float* lse, hipStream_t st) {
+  const dim3 grid((unsigned)(B * Hkv));
+  const float sl2 = scale * 1.4426950408889634f;
+  if (D == 128)
+    hipLaunchKernelGGL(nsa_decode_range<128>, grid, dim3(64 * kRangeWaves), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)keys, (const uint16_t*)vals, lens, B,
+                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL(nsa_decode_range<64>, grid, dim3(64 * kRangeWaves), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)keys, (const uint16_t*)vals, lens, B,
+                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void nsa_combine_k(const uint16_t* __restrict__ oc,

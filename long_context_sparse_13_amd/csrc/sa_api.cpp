@@ -246,10 +246,32 @@ int sa_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, 
     SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
     REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
     return hip_status(sa::launch_block_meanpool(kcache, lens, B, Lmax, Hkv, D, block,
-                                                dtype == SA_BF16, kbar, as_stream(stream)),
+                                                dtype == SA_BF16, kbar, false, as_stream(stream)),
                       "sa_block_meanpool launch");
   } catch (...) {
     return fail(SA_ERR_INTERNAL, "sa_block_meanpool: unexpected exception");
+  }
+}
+
+int sa_block_meanpool_bf16(const void* kcache, const int32_t* lens, int B, int Lmax, int Hkv,
+                           int D, int block, int dtype, void* kbar, void* stream) {
+  try {
+    REQUIRE_PTR(kcache);
+    REQUIRE(lens, "lens is NULL");
+    REQUIRE_PTR(kbar);
+    REQUIRE(B >= 1 && Lmax >= 1 && Hkv >= 1, "B, Lmax and Hkv must be >= 1");
+    REQUIRE(D >= 4 && D % 4 == 0, "D must be a positive multiple of 4 (got %d)", D);
+    REQUIRE(block == 16 || block == 32 || block == 64 || block == 128,
+            "block must be 16, 32, 64 or 128 (got %d)", block);
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+            dtype);
+    SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
+    REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
+    return hip_status(sa::launch_block_meanpool(kcache, lens, B, Lmax, Hkv, D, block,
+                                                dtype == SA_BF16, kbar, true, as_stream(stream)),
+                      "sa_block_meanpool_bf16 launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_block_meanpool_bf16: unexpected exception");
   }
 }
 
@@ -330,6 +352,37 @@ int sa_block_select(const void* q, const float* kbar, int B, int T, int Hq, int 
                       "sa_block_select launch");
   } catch (...) {
     return fail(SA_ERR_INTERNAL, "sa_block_select: unexpected exception");
+  }
+}
+
+int sa_nsa_decode_branch(const void* q, const void* keys, const void* vals,
+                         const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D, int kind,
+                         int block, int window, float scale, int dtype, void* out, float* lse,
+                         void* stream) {
+  try {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(keys);
+    REQUIRE_PTR(vals);
+    REQUIRE(lens, "lens is NULL");
+    REQUIRE_PTR(out);
+    REQUIRE(B >= 1 && Lrows >= 1, "B and Lrows must be >= 1 (B=%d Lrows=%d)", B, Lrows);
+    REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
+    REQUIRE(kind == 0 || kind == 1, "kind must be 0 (window) or 1 (compressed) (got %d)", kind);
+    REQUIRE(nsa_block_ok(block), "block must be 16, 32, 64 or 128 (got %d)", block);
+    REQUIRE(window >= 0, "window must be >= 0 (got %d)", window);
+    REQUIRE(std::isfinite(scale), "scale must be finite");
+    REQUIRE((int64_t)B * Hkv <= 0x7fffffff, "too many (sequence, KV head) pairs");
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * Lrows * Hkv * D <= kMaxElems, "cache too large");
+    SUPPORT(dtype == SA_BF16, "the decode branches take bf16 tensors (dtype=%d)", dtype);
+    SUPPORT(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+    SUPPORT(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+    return hip_status(sa::launch_nsa_decode_range(q, keys, vals, lens, B, Lrows, Hq, Hkv, D, kind,
+                                                  block, window, scale, out, lse,
+                                                  as_stream(stream)),
+                      "sa_nsa_decode_branch launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_nsa_decode_branch: unexpected exception");
   }
 }
 

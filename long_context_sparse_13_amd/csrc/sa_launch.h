@@ -42,7 +42,8 @@ hipError_t launch_graph_attn_fwd(const void* cq, const void* ck, const void* v, 
                                  bool bf16, void* out, float* lse, hipStream_t st);
 
 hipError_t launch_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, int Hkv,
-                                 int D, int block, bool bf16, float* kbar, hipStream_t st);
+                                 int D, int block, bool bf16, void* kbar, bool out16,
+                                 hipStream_t st);
 
 struct DecodeWs {
   uint32_t* cand;        // [B, Hkv, scoring workgroups, 16] packed (order key, block)
@@ -71,6 +72,13 @@ size_t block_select_workspace_bytes(int B, int T, int Hkv, int D, int block, int
 hipError_t launch_block_select(const void* q, const float* kbar, int B, int T, int Hq, int Hkv,
                                int D, bool bf16, int block, int top_blocks, int row_begin,
                                int row_end, int32_t* idx, void* workspace, hipStream_t st);
+// Decode attention of each sequence's query over one contiguous row range of a bf16
+// cache: kind 0 = the window [max(0, L - window), L) of the token cache, kind 1 = the
+// complete blocks [0, L / block) of the pooled cache.
+hipError_t launch_nsa_decode_range(const void* q, const void* keys, const void* vals,
+                                   const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D,
+                                   int kind, int block, int window, float scale, void* out,
+                                   float* lse, hipStream_t st);
 hipError_t launch_nsa_combine(const void* oc, const void* os, const void* ow, const float* gates,
                               int B, int T, int Hq, int D, void* out, hipStream_t st);
 

@@ -142,3 +142,46 @@ def test_nsa_prefill_pipeline_vs_oracle():
             continue
         assert np.abs(out[0, t] - want[0, r]).max() < BF16_TOL, t
     assert bad <= 2
+
+
+# ------------------------------------------------------------------------------ decode
+
+def test_meanpool_bf16_is_rounded_float32_mean():
+    import torch
+    x = sa_synth.decode_inputs(851, 3, 500, 4, 2, 64, "bf16", lens=[500, 130, 63])
+    note("block_meanpool_bf16")
+    kc = dev(x["kcache"], "bf16")
+    lens = dev(np.asarray(x["lens"], np.int32), "i32")
+    f32 = sa.sa_block_meanpool(kc, lens, 32)
+    b16 = sa.sa_block_meanpool_bf16(kc, lens, 32)
+    for b, L in enumerate(x["lens"]):
+        nfull = int(L) // 32
+        assert torch.equal(b16[b, :nfull], f32[b, :nfull].to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,block,top,W", [(16, 1, 128, 64, 4, 200), (8, 2, 64, 32, 8, 100)])
+def test_nsa_decode_vs_oracle(Hq, Hkv, D, block, top, W):
+    import torch
+    lens_h = [1500, 999, 64, 1]
+    x = sa_synth.decode_inputs(861 + D, 4, 1500, Hq, Hkv, D, "bf16", lens=lens_h)
+    gates = sa_synth.rng(862).uniform(0, 1, size=(4, Hq, 3)).astype(np.float32)
+    note(f"nsa decode B=4 Lmax=1500 Hq={Hq} Hkv={Hkv} D={D} block={block} top={top} W={W}")
+    scale = D ** -0.5
+    q, kc, vc = dev(x["q"], "bf16"), dev(x["kcache"], "bf16"), dev(x["vcache"], "bf16")
+    lens = dev(np.asarray(lens_h, np.int32), "i32")
+    kbar = sa.sa_block_meanpool(kc, lens, block)
+    kb16 = sa.sa_block_meanpool_bf16(kc, lens, block)
+    vb16 = sa.sa_block_meanpool_bf16(vc, lens, block)
+    oc = sa.sa_nsa_decode_branch(q, kb16, vb16, lens, 1, block, W, scale)
+    ow = sa.sa_nsa_decode_branch(q, kc, vc, lens, 0, block, W, scale)
+    ws = torch.zeros(sa.sa_sparse_decode_workspace(4, 1500, Hq, Hkv, D, block, top, 0), dtype=torch.uint8,
+                     device="cuda")
+    osl = sa.sa_sparse_decode(q, kc, vc, kbar, lens, block, top, 0, scale, workspace=ws)
+    out = sa.sa_nsa_combine(oc[:, None], osl[:, None], ow[:, None], dev(gates[:, None], "f32"))[:, 0]
+    want, (wc, ws_, ww), sel = orc.nsa_decode(x["q"], x["kcache"], x["vcache"], np.asarray(lens_h),
+                                              gates, block, top, W, scale)
+    assert np.abs(host(oc) - wc).max() < BF16_TOL
+    assert np.abs(host(ow) - ww).max() < BF16_TOL
+    assert np.abs(host(osl) - ws_).max() < BF16_TOL
+    assert np.abs(host(out) - want).max() < BF16_TOL
+    assert not host(oc)[3].any()  # one token: no complete block

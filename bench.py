@@ -452,6 +452,37 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
                                                     p["top_blocks"], p["window"]),
         "meanpool_ms_once_per_cache": t_pool,
     }
+    # NSA's three branches on the same caches: compressed (bf16 block means, pooled once per
+    # cache), selected (the chosen blocks' tokens: sa_sparse_decode with window 0), window,
+    # gated combine
+    log("NSA three-branch decode (32 x 128K)")
+    kb16 = sa.sa_block_meanpool_bf16(kc, lens, p["block"])
+    vb16 = sa.sa_block_meanpool_bf16(vc, lens, p["block"])
+    t_pool16 = timed(lambda: (sa.sa_block_meanpool_bf16(kc, lens, p["block"], kb16),
+                              sa.sa_block_meanpool_bf16(vc, lens, p["block"], vb16)), 3)
+    ws0 = torch.zeros(sa.sa_sparse_decode_workspace(p["B"], p["L"], p["Hq"], p["Hkv"], p["D"],
+                                                    p["block"], p["top_blocks"], 0, 0),
+                      dtype=torch.uint8, device=dev)
+    ocd, osd, owd, ond = (torch.empty_like(qd) for _ in range(4))
+    gd = torch.rand((p["B"], 1, p["Hq"], 3), generator=torch.Generator(device=dev).manual_seed(1005),
+                    device=dev, dtype=torch.float32)
+    dparts = {
+        "compressed": lambda: sa.sa_nsa_decode_branch(qd, kb16, vb16, lens, 1, p["block"],
+                                                      p["window"], p["scale"], out=ocd),
+        "selected": lambda: sa.sa_sparse_decode(qd, kc, vc, kbar, lens, p["block"], p["top_blocks"],
+                                                0, p["scale"], workspace=ws0, out=osd),
+        "window": lambda: sa.sa_nsa_decode_branch(qd, kc, vc, lens, 0, p["block"], p["window"],
+                                                  p["scale"], out=owd),
+        "combine": lambda: sa.sa_nsa_combine(ocd[:, None], osd[:, None], owd[:, None], gd,
+                                             out=ond[:, None]),
+    }
+    dpart_us = {name: timed(fn, 20) * 1e3 for name, fn in dparts.items()}
+    t_nd = timed(lambda: [fn() for fn in dparts.values()], 20)
+    rows["nsa_decode_b32_128k"] = {
+        "us_per_step": t_nd * 1e3, "tokens_per_s": p["B"] / (t_nd * 1e-3), "parts_us": dpart_us,
+        "bf16_meanpool_ms_once_per_cache": t_pool16,
+    }
+    del kb16, vb16, ws0, ocd, osd, owd, ond, gd
     del qd, kc, vc, kbar, ws, od
     torch.cuda.empty_cache()
 

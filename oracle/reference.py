@@ -212,6 +212,47 @@ def sparse_attn(q, k, v, idx, window: int, scale: float, rows=None):
     return O, LSE
 
 
+def sparse_attn_bwd(q, k, v, idx, window: int, scale: float, dout):
+    """Gradients of ``sparse_attn`` with respect to q, k and v for the upstream gradient
+    dout [B,T,Hq,D], on the same mask: with P[t,h,s] = softmax_s over S_t and
+    dP[t,h,s] = dout[t,h] . v[s,g],
+
+      dV[s,g] = Σ_t Σ_{h in g} P[t,h,s] dout[t,h]
+      dS[t,h,s] = P[t,h,s] (dP[t,h,s] - Σ_{s'} P[t,h,s'] dP[t,h,s'])
+      dQ[t,h] = scale Σ_s dS[t,h,s] k[s,g]
+      dK[s,g] = scale Σ_t Σ_{h in g} dS[t,h,s] q[t,h]
+
+    (the chain rule through the masked softmax; every unselected key has P = 0).
+    Returns (dQ [B,T,Hq,D], dK [B,T,Hkv,D], dV [B,T,Hkv,D]) in float64.  [NSA] "Puntos
+    Clave" reports the backward pass of sparse attention beside the forward."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    dQ = np.zeros((B, T, Hq, D))
+    dK = np.zeros((B, T, Hkv, D))
+    dV = np.zeros((B, T, Hkv, D))
+    for b in range(B):
+        kb, vb = _f64(k[b]), _f64(v[b])
+        for t in range(T):
+            mask = selected_mask_row(t, idx[b, t], window)
+            if not mask.any():
+                continue
+            for g in range(Hkv):
+                hs = slice(g * G, (g + 1) * G)
+                qh = _f64(q[b, t, hs])                                   # [G, D]
+                do = _f64(dout[b, t, hs])                                # [G, D]
+                logits = scale * np.matmul(qh, kb[: t + 1, g].T)         # [G, t+1]
+                lg = np.where(mask[None, :], logits, NEG_INF)
+                p = np.exp(lg - lg.max(axis=1, keepdims=True))
+                p = p / p.sum(axis=1, keepdims=True)                     # masked softmax
+                dp = np.matmul(do, vb[: t + 1, g].T)                     # [G, t+1]
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dQ[b, t, hs] = scale * np.matmul(ds, kb[: t + 1, g])
+                dK[b, : t + 1, g] += scale * np.matmul(ds.T, qh)
+                dV[b, : t + 1, g] += np.matmul(p.T, do)
+    return dQ, dK, dV
+
+
 # ----------------------------------------------------------------------------------------
 # Fixed-graph distance attention  [SLM] "Cómo eligen los tokens a quién escuchar"
 # ----------------------------------------------------------------------------------------

@@ -480,6 +480,62 @@ def pin_indexer_e4m3_exact(orc):
             assert abs(row[s] - float(tot)) <= 1e-12 * max(1.0, abs(float(tot))), (t, s)
 
 
+# ------------------------------------------------------------------------------ backward
+
+def pin_attn_bwd_vs_autograd(orc):
+    """The gradients against torch autograd in float64 through a dense attention with the
+    same boolean mask (masked logits set to -inf before softmax), two KV groups, listed
+    indices that fall inside the window, -1 padding and out-of-range entries."""
+    import torch
+    B, T, Hq, Hkv, D, k, W = 1, 21, 4, 2, 8, 5, 3
+    x = sa_synth.attn_inputs(91, B, T, Hq, Hkv, D, "f32")
+    idx = sa_synth.random_topk_idx(92, B, T, k, junk=True)
+    dout = sa_synth.rng(93).standard_normal((B, T, Hq, D))
+    dQ, dK, dV = orc.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, W, 0.3, dout)
+    q = torch.tensor(x["q"], dtype=torch.float64, requires_grad=True)
+    kk = torch.tensor(x["k"], dtype=torch.float64, requires_grad=True)
+    vv = torch.tensor(x["v"], dtype=torch.float64, requires_grad=True)
+    mask = np.zeros((T, T), dtype=bool)
+    for t in range(T):
+        for s_ in idx[0, t]:
+            if 0 <= s_ <= t:
+                mask[t, s_] = True
+        mask[t, max(0, t - W + 1): t + 1] = True
+    m = torch.from_numpy(mask)
+    G = Hq // Hkv
+    ke = kk[0].repeat_interleave(G, dim=1).transpose(0, 1)        # [Hq, T, D]
+    ve = vv[0].repeat_interleave(G, dim=1).transpose(0, 1)
+    qe = q[0].transpose(0, 1)
+    lg = 0.3 * torch.matmul(qe, ke.transpose(1, 2))
+    lg = lg.masked_fill(~m[None], float("-inf"))
+    o = torch.matmul(torch.softmax(lg, dim=-1), ve).transpose(0, 1)[None]
+    o.backward(torch.from_numpy(dout))
+    assert np.abs(dQ - q.grad.numpy()).max() < 1e-12
+    assert np.abs(dK - kk.grad.numpy()).max() < 1e-12
+    assert np.abs(dV - vv.grad.numpy()).max() < 1e-12
+
+
+def pin_attn_bwd_finite_differences(orc):
+    """Central differences of <dout, O> through the forward oracle on a tiny case match
+    every gradient entry (step 1e-5, error O(step^2))."""
+    B, T, Hq, Hkv, D, k, W = 1, 7, 2, 1, 3, 3, 2
+    x = sa_synth.attn_inputs(94, B, T, Hq, Hkv, D, "f32")
+    q, kk, vv = (x[n].astype(np.float64) for n in ("q", "k", "v"))
+    idx = sa_synth.random_topk_idx(95, B, T, k)
+    dout = sa_synth.rng(96).standard_normal((B, T, Hq, D))
+    dQ, dK, dV = orc.sparse_attn_bwd(q, kk, vv, idx, W, 0.7, dout)
+    f = lambda a, b_, c: float(np.sum(orc.sparse_attn(a, b_, c, idx, W, 0.7)[0] * dout))
+    eps = 1e-5
+    for arr, grad, which in ((q, dQ, 0), (kk, dK, 1), (vv, dV, 2)):
+        for pos in np.ndindex(arr.shape):
+            a = [q.copy(), kk.copy(), vv.copy()]
+            a[which][pos] += eps
+            up = f(*a)
+            a[which][pos] -= 2 * eps
+            dn = f(*a)
+            assert abs((up - dn) / (2 * eps) - grad[pos]) < 1e-7, (which, pos)
+
+
 # ------------------------------------------------------------------------------ NSA branches
 
 def _mask_attend64(q, k, v, scale, mask):

@@ -69,6 +69,13 @@ MUTANTS = [
     ("nsa_decode_selected_before_window",
      "m_slc[int(j) * block: int(j) * block + block] = True",
      "m_slc[int(j) * block: min(int(j) * block + block, L - window)] = True"),
+    ("bwd_delta_dropped", "ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    ("bwd_dq_scale_dropped", "dQ[b, t, hs] = scale * np.matmul(ds, kb[: t + 1, g])",
+     "dQ[b, t, hs] = np.matmul(ds, kb[: t + 1, g])"),
+    ("bwd_dk_uses_dout", "dK[b, : t + 1, g] += scale * np.matmul(ds.T, qh)",
+     "dK[b, : t + 1, g] += scale * np.matmul(ds.T, do)"),
+    ("bwd_dv_transposed", "dV[b, : t + 1, g] += np.matmul(p.T, do)",
+     "dV[b, : t + 1, g] += np.matmul(p.T, qh)"),
     ("nsa_decode_window_without_self", "m_win[max(0, L - window): L] = True",
      "m_win[max(0, L - window): L - 1] = True"),
 ]

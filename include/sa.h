@@ -155,6 +155,28 @@ int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_
                        int dtype, void* out, float* lse, void* stream);
 
 /*
+ * Sparse attention backward.  [NSA] "Puntos Clave" (the backward pass of sparse attention,
+ * reported beside the forward).  For the forward of sa_sparse_attn_fwd on the same
+ * q, k, v, idx, window and scale, with its out and lse, and the upstream gradient dout:
+ *
+ *   P[t,h,s] = exp(scale q[t,h].k[s,g] - lse[h,t]) on S_t (0 elsewhere)
+ *   dS[t,h,s] = P (dout[t,h].v[s,g] - dout[t,h].out[t,h])
+ *   dq[t,h]   = scale sum_s dS[t,h,s] k[s,g]
+ *   dk[s,g]   = scale sum_{t, h in g} dS[t,h,s] q[t,h]
+ *   dv[s,g]   = sum_{t, h in g} P[t,h,s] dout[t,h]
+ *
+ * q, k, v, out, dout bf16 in the forward's layouts; idx as for the forward (NULL with
+ * topk = 0); lse [B, Hq, T] float32 from the forward (required).  dq [B, T, Hq, D],
+ * dk, dv [B, T, Hkv, D] float32: every entry is written (dk, dv are cleared by the call,
+ * then accumulated with float atomics, so their low bits depend on the order of the
+ * additions).  Requires bf16, D in {64, 128}, Hq/Hkv <= 16.
+ */
+int sa_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                       int T, int Hq, int Hkv, int D, int topk, int window, float scale,
+                       int dtype, const void* out, const float* lse, const void* dout, float* dq,
+                       float* dk, float* dv, void* stream);
+
+/*
  * Fixed-graph distance attention.  [SLM] "Cómo eligen los tokens a quién escuchar": a
  * fixed list of allowed positions (the token itself, its near predecessors and
  * positions at distances 1, 2, 4, 8, ...), never future ones; the weight grows as the

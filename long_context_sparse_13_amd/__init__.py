@@ -42,6 +42,10 @@ _SIGS = {
     "sa_sparse_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_void_p, _c_void_p, _c_void_p]),
+    "sa_sparse_attn_bwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_void_p]),
     "sa_graph_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float, _c_int,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p,
                                    _c_void_p, _c_void_p]),
@@ -430,3 +434,26 @@ def sa_nsa_decode_branch(q, keys, vals, lens, kind: int, block: int, window: int
                                     _p(lse), _stream(q.device))
     _check("sa_nsa_decode_branch", rc)
     return (out, lse) if want_lse else out
+
+
+def sa_sparse_attn_bwd(q, k, v, idx, window: int, scale: float, out, lse, dout, dq=None,
+                       dk=None, dv=None):
+    """Gradients of sa_sparse_attn_fwd: returns (dq [B,T,Hq,D], dk, dv [B,T,Hkv,D]) float32."""
+    torch = _torch()
+    _dev(q, "q"); _dev(k, "k", q.dtype); _dev(v, "v", q.dtype)
+    _dev(out, "out", q.dtype); _dev(dout, "dout", q.dtype); _dev(lse, "lse", torch.float32)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    topk = 0
+    if idx is not None:
+        _dev(idx, "idx", torch.int32)
+        topk = idx.shape[2]
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, T, Hq, D), **f32) if dq is None else dq
+    dk = torch.empty((B, T, Hkv, D), **f32) if dk is None else dk
+    dv = torch.empty((B, T, Hkv, D), **f32) if dv is None else dv
+    rc = lib().sa_sparse_attn_bwd(_p(q), _p(k), _p(v), _p(idx), B, T, Hq, Hkv, D, topk, window,
+                                  float(scale), _dtype_code(q), _p(out), _p(lse), _p(dout),
+                                  _p(dq), _p(dk), _p(dv), _stream(q.device))
+    _check("sa_sparse_attn_bwd", rc)
+    return dq, dk, dv

@@ -275,6 +275,40 @@ int sa_block_meanpool_bf16(const void* kcache, const int32_t* lens, int B, int L
   }
 }
 
+int sa_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                       int T, int Hq, int Hkv, int D, int topk, int window, float scale,
+                       int dtype, const void* out, const float* lse, const void* dout, float* dq,
+                       float* dk, float* dv, void* stream) {
+  try {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(lse);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+    REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
+    REQUIRE(topk >= 0 && window >= 0 && topk + window >= 1,
+            "need topk >= 0, window >= 0 and topk + window >= 1 (topk=%d window=%d)", topk, window);
+    REQUIRE(topk == 0 || idx != nullptr, "idx is NULL with topk=%d", topk);
+    REQUIRE(std::isfinite(scale), "scale must be finite");
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * T * Hq * D <= kMaxElems, "tensors too large");
+    SUPPORT(dtype == SA_BF16, "the backward takes bf16 tensors (dtype=%d)", dtype);
+    SUPPORT(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+    SUPPORT(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+    return hip_status(sa::launch_sparse_attn_bwd(q, k, v, idx, B, T, Hq, Hkv, D, topk, window,
+                                                 scale, out, lse, dout, dq, dk, dv,
+                                                 as_stream(stream)),
+                      "sa_sparse_attn_bwd launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_sparse_attn_bwd: unexpected exception");
+  }
+}
+
 // ---------------------------------------------------------------- NSA branches (prefill)
 static bool nsa_block_ok(int block) { return block == 16 || block == 32 || block == 64 || block == 128; }
 

@@ -37,6 +37,12 @@ hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, c
                                   int B, int T, int Hq, int Hkv, int D, int topk, int window,
                                   float scale, bool bf16, void* out, float* lse, hipStream_t st);
 
+hipError_t launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                                  int B, int T, int Hq, int Hkv, int D, int topk, int window,
+                                  float scale, const void* out, const float* lse,
+                                  const void* dout, float* dq, float* dk, float* dv,
+                                  hipStream_t st);
+
 hipError_t launch_graph_attn_fwd(const void* cq, const void* ck, const void* v, const float* bias,
                                  float tau, int B, int T, int H, int D, int local, int n_pow2,
                                  bool bf16, void* out, float* lse, hipStream_t st);

@@ -314,6 +314,29 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # ---- the backward of the 64K sparse attention (same q, k, v, indices; a seeded bf16
+    # upstream gradient), with the forward timed beside it
+    log("sparse attention backward (64K)")
+    p3 = sa_synth.WORKLOADS[3].params
+    o_f = torch.empty_like(q64)
+    t_fwd = timed(lambda: sa.sa_sparse_attn_fwd(q64, k64, v64, idx64, p3["window"], p3["scale"],
+                                                out=o_f), 2)
+    o_f, lse_f = sa.sa_sparse_attn_fwd(q64, k64, v64, idx64, p3["window"], p3["scale"],
+                                       return_lse=True)
+    g_out = torch.randn(q64.shape, generator=torch.Generator(device=dev).manual_seed(1006),
+                        device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dq_b = torch.empty(q64.shape, dtype=torch.float32, device=dev)
+    dk_b = torch.empty(k64.shape, dtype=torch.float32, device=dev)
+    dv_b = torch.empty(v64.shape, dtype=torch.float32, device=dev)
+    t_bwd = timed(lambda: sa.sa_sparse_attn_bwd(q64, k64, v64, idx64, p3["window"], p3["scale"],
+                                                o_f, lse_f, g_out, dq_b, dk_b, dv_b), 2)
+    rows["sparse_attn_bwd_64k"] = {
+        "ms": t_bwd, "forward_ms": t_fwd, "bwd_over_fwd": t_bwd / t_fwd,
+        "query_tokens_per_s": q64.shape[1] / (t_bwd * 1e-3),
+    }
+    del o_f, lse_f, g_out, dq_b, dk_b, dv_b
+    torch.cuda.empty_cache()
+
     # ---- the 64K fused index path with 8-bit (E4M3) indexer inputs: the same draws as the
     # bf16 step, encoded to E4M3; bf16 timed beside on the same sizes
     W3 = sa_synth.WORKLOADS[3]

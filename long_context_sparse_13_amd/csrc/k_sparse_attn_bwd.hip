@@ -11,10 +11,13 @@
 //   dP^T = V . dO^T       A = V rows, B = dO
 //   P = exp2(S * scale * log2 e - lse2),  dS = P (dP - delta),  delta = dO . O
 //   dQ^T += K^T . dS^T    A = K^T read transposed from LDS, B = dS^T (bf16)
-//   dV^T  = dO^T . P      16x16x16: A = dO^T (registers, once per wavefront), B = P
-//   dK^T  = Q^T . dS      transposed through LDS
+//   dV    = P^T . dO      16x16x16: A = P^T through LDS, B = dO (registers, once per
+//   dK    = dS^T . Q      wavefront); each atomic instruction covers 16 consecutive floats
+//                         of 4 rows
 // dK and dV rows are added with float atomics into float32 buffers that the launch clears
-// first (a key is selected by many queries); dQ is written once per (token, head).
+// first (a key is selected by many queries); dQ is written once per (token, head).  The
+// atomics bound the kernel: at 64K (139 M selected (query, key) pairs, 256 float adds
+// each) they take ~95% of its time.
 #include "attn_tile.h"
 #include "sa_launch.h"
 
@@ -193,27 +196,32 @@ __global__ __launch_bounds__(64) void sparse_attn_bwd_mfma(
                                                         as_bf16x8(dsw), acc[dt], 0, 0, 0);
     }
 
-    // ---- dV^T[d, key] = dO^T . P and dK^T[d, key] = scale Q^T . dS; B = [head][key] from
-    // LDS (lane: key c2*16 + n, heads grp*4 .. +3); C: d = dt*16 + grp*4 + i, key c2*16 + n
+    // ---- dV[key, d] = P^T . dO and dK[key, d] = scale dS^T . Q on the 16x16x16 MFMA:
+    // A = [key][head] from LDS (lane: key c2*16 + n, heads grp*4 .. +3), B = the dO / Q
+    // registers (heads grp*4 + j, d = dt*16 + n); C: keys c2*16 + grp*4 + i, d = dt*16 + n,
+    // so each atomic instruction covers 16 consecutive floats of 4 rows
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
-      const int sk = c2 * 16 + n;
-      const s16x4 bP = *reinterpret_cast<const s16x4*>(&pl[sk][grp * 4]);
-      const s16x4 bS = *reinterpret_cast<const s16x4*>(&sl[sk][grp * 4]);
-      const bool okr = (vm >> sk) & 1u;
-      const int kr = shfl_i(key, sk);
-      float* dvr = dvbase + (int64_t)kr * stride;
-      float* dkr = dkbase + (int64_t)kr * stride;
+      const s16x4 aP = *reinterpret_cast<const s16x4*>(&pl[c2 * 16 + n][grp * 4]);
+      const s16x4 aS = *reinterpret_cast<const s16x4*>(&sl[c2 * 16 + n][grp * 4]);
+      int kr[4];
+      bool okr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sk = c2 * 16 + grp * 4 + i;
+        kr[i] = shfl_i(key, sk);
+        okr[i] = (vm >> sk) & 1u;
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 cv = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aDO[dt], bP, z, 0, 0, 0);
-        const f32x4 ck = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aQ[dt], bS, z, 0, 0, 0);
-        if (okr) {
+        const f32x4 cv = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aP, aDO[dt], z, 0, 0, 0);
+        const f32x4 ck = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aS, aQ[dt], z, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            atomicAdd(dvr + dt * 16 + grp * 4 + i, cv[i]);
-            atomicAdd(dkr + dt * 16 + grp * 4 + i, ck[i] * scale);
+        for (int i = 0; i < 4; ++i) {
+          if (okr[i]) {
+            atomicAdd(dvbase + (int64_t)kr[i] * stride + dt * 16 + n, cv[i]);
+            atomicAdd(dkbase + (int64_t)kr[i] * stride + dt * 16 + n, ck[i] * scale);
           }
         }
       }

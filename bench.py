@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip graph/decode/reuse rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--bwd-rows", type=int, default=16384,
+                    help="query rows per chunk of the backward's partial-row workspace")
     ap.add_argument("--only", choices=["attn", "prefill"], default=None,
                     help="time only one part (for profiling runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
@@ -328,13 +330,32 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
     dq_b = torch.empty(q64.shape, dtype=torch.float32, device=dev)
     dk_b = torch.empty(k64.shape, dtype=torch.float32, device=dev)
     dv_b = torch.empty(v64.shape, dtype=torch.float32, device=dev)
+    B3, T3b, Hkv3, D3 = k64.shape[0], k64.shape[1], k64.shape[2], k64.shape[3]
+    topk3b = idx64.shape[2]
+    ws_n = sa.sa_sparse_attn_bwd_workspace(B3, T3b, Hkv3, D3, topk3b, p3["window"], args.bwd_rows)
+    ws_b = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     t_bwd = timed(lambda: sa.sa_sparse_attn_bwd(q64, k64, v64, idx64, p3["window"], p3["scale"],
-                                                o_f, lse_f, g_out, dq_b, dk_b, dv_b), 2)
+                                                o_f, lse_f, g_out, dq_b, dk_b, dv_b,
+                                                workspace=ws_b), 3)
+    dk_w, dv_w = dk_b.clone(), dv_b.clone()
+    t_atom = timed(lambda: sa.sa_sparse_attn_bwd(q64, k64, v64, idx64, p3["window"], p3["scale"],
+                                                 o_f, lse_f, g_out, dq_b, dk_b, dv_b), 1)
+    # the two ways of summing dK / dV agree (the workspace path rounds each pair's
+    # contribution to bf16)
+    agree = max(float((a - b).abs().max() / b.abs().max()) for a, b in ((dk_w, dk_b), (dv_w, dv_b)))
+    tt = torch.arange(T3b, device=dev, dtype=torch.int32)[:, None]
+    pairs = int((((idx64[0] >= 0) & (idx64[0] <= tt - p3["window"])).sum(dtype=torch.int64)
+                 + torch.clamp(torch.arange(T3b, device=dev) + 1, max=p3["window"]).sum()).item())
+    part_bytes = pairs * 4 * D3 * 2  # each pair's bf16 [dK | dV] row written once, read once
     rows["sparse_attn_bwd_64k"] = {
         "ms": t_bwd, "forward_ms": t_fwd, "bwd_over_fwd": t_bwd / t_fwd,
         "query_tokens_per_s": q64.shape[1] / (t_bwd * 1e-3),
+        "path": f"partial rows, workspace {ws_n / 2**30:.1f} GiB (chunks of {args.bwd_rows} rows)",
+        "atomic_path_ms": t_atom, "max_rel_diff_vs_atomic": agree,
+        "pairs": pairs, "partial_row_bytes": part_bytes,
+        "atomic_float_adds": pairs * 2 * D3,
     }
-    del o_f, lse_f, g_out, dq_b, dk_b, dv_b
+    del o_f, lse_f, g_out, dq_b, dk_b, dv_b, ws_b, dk_w, dv_w
     torch.cuda.empty_cache()
 
     # ---- the 64K fused index path with 8-bit (E4M3) indexer inputs: the same draws as the

@@ -166,15 +166,27 @@ int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_
  *   dv[s,g]   = sum_{t, h in g} P[t,h,s] dout[t,h]
  *
  * q, k, v, out, dout bf16 in the forward's layouts; idx as for the forward (NULL with
- * topk = 0); lse [B, Hq, T] float32 from the forward (required).  dq [B, T, Hq, D],
- * dk, dv [B, T, Hkv, D] float32: every entry is written (dk, dv are cleared by the call,
- * then accumulated with float atomics, so their low bits depend on the order of the
- * additions).  Requires bf16, D in {64, 128}, Hq/Hkv <= 16.
+ * topk = 0), in any order; lse [B, Hq, T] float32 from the forward (required).
+ * dq [B, T, Hq, D], dk, dv [B, T, Hkv, D] float32: every entry is written.
+ *
+ * workspace NULL: dk and dv are cleared, then accumulated with float atomics (one per
+ * (query, key, feature)); no extra memory, but the atomics bound the call.
+ * workspace non-NULL (ws_bytes of device memory, any contents, 16-byte aligned): each
+ * (query, key) pair's dK and dV contributions are written as a bf16 row into the
+ * workspace, then summed per key in float32 (the query rows go in chunks of as many rows
+ * as the workspace holds; sa_sparse_attn_bwd_workspace gives the size for a chunk of
+ * `rows` rows, rows <= 0 meaning all T: about B*Hkv*rows*(topk+window)*4*D bytes).  The
+ * contributions are rounded to bf16 before the sum (2^-9 relative each).  Needs T <= 2^20
+ * and B*T*(topk+window) < 2^31; a workspace too small for one row gives SA_ERR_WORKSPACE.
+ * Both ways add in an order that varies from run to run, so the low bits of dk and dv do.
+ * Requires bf16, D in {64, 128}, Hq/Hkv <= 16.
  */
 int sa_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
                        int T, int Hq, int Hkv, int D, int topk, int window, float scale,
                        int dtype, const void* out, const float* lse, const void* dout, float* dq,
-                       float* dk, float* dv, void* stream);
+                       float* dk, float* dv, void* workspace, size_t ws_bytes, void* stream);
+size_t sa_sparse_attn_bwd_workspace(int B, int T, int Hkv, int D, int topk, int window,
+                                    int rows);
 
 /*
  * Fixed-graph distance attention.  [SLM] "Cómo eligen los tokens a quién escuchar": a

@@ -45,7 +45,8 @@ _SIGS = {
     "sa_sparse_attn_bwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                    _c_void_p, _c_void_p]),
+                                    _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "sa_sparse_attn_bwd_workspace": (_c_size_t, [_c_int] * 7),
     "sa_graph_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float, _c_int,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p,
                                    _c_void_p, _c_void_p]),
@@ -436,9 +437,17 @@ def sa_nsa_decode_branch(q, keys, vals, lens, kind: int, block: int, window: int
     return (out, lse) if want_lse else out
 
 
+def sa_sparse_attn_bwd_workspace(B, T, Hkv, D, topk, window, rows=0) -> int:
+    """Bytes of workspace for the partial-row backward over chunks of `rows` query rows
+    (0: all T); 0 when the shapes are outside that path."""
+    return int(lib().sa_sparse_attn_bwd_workspace(B, T, Hkv, D, topk, window, rows))
+
+
 def sa_sparse_attn_bwd(q, k, v, idx, window: int, scale: float, out, lse, dout, dq=None,
-                       dk=None, dv=None):
-    """Gradients of sa_sparse_attn_fwd: returns (dq [B,T,Hq,D], dk, dv [B,T,Hkv,D]) float32."""
+                       dk=None, dv=None, workspace=None):
+    """Gradients of sa_sparse_attn_fwd: returns (dq [B,T,Hq,D], dk, dv [B,T,Hkv,D]) float32.
+    workspace: None (float atomics) or a device uint8 tensor (partial rows summed per key;
+    its size sets the chunk of query rows, see sa_sparse_attn_bwd_workspace)."""
     torch = _torch()
     _dev(q, "q"); _dev(k, "k", q.dtype); _dev(v, "v", q.dtype)
     _dev(out, "out", q.dtype); _dev(dout, "dout", q.dtype); _dev(lse, "lse", torch.float32)
@@ -452,8 +461,13 @@ def sa_sparse_attn_bwd(q, k, v, idx, window: int, scale: float, out, lse, dout, 
     dq = torch.empty((B, T, Hq, D), **f32) if dq is None else dq
     dk = torch.empty((B, T, Hkv, D), **f32) if dk is None else dk
     dv = torch.empty((B, T, Hkv, D), **f32) if dv is None else dv
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().sa_sparse_attn_bwd(_p(q), _p(k), _p(v), _p(idx), B, T, Hq, Hkv, D, topk, window,
                                   float(scale), _dtype_code(q), _p(out), _p(lse), _p(dout),
-                                  _p(dq), _p(dk), _p(dv), _stream(q.device))
+                                  _p(dq), _p(dk), _p(dv), _p(workspace), ws_bytes,
+                                  _stream(q.device))
     _check("sa_sparse_attn_bwd", rc)
     return dq, dk, dv

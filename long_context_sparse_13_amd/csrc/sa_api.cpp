@@ -278,7 +278,7 @@ int sa_block_meanpool_bf16(const void* kcache, const int32_t* lens, int B, int L
 int sa_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
                        int T, int Hq, int Hkv, int D, int topk, int window, float scale,
                        int dtype, const void* out, const float* lse, const void* dout, float* dq,
-                       float* dk, float* dv, void* stream) {
+                       float* dk, float* dv, void* workspace, size_t ws_bytes, void* stream) {
   try {
     REQUIRE_PTR(q);
     REQUIRE_PTR(k);
@@ -300,13 +300,31 @@ int sa_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_
     SUPPORT(dtype == SA_BF16, "the backward takes bf16 tensors (dtype=%d)", dtype);
     SUPPORT(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
     SUPPORT(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+    if (workspace) {
+      SUPPORT(sa::sparse_attn_bwd_partial_ok(B, T, topk, window),
+              "the workspace path needs T <= 2^20 and B*T*(topk+window) < 2^31");
+      REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+      const int C = sa::sparse_attn_bwd_chunk_rows(B, T, Hkv, D, topk, window, ws_bytes);
+      if (C < 1)
+        return fail(SA_ERR_WORKSPACE,
+                    "sa_sparse_attn_bwd: workspace of at least %zu bytes needed (got %zu)",
+                    sa::sparse_attn_bwd_workspace_bytes(B, T, Hkv, D, topk, window, 1), ws_bytes);
+    }
     return hip_status(sa::launch_sparse_attn_bwd(q, k, v, idx, B, T, Hq, Hkv, D, topk, window,
-                                                 scale, out, lse, dout, dq, dk, dv,
-                                                 as_stream(stream)),
+                                                 scale, out, lse, dout, dq, dk, dv, workspace,
+                                                 ws_bytes, as_stream(stream)),
                       "sa_sparse_attn_bwd launch");
   } catch (...) {
     return fail(SA_ERR_INTERNAL, "sa_sparse_attn_bwd: unexpected exception");
   }
+}
+
+size_t sa_sparse_attn_bwd_workspace(int B, int T, int Hkv, int D, int topk, int window,
+                                    int rows) {
+  if (B < 1 || T < 1 || Hkv < 1 || (D != 64 && D != 128) || topk < 0 || window < 0 ||
+      topk + window < 1 || !sa::sparse_attn_bwd_partial_ok(B, T, topk, window))
+    return 0;
+  return sa::sparse_attn_bwd_workspace_bytes(B, T, Hkv, D, topk, window, rows);
 }
 
 // ---------------------------------------------------------------- NSA branches (prefill)

@@ -41,7 +41,14 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* k, const void* v, c
                                   int B, int T, int Hq, int Hkv, int D, int topk, int window,
                                   float scale, const void* out, const float* lse,
                                   const void* dout, float* dq, float* dk, float* dv,
-                                  hipStream_t st);
+                                  void* workspace, size_t ws_bytes, hipStream_t st);
+// The workspace path: its size for chunks of `rows` query rows (rows <= 0: all T), the
+// chunk that a workspace of ws_bytes holds (0 if none), and the shapes it handles.
+size_t sparse_attn_bwd_workspace_bytes(int B, int T, int Hkv, int D, int topk, int window,
+                                       int rows);
+int sparse_attn_bwd_chunk_rows(int B, int T, int Hkv, int D, int topk, int window,
+                               size_t ws_bytes);
+bool sparse_attn_bwd_partial_ok(int B, int T, int topk, int window);
 
 hipError_t launch_graph_attn_fwd(const void* cq, const void* ck, const void* v, const float* bias,
                                  float tau, int B, int T, int H, int D, int local, int n_pow2,

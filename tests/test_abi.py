@@ -189,3 +189,25 @@ def test_nsa_validation(L):
     mb = L.sa_block_meanpool_bf16
     assert mb(P, P, 1, 1024, 1, 128, 48, 1, P, None) == 1                              # block
     assert mb(P, P, 1, 1024, 1, 128, 64, 2, P, None) == 2                              # E4M3
+
+
+def test_bwd_validation_and_workspace(L):
+    # every call fails validation before any launch
+    q = L.sa_sparse_attn_bwd_workspace
+    w1, w2, wall = q(1, 4096, 1, 128, 64, 16, 1), q(1, 4096, 1, 128, 64, 16, 2), q(1, 4096, 1, 128, 64, 16, 0)
+    assert 0 < w1 < w2 < wall and q(1, 4096, 1, 128, 64, 16, 4096) == wall
+    assert w2 - w1 >= 80 * 4 * 128                      # one row: (topk + window) bf16 rows of 4*D bytes
+    assert q(1, 4096, 1, 96, 64, 16, 0) == 0            # D
+    assert q(1, 4096, 1, 128, 0, 0, 0) == 0             # empty selection
+    assert q(1, (1 << 20) + 1, 1, 128, 64, 16, 1) == 0  # beyond the bucket histogram
+    b = L.sa_sparse_attn_bwd
+    args = lambda T=4096, Hq=16, D=128, dt=1, lse=P, ws=None, n=0: (
+        P, P, P, P, 1, T, Hq, 1, D, 64, 16, 0.1, dt, P, lse, P, P, P, P, ws, n, None)
+    assert b(*args(dt=0)) == 2                          # f32
+    assert b(*args(D=96)) == 2
+    assert b(*args(Hq=32)) == 2                         # 32 heads per group
+    assert b(*args(lse=None)) == 1
+    assert b(*args(ws=P, n=w1 - 1)) == 3                # smaller than one row
+    assert "workspace" in _err(L)
+    assert b(*args(ws=MIS, n=wall)) == 1                # alignment
+    assert b(*args(T=(1 << 20) + 1, Hq=1, D=64, ws=P, n=1 << 40)) == 2

@@ -1,10 +1,14 @@
 """Sparse-attention backward on the GPU (sa_sparse_attn_bwd) against the float64 oracle
 (oracle.reference.sparse_attn_bwd) on the same bf16 inputs and bf16 upstream gradient.
 
+Both ways of forming dk and dv are covered: float atomics (no workspace) and the partial
+rows summed per key (a workspace, for all rows at once or for chunks of query rows).
+
 Tolerance: the kernel rounds P and dS to bf16 for the products that build dq, dk and dv
-(relative 2^-9 per term) and uses the forward's bf16-rounded output in dout . out, with
-float32 accumulation; each gradient tensor is held to max |err| <= 1e-2 * max |grad| of
-that tensor (a bf16-level relative error on the largest entries)."""
+(relative 2^-9 per term), and the workspace path also rounds each pair's dk / dv
+contribution to bf16 before the float32 sum; it uses the forward's bf16-rounded output in
+dout . out.  Each gradient tensor is held to max |err| <= 1e-2 * max |grad| of that tensor
+(a bf16-level relative error on the largest entries)."""
 
 import numpy as np
 import pytest
@@ -19,14 +23,29 @@ pytestmark = pytest.mark.gpu
 REL = 1e-2
 
 
-def _run(x, idx, window, scale, seed):
+def _workspace(B, T, Hkv, D, topk, window, mode):
+    """None (atomics), or a workspace holding all rows ("ws") or chunks of T // 3 rows
+    ("chunked", so the last chunk is ragged), filled with junk bytes."""
+    import torch
+    if mode == "atomic":
+        return None
+    rows = 0 if mode == "ws" else max(1, T // 3)
+    n = sa.sa_sparse_attn_bwd_workspace(B, T, Hkv, D, topk, window, rows)
+    assert n > 0
+    return torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+
+
+def _run(x, idx, window, scale, seed, mode="atomic"):
     import torch
     B, T, Hq, D = x["q"].shape
     dout = sa_synth.round_bf16(sa_synth.rng(seed).standard_normal((B, T, Hq, D), dtype=np.float32))
     q, k, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
     idx_d = dev(idx, "i32") if idx is not None else None
     out, lse = sa.sa_sparse_attn_fwd(q, k, v, idx_d, window, scale, return_lse=True)
-    dq, dk, dv = sa.sa_sparse_attn_bwd(q, k, v, idx_d, window, scale, out, lse, dev(dout, "bf16"))
+    topk = idx.shape[2] if idx is not None else 0
+    ws = _workspace(B, T, k.shape[2], D, topk, window, mode)
+    dq, dk, dv = sa.sa_sparse_attn_bwd(q, k, v, idx_d, window, scale, out, lse, dev(dout, "bf16"),
+                                       workspace=ws)
     idx_o = idx if idx is not None else np.full((B, T, 1), -1, dtype=np.int32)
     want = orc.sparse_attn_bwd(x["q"], x["k"], x["v"], idx_o, window, scale, dout)
     for name, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
@@ -36,19 +55,72 @@ def _run(x, idx, window, scale, seed):
         assert err <= REL * max(top, 1e-6), (name, err, top)
 
 
+MODES = ["atomic", "ws", "chunked"]
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("B,T,Hq,Hkv,D,k,W", [(2, 300, 4, 2, 64, 32, 16), (1, 700, 16, 1, 128, 64, 32),
                                               (1, 400, 8, 1, 128, 40, 0)])
-def test_bwd_vs_oracle(B, T, Hq, Hkv, D, k, W):
+def test_bwd_vs_oracle(B, T, Hq, Hkv, D, k, W, mode):
     x = sa_synth.attn_inputs(901 + T, B, T, Hq, Hkv, D, "bf16")
     idx = sa_synth.random_topk_idx(902 + T, B, T, k, junk=True)
-    note(f"sparse_attn_bwd B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} k={k} W={W}")
-    _run(x, idx, W, D ** -0.5, 903 + T)
+    note(f"sparse_attn_bwd B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} k={k} W={W} {mode}")
+    _run(x, idx, W, D ** -0.5, 903 + T, mode)
 
 
-def test_bwd_window_only():
+@pytest.mark.parametrize("mode", MODES)
+def test_bwd_window_only(mode):
     x = sa_synth.attn_inputs(911, 1, 500, 16, 1, 128, "bf16")
-    note("sparse_attn_bwd window only T=500 W=128")
-    _run(x, None, 128, 128 ** -0.5, 912)
+    note(f"sparse_attn_bwd window only T=500 W=128 {mode}")
+    _run(x, None, 128, 128 ** -0.5, 912, mode)
+
+
+@pytest.mark.parametrize("mode", ["ws", "chunked"])
+def test_bwd_unsorted_lists(mode):
+    # the index lists in a shuffled order (keys spread over many 64-key buckets, several
+    # chunks); the result does not depend on the order
+    B, T, k, W = 1, 900, 96, 24
+    x = sa_synth.attn_inputs(931, B, T, 8, 1, 128, "bf16")
+    idx = sa_synth.random_topk_idx(932, B, T, k, junk=True)
+    g = sa_synth.rng(933)
+    for t in range(T):
+        idx[0, t] = idx[0, t, g.permutation(k)]
+    note(f"sparse_attn_bwd shuffled lists T={T} k={k} W={W} {mode}")
+    _run(x, idx, W, 128 ** -0.5, 934, mode)
+
+
+def test_bwd_workspace_one_row_chunks():
+    # a workspace for a single query row: one chunk per row, 5 launches each
+    import torch
+    B, T, Hq, Hkv, D, k, W = 1, 96, 4, 1, 64, 16, 8
+    x = sa_synth.attn_inputs(941, B, T, Hq, Hkv, D, "bf16")
+    idx = sa_synth.random_topk_idx(942, B, T, k, junk=True)
+    n1 = sa.sa_sparse_attn_bwd_workspace(B, T, Hkv, D, k, W, 1)
+    n2 = sa.sa_sparse_attn_bwd_workspace(B, T, Hkv, D, k, W, 2)
+    assert 0 < n1 < n2
+    dout = sa_synth.round_bf16(sa_synth.rng(943).standard_normal((B, T, Hq, D), dtype=np.float32))
+    q, kk, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+    idx_d = dev(idx, "i32")
+    out, lse = sa.sa_sparse_attn_fwd(q, kk, v, idx_d, W, 0.125, return_lse=True)
+    ws = torch.zeros(n1, dtype=torch.uint8, device="cuda")
+    note("sparse_attn_bwd one-row chunks T=96")
+    got = sa.sa_sparse_attn_bwd(q, kk, v, idx_d, W, 0.125, out, lse, dev(dout, "bf16"), workspace=ws)
+    want = orc.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, W, 0.125, dout)
+    for g, w in zip(got, want):
+        assert np.abs(host(g) - w).max() <= REL * np.abs(w).max()
+
+
+def test_bwd_workspace_too_small_is_an_error():
+    import torch
+    B, T, Hq, Hkv, D, k, W = 1, 64, 4, 1, 64, 16, 8
+    x = sa_synth.attn_inputs(951, B, T, Hq, Hkv, D, "bf16")
+    q, kk, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+    idx_d = dev(sa_synth.random_topk_idx(952, B, T, k), "i32")
+    out, lse = sa.sa_sparse_attn_fwd(q, kk, v, idx_d, W, 0.125, return_lse=True)
+    n1 = sa.sa_sparse_attn_bwd_workspace(B, T, Hkv, D, k, W, 1)
+    ws = torch.zeros(n1 - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sa.SAError, match="workspace"):
+        sa.sa_sparse_attn_bwd(q, kk, v, idx_d, W, 0.125, out, lse, q, workspace=ws)
 
 
 def test_bwd_listed_keys_inside_window_count_once():
@@ -58,5 +130,6 @@ def test_bwd_listed_keys_inside_window_count_once():
     idx = np.full((1, T, k), -1, dtype=np.int32)
     for t in range(T):
         idx[0, t, : min(k, t + 1)] = np.arange(t, max(-1, t - k), -1)[: min(k, t + 1)][::-1]
-    note("sparse_attn_bwd listed keys inside the window")
-    _run(x, idx, W, 0.125, 922)
+    for mode in MODES:
+        note(f"sparse_attn_bwd listed keys inside the window {mode}")
+        _run(x, idx, W, 0.125, 922, mode)

@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip graph/decode/reuse rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--bwd-rows", type=int, default=16384,
+    ap.add_argument("--bwd-rows", type=int, default=32768,
                     help="query rows per chunk of the backward's partial-row workspace")
     ap.add_argument("--only", choices=["attn", "prefill"], default=None,
                     help="time only one part (for profiling runs)")

@@ -68,6 +68,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
   __shared__ __attribute__((aligned(16))) unsigned char kl[32 * LROW];
   __shared__ __attribute__((aligned(16))) uint16_t pl[32][16];  // P as [key][head] (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t sl[32][16];  // dS as [key][head]
+  // the S / dP B operands (Q and dO rows of the group's heads), parked in LDS between
+  // tiles so that the registers hold the next tile's K and V rows instead; each lane
+  // reads back only what it wrote
+  __shared__ __attribute__((aligned(16))) unsigned char qsl[16 * LROW];
+  __shared__ __attribute__((aligned(16))) unsigned char dsl[16 * LROW];
 
   const int lane = threadIdx.x;
   const int n = lane & 15, grp = lane >> 4;
@@ -84,7 +89,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 
   // ---- per (token, head): Q and dO as B operands; delta = dO . O; the log2-domain lse
   const int64_t hrow = ((int64_t)b * T + t) * Hq + h;
-  bf16x8 qB[KS], dB[KS];
   float delta = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -94,8 +98,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
       wd = ld16(dout + hrow * D + ks * 32 + grp * 8);
       wo = ld16(o + hrow * D + ks * 32 + grp * 8);
     }
-    qB[ks] = as_bf16x8(wq);
-    dB[ks] = as_bf16x8(wd);
+    st16(qsl + n * LROW + (ks * 32 + grp * 8) * 2, wq);
+    st16(dsl + n * LROW + (ks * 32 + grp * 8) * 2, wd);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       delta += bf16_lo(wd[c]) * bf16_lo(wo[c]) + bf16_hi(wd[c]) * bf16_hi(wo[c]);
@@ -162,30 +166,51 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
   const int last_listed = t - window;
   const int wlo = t - window + 1;
 
-  for (int tile = 0; tile < n_idx + n_win; ++tile) {
-    // the tile's keys, as in the forward: listed positions outside [0, t - window] and
-    // window positions outside [0, t] are masked out, so each key counts once
-    int raw;
-    bool ok;
-    if (tile < n_idx) {
-      const int e = tile * 32 + slot;
-      raw = e < topk ? irow[e] : -1;
-      ok = raw >= 0 && raw <= last_listed;
-    } else {
-      raw = wlo + (tile - n_idx) * 32 + slot;
-      ok = raw >= 0 && raw <= t;
+  // The tiles' keys, as in the forward: listed positions outside [0, t - window] and window
+  // positions outside [0, t] are masked out, so each key counts once; tiles with no key
+  // are skipped.  next_tile() advances a cursor to the next non-empty tile (the listed
+  // positions one tile ahead are always in flight), and its K and V rows are requested
+  // while the current tile is still being worked on.
+  auto listed = [&](int tile) {
+    const int e = tile * 32 + slot;
+    return (tile < n_idx && e < topk) ? irow[e] : -1;
+  };
+  const int ntiles = n_idx + n_win;
+  int cursor = 0;
+  int raw_next = listed(0);
+  auto next_tile = [&](int& tile_out, uint32_t& vm_out, int& key_out) {
+    while (cursor < ntiles) {
+      const int tile = cursor++;
+      int raw;
+      bool ok;
+      if (tile < n_idx) {
+        raw = raw_next;
+        raw_next = listed(tile + 1);
+        ok = raw >= 0 && raw <= last_listed;
+      } else {
+        raw = wlo + (tile - n_idx) * 32 + slot;
+        ok = raw >= 0 && raw <= t;
+      }
+      const uint32_t vm_ = (uint32_t)ballot(ok);
+      if (vm_ != 0u) {
+        tile_out = tile;
+        vm_out = vm_;
+        key_out = ok ? raw : 0;
+        return;
+      }
     }
-    const uint32_t vm = (uint32_t)ballot(ok);
-    if (vm == 0u) continue;
-    const int key = ok ? raw : 0;
-
-    // K and V rows of the tile's two 16-key halves as A operands
-    u32x4 kA[2][KS], vA[2][KS];
+    tile_out = ntiles;
+    vm_out = 0u;
+    key_out = 0;
+  };
+  // K and V rows of a tile's two 16-key halves as A operands
+  u32x4 kA[2][KS], vA[2][KS];
+  auto fetch_kv = [&](uint32_t vm_, int key_) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int sl_ = c2 * 16 + n;
-      const int kr = shfl_i(key, sl_);
-      const bool okr = (vm >> sl_) & 1u;
+      const int kr = shfl_i(key_, sl_);
+      const bool okr = (vm_ >> sl_) & 1u;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 wk = {0u, 0u, 0u, 0u}, wv = wk;
@@ -197,6 +222,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
         vA[c2][ks] = wv;
       }
     }
+  };
+
+  int tile, key;
+  uint32_t vm;
+  next_tile(tile, vm, key);
+  if (tile < ntiles) fetch_kv(vm, key);
+  while (tile < ntiles) {
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
@@ -204,14 +236,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
       dp[c2] = s[c2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kA[c2][ks]), qB[ks], s[c2], 0, 0, 0);
-        dp[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vA[c2][ks]), dB[ks], dp[c2], 0, 0, 0);
+        const bf16x8 qB = as_bf16x8(ld16(qsl + n * LROW + (ks * 32 + grp * 8) * 2));
+        const bf16x8 dB = as_bf16x8(ld16(dsl + n * LROW + (ks * 32 + grp * 8) * 2));
+        s[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kA[c2][ks]), qB, s[c2], 0, 0, 0);
+        dp[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vA[c2][ks]), dB, dp[c2], 0, 0, 0);
       }
       // stage the K rows (key c2*16 + n, features ks*32 + grp*8) for the K^T reads
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         st16(kl + (c2 * 16 + n) * LROW + (ks * 32 + grp * 8) * 2, kA[c2][ks]);
     }
+
+    // the next non-empty tile; its K and V rows are in flight from here on
+    int tile_n, key_n;
+    uint32_t vm_n;
+    next_tile(tile_n, vm_n, key_n);
+    if (tile_n < ntiles) fetch_kv(vm_n, key_n);
 
     // P and dS: lane (n, grp) holds keys c2*16 + grp*4 + i of head n
     float pv[8], dsv[8];
@@ -260,33 +300,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
       const s16x4 aP = *reinterpret_cast<const s16x4*>(&pl[c2 * 16 + n][grp * 4]);
       const s16x4 aS = *reinterpret_cast<const s16x4*>(&sl[c2 * 16 + n][grp * 4]);
       if constexpr (PART) {
-        f32x4 cv[DT], ck[DT];
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        // dV rows (bf16, d = n*DT .. +DT-1 per lane) at +D, then dK rows at +0
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          cv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aP, aDO[dt], z, 0, 0, 0);
-          ck[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aS, aQ[dt], z, 0, 0, 0);
-        }
+        for (int part_k = 0; part_k < 2; ++part_k) {
+          f32x4 c[DT];
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sk = c2 * 16 + grp * 4 + i;
-          if ((vm >> sk) & 1u) {
-            uint16_t* pr = prow + (int64_t)(slot_base + sk) * (2 * D) + n * DT;
-            if constexpr (DT == 8) {
-              const u32x4 wk = {pack_bf16x2(ck[0][i] * scale, ck[1][i] * scale),
-                                pack_bf16x2(ck[2][i] * scale, ck[3][i] * scale),
-                                pack_bf16x2(ck[4][i] * scale, ck[5][i] * scale),
-                                pack_bf16x2(ck[6][i] * scale, ck[7][i] * scale)};
-              const u32x4 wv = {pack_bf16x2(cv[0][i], cv[1][i]), pack_bf16x2(cv[2][i], cv[3][i]),
-                                pack_bf16x2(cv[4][i], cv[5][i]), pack_bf16x2(cv[6][i], cv[7][i])};
-              __builtin_nontemporal_store(wk, reinterpret_cast<u32x4*>(pr));
-              __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(pr + D));
-            } else {
-              const u32x2 wk = {pack_bf16x2(ck[0][i] * scale, ck[1][i] * scale),
-                                pack_bf16x2(ck[2][i] * scale, ck[3][i] * scale)};
-              const u32x2 wv = {pack_bf16x2(cv[0][i], cv[1][i]), pack_bf16x2(cv[2][i], cv[3][i])};
-              __builtin_nontemporal_store(wk, reinterpret_cast<u32x2*>(pr));
-              __builtin_nontemporal_store(wv, reinterpret_cast<u32x2*>(pr + D));
+          for (int dt = 0; dt < DT; ++dt)
+            c[dt] = part_k ? __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aS, aQ[dt], z, 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aP, aDO[dt], z, 0, 0, 0);
+          const float m = part_k ? scale : 1.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int sk = c2 * 16 + grp * 4 + i;
+            if ((vm >> sk) & 1u) {
+              uint16_t* pr = prow + (int64_t)(slot_base + sk) * (2 * D) + (part_k ? 0 : D) + n * DT;
+              if constexpr (DT == 8) {
+                const u32x4 wv = {pack_bf16x2(c[0][i] * m, c[1][i] * m), pack_bf16x2(c[2][i] * m, c[3][i] * m),
+                                  pack_bf16x2(c[4][i] * m, c[5][i] * m), pack_bf16x2(c[6][i] * m, c[7][i] * m)};
+                __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(pr));
+              } else {
+                const u32x2 wv = {pack_bf16x2(c[0][i] * m, c[1][i] * m), pack_bf16x2(c[2][i] * m, c[3][i] * m)};
+                __builtin_nontemporal_store(wv, reinterpret_cast<u32x2*>(pr));
+              }
             }
           }
         }
@@ -315,6 +351,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
       }
     }
     wave_lds_sync();  // the staging areas are rewritten by the next tile
+    tile = tile_n;
+    vm = vm_n;
+    key = key_n;
   }
 
   if (hv) {

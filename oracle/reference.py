@@ -253,6 +253,64 @@ def sparse_attn_bwd(q, k, v, idx, window: int, scale: float, dout):
     return dQ, dK, dV
 
 
+def _row_grads(q, k, v, idx, window: int, scale: float, dout, b: int, t: int, g: int, G: int):
+    """The per-row pieces of ``sparse_attn_bwd`` for (b, t, KV group g), over the keys of
+    S_t only: (keys [n], P [G, n], dS [G, n]); the softmax over S_t is the same as the
+    masked dense one since every other key has P = 0."""
+    keys = np.nonzero(selected_mask_row(t, idx[b, t], window))[0]
+    hs = slice(g * G, (g + 1) * G)
+    qh, do = _f64(q[b, t, hs]), _f64(dout[b, t, hs])
+    logits = scale * np.matmul(qh, _f64(k[b, keys, g]).T)                  # [G, n]
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    dp = np.matmul(do, _f64(v[b, keys, g]).T)
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return keys, p, ds
+
+
+def sparse_attn_bwd_rows(q, k, v, idx, window: int, scale: float, dout, rows):
+    """dQ of ``sparse_attn_bwd`` for the requested rows only: [B, R, Hq, D] float64
+    (dQ[t,h] = scale Σ_{s∈S_t} dS[t,h,s] k[s,g]); for sampled checks at sizes where the
+    full gradient is out of reach."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    rows = list(rows)
+    dQ = np.zeros((B, len(rows), Hq, D))
+    for b in range(B):
+        for r, t in enumerate(rows):
+            for g in range(Hkv):
+                keys, p, ds = _row_grads(q, k, v, idx, window, scale, dout, b, t, g, G)
+                if keys.size:
+                    dQ[b, r, g * G:(g + 1) * G] = scale * np.matmul(ds, _f64(k[b, keys, g]))
+    return dQ
+
+
+def sparse_attn_bwd_keys(q, k, v, idx, window: int, scale: float, dout, b: int, keys):
+    """dK and dV of ``sparse_attn_bwd`` for the requested key positions of sequence b:
+    ([R, Hkv, D], [R, Hkv, D]) float64, each summed over every row t whose S_t holds the
+    key (the window rows t in [s, s + window) and the rows that list s with s <= t - window,
+    each row once)."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    keys = list(keys)
+    dK = np.zeros((len(keys), Hkv, D))
+    dV = np.zeros((len(keys), Hkv, D))
+    tt = np.arange(T)[:, None]
+    for r, s in enumerate(keys):
+        listed = np.nonzero(((idx[b] == s) & (s <= tt - window)).any(axis=1))[0]
+        win = np.arange(s, min(T, s + window))
+        for t in np.union1d(listed, win):
+            for g in range(Hkv):
+                ks, p, ds = _row_grads(q, k, v, idx, window, scale, dout, b, int(t), g, G)
+                j = int(np.searchsorted(ks, s))
+                hs = slice(g * G, (g + 1) * G)
+                dK[r, g] += scale * np.matmul(ds[:, j], _f64(q[b, t, hs]))
+                dV[r, g] += np.matmul(p[:, j], _f64(dout[b, t, hs]))
+    return dK, dV
+
+
 # ----------------------------------------------------------------------------------------
 # Fixed-graph distance attention  [SLM] "Cómo eligen los tokens a quién escuchar"
 # ----------------------------------------------------------------------------------------

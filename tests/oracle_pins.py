@@ -536,6 +536,25 @@ def pin_attn_bwd_finite_differences(orc):
             assert abs((up - dn) / (2 * eps) - grad[pos]) < 1e-7, (which, pos)
 
 
+def pin_attn_bwd_sampled_rows_and_keys(orc):
+    """The sampled forms (dQ of chosen rows over S_t only; dK and dV of chosen keys summed
+    over the rows that hold them) equal the full backward on a case with two sequences,
+    two KV groups, listed keys inside the window, -1 padding and out-of-range entries."""
+    B, T, Hq, Hkv, D, k, W = 2, 40, 4, 2, 8, 6, 4
+    x = sa_synth.attn_inputs(97, B, T, Hq, Hkv, D, "f32")
+    idx = sa_synth.random_topk_idx(98, B, T, k, junk=True)
+    dout = sa_synth.rng(99).standard_normal((B, T, Hq, D))
+    dQ, dK, dV = orc.sparse_attn_bwd(x["q"], x["k"], x["v"], idx, W, 0.4, dout)
+    rows = [0, 1, 5, 17, 39]
+    dq = orc.sparse_attn_bwd_rows(x["q"], x["k"], x["v"], idx, W, 0.4, dout, rows)
+    assert np.abs(dq - dQ[:, rows]).max() < 1e-12
+    for b in range(B):
+        keys = [0, 3, 20, 38, 39]
+        dk, dv = orc.sparse_attn_bwd_keys(x["q"], x["k"], x["v"], idx, W, 0.4, dout, b, keys)
+        assert np.abs(dk - dK[b, keys]).max() < 1e-12
+        assert np.abs(dv - dV[b, keys]).max() < 1e-12
+
+
 # ------------------------------------------------------------------------------ NSA branches
 
 def _mask_attend64(q, k, v, scale, mask):

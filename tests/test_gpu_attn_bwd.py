@@ -133,3 +133,50 @@ def test_bwd_listed_keys_inside_window_count_once():
     for mode in MODES:
         note(f"sparse_attn_bwd listed keys inside the window {mode}")
         _run(x, idx, W, 0.125, 922, mode)
+
+
+@pytest.mark.slow
+def test_bwd_64k_sampled():
+    """The 64K workload (T=65536, Hq=16, Hkv=1, D=128, top-2048 from the fused indexer,
+    window 128) with the workspace of 32768-row chunks that the bench uses: dQ on sampled
+    rows and dK / dV on sampled keys against the oracle, and the two ways of forming dK /
+    dV (partial rows, float atomics) against each other on every entry."""
+    import torch
+    p = sa_synth.WORKLOADS[3].params
+    T, k, W, scale = p["T"], p["topk"], p["window"], p["scale"]
+    note("sparse_attn_bwd T=65536 k=2048 W=128 (sampled rows and keys)")
+    x = sa_synth.prefill_inputs(1005, 1, T, p["Hq"], p["Hkv"], p["D"], p["H_I"], p["D_I"], "bf16")
+    qi, ki, w = dev(x["qi"], "bf16"), dev(x["ki"], "bf16"), dev(x["w"], "f32")
+    idx = torch.full((1, T, k), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(sa.sa_indexer_topk_workspace(1, T, p["H_I"], p["D_I"], T // 2, T, k),
+                     dtype=torch.uint8, device="cuda")
+    for r0 in (0, T // 2):
+        sa.sa_indexer_topk(qi, ki, w, k, r0, r0 + T // 2, idx, ws)
+    del ws
+    q, kk, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+    out, lse = sa.sa_sparse_attn_fwd(q, kk, v, idx, W, scale, return_lse=True)
+    dout = sa_synth.round_bf16(sa_synth.rng(1006).standard_normal(x["q"].shape, dtype=np.float32))
+    do = dev(dout, "bf16")
+    wsb = torch.empty(sa.sa_sparse_attn_bwd_workspace(1, T, p["Hkv"], p["D"], k, W, 32768),
+                      dtype=torch.uint8, device="cuda")
+    dq, dk, dv = sa.sa_sparse_attn_bwd(q, kk, v, idx, W, scale, out, lse, do, workspace=wsb)
+    del wsb
+    _, dk_a, dv_a = sa.sa_sparse_attn_bwd(q, kk, v, idx, W, scale, out, lse, do)
+    for name, a, b_ in (("dk", dk, dk_a), ("dv", dv, dv_a)):
+        diff = float((a - b_).abs().max() / b_.abs().max())
+        print(f"  {name}: partial rows vs atomics, max diff {diff:.2e} of max |grad|")
+        assert diff <= REL, (name, diff)
+    idx_h = host(idx)
+    g = sa_synth.rng(1007)
+    rows = sorted(set([0, 1, k - 1, k, T - 1] + g.integers(k, T, size=8).tolist()))
+    want = orc.sparse_attn_bwd_rows(x["q"], x["k"], x["v"], idx_h, W, scale, dout, rows)
+    got = host(dq)[:, rows]
+    err, top = np.abs(got - want).max(), np.abs(want).max()
+    print(f"  dq on {len(rows)} rows: max err {err:.3e} of max |grad| {top:.3e}")
+    assert err <= REL * top
+    keys = sorted(set([3, k + 5, T // 2 + 7, T - 130, T - 1] + g.integers(0, T, size=2).tolist()))
+    wk, wv = orc.sparse_attn_bwd_keys(x["q"], x["k"], x["v"], idx_h, W, scale, dout, 0, keys)
+    for name, got, want in (("dk", host(dk)[0, keys], wk), ("dv", host(dv)[0, keys], wv)):
+        err, top = np.abs(got - want).max(), np.abs(want).max()
+        print(f"  {name} on {len(keys)} keys: max err {err:.3e} of max |grad| {top:.3e}")
+        assert err <= REL * top

@@ -9,11 +9,13 @@ before the timed region.  ``value`` is query tokens per second of the whole step
 
 The JSON line also carries the roofline of the dominant kernel (sparse attention; bytes
 gathered per launch / its average HIP-event duration / 8 TB/s), the float64 CPU oracle
-timed on a bounded row sample, and the other hot-path rows: fixed-graph attention (16K),
-block-sparse decode (32 x 128K) and cross-layer index reuse (128K, F,S,S,S).
+timed on a bounded row sample, and the other hot-path rows: the sparse-attention backward
+(64K), E4M3 indexer inputs (64K), NSA's three branches (prefill 64K, decode 32 x 128K),
+fixed-graph attention (16K, 64K, 128K), block-sparse decode (32 x 128K) and cross-layer
+index reuse (128K, F,S,S,S).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk ROWS] [--no-extra]
-       [--no-cpu] [--only attn|prefill]
+       [--no-cpu] [--only attn|prefill] [--extra all|bwd] [--bwd-rows N]
 """
 
 from __future__ import annotations
@@ -68,6 +70,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip graph/decode/reuse rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--extra", choices=["all", "bwd"], default="all",
+                    help="the extra rows to run (bwd: only the backward, for profiling runs)")
     ap.add_argument("--bwd-rows", type=int, default=32768,
                     help="query rows per chunk of the backward's partial-row workspace")
     ap.add_argument("--only", choices=["attn", "prefill"], default=None,
@@ -357,6 +361,8 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
     }
     del o_f, lse_f, g_out, dq_b, dk_b, dv_b, ws_b, dk_w, dv_w
     torch.cuda.empty_cache()
+    if args.extra == "bwd":
+        return rows
 
     # ---- the 64K fused index path with 8-bit (E4M3) indexer inputs: the same draws as the
     # bf16 step, encoded to E4M3; bf16 timed beside on the same sizes

@@ -9,10 +9,10 @@
 //
 //  * round_bf16: the float32 block means (sa_block_meanpool of K and of V) rounded once
 //    per call to bf16 rows for the MFMA tiles.
-//  * cmp_attn_mfma<D>: the compressed branch.  One wavefront per (batch, token, KV head)
-//    runs GroupAttn (attn_tile.h) over the compressed keys j < (t+1)/block, 32 per step;
-//    tokens are dealt round-robin over the XCDs, longest first (the work grows with t, and
-//    the compressed rows are few enough for every XCD's L2).
+//  * cmp_attn_tile<D>: the compressed branch.  One workgroup per (batch, 8 tokens, KV
+//    head), one wavefront per token attending to the compressed keys j < (t+1)/block with
+//    GroupAttn's arithmetic; the 32-row K/V tiles are loaded once per workgroup into LDS
+//    and shared by its 8 tokens; token groups are dealt longest first.
 //  * head_sum + block_scores: score[t, j] = sum_h q[t,h] . kbar[j, g(h)] in float32 for the
 //    complete blocks of each row (the queries of each KV group summed first); a workgroup
 //    owns 64 rows x 64 blocks with the summed queries and the pooled keys staged in LDS,
@@ -40,54 +40,161 @@ __global__ __launch_bounds__(256) void round_bf16(const float* __restrict__ src,
   st8(dst + 4 * i, u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
 }
 
+// One workgroup of 8 wavefronts per (batch, 8 consecutive tokens, KV head); wavefront w
+// takes token 8 tb + w.  The compressed K and V rows are streamed in 32-row tiles that
+// the whole workgroup loads once into LDS (the next tile's rows in flight in registers
+// while the current one is used), so each row leaves L2 once per 8 tokens instead of
+// once per token.  Per token the arithmetic is GroupAttn's (attn_tile.h): S^T = K . Q^T
+// with the group's heads as the MFMA N dimension, an online softmax in the log2 domain,
+// O^T += V^T . P^T with V^T read from LDS, over the tiles that hold its compressed keys
+// j < (t + 1) / block.  Token groups are dealt longest first.
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void cmp_attn_mfma(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void cmp_attn_tile(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, int B, int T, int Hq, int Hkv, int nb, int block,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  using GA = GroupAttn<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char vl[GA::LDS_BYTES];
-  const int lane = threadIdx.x;
+  constexpr int KS = D / 32, DT = D / 16, CH = D * 2 / 16;  // 16-byte chunks per row
+  constexpr int LROW = D * 2 + 16;                          // padded LDS row (bytes)
+  constexpr int TPG = 8;                                    // tokens per workgroup
+  __shared__ __attribute__((aligned(16))) unsigned char kt[32 * LROW];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[32 * LROW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
-  // the work of a token grows with t: tokens are dealt round-robin over the XCDs (every
-  // XCD keeps all the compressed rows in its L2), longest first
-  const int64_t items = (int64_t)B * T * Hkv;
+  const int ntg = (T + TPG - 1) / TPG;
+  const int64_t items = (int64_t)B * ntg * Hkv;
   if ((int64_t)blockIdx.x >= items) return;
-  const int64_t item = items - 1 - (int64_t)blockIdx.x;
+  const int64_t item = items - 1 - (int64_t)blockIdx.x;  // longest first
   const int g = (int)(item % Hkv);
   const int b = (int)((item / Hkv) % B);
-  const int t = (int)(item / ((int64_t)Hkv * B));
+  const int tg = (int)(item / ((int64_t)Hkv * B));
+  const int t = tg * TPG + w;
+  const bool tok = t < T;
   const int G = Hq / Hkv;
   const int h = g * G + n;
-  const bool hv = n < G;
+  const bool hv = tok && n < G;
 
-  GA ga;
-  ga.init(hv ? q + (((int64_t)b * T + t) * Hq + h) * D : nullptr, grp);
-  const int nfull = (t + 1) / block;  // complete blocks at or before t
+  bf16x8 qB[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (hv) x = ld16_nt(q + (((int64_t)b * T + t) * Hq + h) * D + ks * 32 + grp * 8);
+    qB[ks] = as_bf16x8(x);
+  }
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int nfull_w = tok ? (t + 1) / block : 0;  // this token's compressed keys
+  const int t_last = min(tg * TPG + TPG - 1, T - 1);
+  const int nfull = (t_last + 1) / block;         // the workgroup's
+  const int ntiles = (nfull + 31) / 32;
   const int64_t stride = (int64_t)Hkv * D;
   const uint16_t* kbase = kb + ((int64_t)b * nb * Hkv + g) * D;
   const uint16_t* vbase = vb + ((int64_t)b * nb * Hkv + g) * D;
-  const int slot = lane & 31;
-  auto fetch = [&](int tile) -> int { return tile * 32 + slot; };
-  auto finish = [&](int, int raw, int& key, uint32_t& vm) {
-    const bool ok = raw < nfull;
-    vm = (uint32_t)ballot(ok);
-    key = ok ? raw : 0;
+  // tile loads: thread tid < 32 * CH takes row tid / CH, 16-byte chunk tid % CH
+  const bool ldr = tid < 32 * CH;
+  const int r_ld = tid / CH, c_ld = tid % CH;
+  u32x4 kr = {0u, 0u, 0u, 0u}, vr = kr;
+  auto ldtile = [&](int tile) {
+    const int j = tile * 32 + r_ld;
+    kr = u32x4{0u, 0u, 0u, 0u};
+    vr = kr;
+    if (ldr && j < nfull) {
+      kr = ld16(kbase + (int64_t)j * stride + c_ld * 8);
+      vr = ld16(vbase + (int64_t)j * stride + c_ld * 8);
+    }
   };
-  ga.template run<false>((nfull + 31) / 32, fetch, finish, kbase, vbase, stride, vl, scale_log2,
-                         lane);
+  if (ntiles > 0) ldtile(0);
 
-  const float l = ga.total_l();
+  const unsigned char* vrow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (j < 4) ? grp * 4 + j : 16 + grp * 4 + (j - 4);
+    vrow[j] = vt + r * LROW + n * 2;
+  }
+  for (int tile = 0; tile < ntiles; ++tile) {
+    if (ldr) {
+      st16(kt + r_ld * LROW + c_ld * 16, kr);
+      st16(vt + r_ld * LROW + c_ld * 16, vr);
+    }
+    __syncthreads();
+    if (tile + 1 < ntiles) ldtile(tile + 1);  // in flight while this tile is used
+    const int valid = nfull_w - tile * 32;     // slots below are this token's keys
+    if (valid > 0) {
+      const uint32_t vm = valid >= 32 ? 0xffffffffu : ((1u << valid) - 1u);
+      // ---- S^T = K . Q^T for the two 16-key halves (K rows from LDS)
+      f32x4 s[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        s[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kA = ld16(kt + (c2 * 16 + n) * LROW + (ks * 32 + grp * 8) * 2);
+          s[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kA), qB[ks], s[c2], 0, 0, 0);
+        }
+      }
+      // ---- online softmax (log2 domain); head n's max over the 4 lane groups
+      float x[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = c2 * 16 + grp * 4 + i;
+          const float v = ((vm >> slot) & 1u) ? s[c2][i] * scale_log2 : -INFINITY;
+          x[c2 * 4 + i] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, shfl_xor_f(mt, 16));
+      mt = fmaxf(mt, shfl_xor_f(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = exp2f(x[j] - m_new);
+        psum += x[j];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      }
+      const u32x4 pw = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                        pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+      const bf16x8 pB = as_bf16x8(pw);
+      // ---- O^T += V^T . P^T (V^T read transposed from LDS)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint32_t a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(vrow[2 * j] + dt * 32);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(vrow[2 * j + 1] + dt * 32);
+          a[j] = lo | (hi << 16);
+        }
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{a[0], a[1], a[2], a[3]}),
+                                                          pB, acc[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the tile's LDS rows are rewritten next
+  }
+
+  float l = l_run;
+  l += shfl_xor_f(l, 16);
+  l += shfl_xor_f(l, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (hv) {
     uint16_t* orow = out + (((int64_t)b * T + t) * Hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < GA::DT; ++dt) {
-      const f32x4 a = ga.acc[dt] * inv;
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 a = acc[dt] * inv;
       st8(orow + dt * 16 + grp * 4, u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
     }
     if (lse && grp == 0)
-      lse[((int64_t)b * Hq + h) * T + t] = l > 0.f ? (ga.m_run + __log2f(l)) * kLn2 : -INFINITY;
+      lse[((int64_t)b * Hq + h) * T + t] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -388,14 +495,14 @@ hipError_t launch_cmp_attn(const void* q, const float* kbar, const float* vbar, 
     hipLaunchKernelGGL(round_bf16, dim3(g), dim3(256), 0, st, kbar, kb, n / 4);
     hipLaunchKernelGGL(round_bf16, dim3(g), dim3(256), 0, st, vbar, vb, n / 4);
   }
-  const int64_t items = (int64_t)B * T * Hkv;
+  const int64_t items = (int64_t)B * ((T + 7) / 8) * Hkv;
   const dim3 grid((unsigned)items);
   const float sl2 = scale * 1.4426950408889634f;
   if (D == 128)
-    hipLaunchKernelGGL(cmp_attn_mfma<128>, grid, dim3(64), 0, st, (const uint16_t*)q, kb, vb, B,
+    hipLaunchKernelGGL(cmp_attn_tile<128>, grid, dim3(512), 0, st, (const uint16_t*)q, kb, vb, B,
                        T, Hq, Hkv, nb, block, sl2, (uint16_t*)out, lse);
   else
-    hipLaunchKernelGGL(cmp_attn_mfma<64>, grid, dim3(64), 0, st, (const uint16_t*)q, kb, vb, B,
+    hipLaunchKernelGGL(cmp_attn_tile<64>, grid, dim3(512), 0, st, (const uint16_t*)q, kb, vb, B,
                        T, Hq, Hkv, nb, block, sl2, (uint16_t*)out, lse);
   return hipGetLastError();
 }

@@ -224,6 +224,44 @@ def main():
         if fused:
             prefill_indices(Timer(torch))  # leave the step's own indices in idx
             torch.cuda.synchronize()
+    # the same step on two streams: the attention of a row chunk starts as soon as that
+    # chunk's indices exist, beside the next chunk's index build (sa_sparse_attn_fwd_rows)
+    two_streams = None
+    if fused and args.only is None:
+        s_idx, s_att = torch.cuda.Stream(), torch.cuda.Stream()
+
+        def piped():
+            cur = torch.cuda.current_stream()
+            s_idx.wait_stream(cur)
+            s_att.wait_stream(cur)
+            for r0 in range(0, T, chunk):
+                r1 = min(T, r0 + chunk)
+                with torch.cuda.stream(s_idx):
+                    sa.sa_indexer_topk(qi, ki, w, topk, r0, r1, idx, ws)
+                    ev = torch.cuda.Event()
+                    ev.record(s_idx)
+                s_att.wait_event(ev)
+                with torch.cuda.stream(s_att):
+                    sa.sa_sparse_attn_fwd_rows(q, k, v, idx, window, scale, r0, r1, out)
+            cur.wait_stream(s_idx)
+            cur.wait_stream(s_att)
+
+        out_seq = out.clone()
+        for _ in range(args.warmup):
+            piped()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            piped()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_p = e0.elapsed_time(e1) / args.steps
+        two_streams = {"ms_per_step": ms_p, "query_tokens_per_s": T / (ms_p * 1e-3),
+                       "vs_sequential_step": ms_step / ms_p,
+                       "same_output": bool(torch.equal(out_seq, out))}
+        log(f"two streams: {ms_p:.3f} ms/step (sequential {ms_step:.3f})")
+        del out_seq
     tsrc = other if fused else tm
     nsteps_two = 3 if fused else args.steps
     idx_ms = tsrc.ms("indexer")[0] / nsteps_two
@@ -253,6 +291,7 @@ def main():
         "step_breakdown_ms": ({"indexer_topk": fused_ms} if fused else
                               {"indexer": idx_ms, "topk": topk_ms}) | {"sparse_attn": attn_avg_ms},
         "sparse_attn_query_tokens_per_s": T / (attn_avg_ms * 1e-3) if attn_n else None,
+        "two_streams": two_streams,
         "roofline": {
             "kernel": "sparse_attn_mfma<128>",
             "bound": "hbm",

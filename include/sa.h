@@ -153,6 +153,17 @@ size_t sa_indexer_topk_workspace(int B, int T, int H_I, int D_I, int row_begin, 
 int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
                        int T, int Hq, int Hkv, int D, int topk, int window, float scale,
                        int dtype, void* out, float* lse, void* stream);
+/*
+ * The same for the query rows [row_begin, row_end) only (0 <= row_begin <= row_end <= T):
+ * out and lse rows outside the range are not touched, and only idx rows inside it are read,
+ * so the attention of a row chunk can run as soon as that chunk's indices exist (on
+ * another stream while the next chunk's indices are built).  sa_sparse_attn_fwd is the
+ * range [0, T).
+ */
+int sa_sparse_attn_fwd_rows(const void* q, const void* k, const void* v, const int32_t* idx,
+                            int B, int T, int Hq, int Hkv, int D, int topk, int window,
+                            float scale, int dtype, int row_begin, int row_end, void* out,
+                            float* lse, void* stream);
 
 /*
  * Sparse attention backward.  [NSA] "Puntos Clave" (the backward pass of sparse attention,

@@ -18,7 +18,8 @@ import re
 
 __all__ = [
     "SAError", "lib", "library_path", "declared_symbols",
-    "sa_indexer_scores", "sa_topk_select", "sa_sparse_attn_fwd", "sa_graph_attn_fwd",
+    "sa_indexer_scores", "sa_topk_select", "sa_sparse_attn_fwd", "sa_sparse_attn_fwd_rows",
+    "sa_graph_attn_fwd",
     "sa_block_meanpool", "sa_sparse_decode", "sa_sparse_decode_workspace",
     "sa_sparse_decode_auto_splits", "sa_version",
 ]
@@ -42,6 +43,10 @@ _SIGS = {
     "sa_sparse_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_void_p, _c_void_p, _c_void_p]),
+    "sa_sparse_attn_fwd_rows": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_float, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                         _c_void_p]),
     "sa_sparse_attn_bwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -261,6 +266,27 @@ def sa_sparse_attn_fwd(q, k, v, idx, window: int, scale: float, out=None, lse=No
                                   _stream(q.device))
     _check("sa_sparse_attn_fwd", rc)
     return (out, lse) if return_lse else out
+
+
+def sa_sparse_attn_fwd_rows(q, k, v, idx, window: int, scale: float, row_begin: int,
+                            row_end: int, out, lse=None):
+    """sa_sparse_attn_fwd for the query rows [row_begin, row_end) only, into the full-size
+    out (and lse); other rows are not touched."""
+    torch = _torch()
+    _dev(q, "q"); _dev(k, "k", q.dtype); _dev(v, "v", q.dtype); _dev(out, "out", q.dtype)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    topk = 0
+    if idx is not None:
+        _dev(idx, "idx", torch.int32)
+        topk = idx.shape[-1]
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = lib().sa_sparse_attn_fwd_rows(_p(q), _p(k), _p(v), _p(idx), B, T, Hq, Hkv, D, topk,
+                                       window, float(scale), _dtype_code(q), row_begin, row_end,
+                                       _p(out), _p(lse), _stream(q.device))
+    _check("sa_sparse_attn_fwd_rows", rc)
+    return out
 
 
 def sa_graph_attn_fwd(cq, ck, v, bias, tau: float, local: int, n_pow2: int, out=None,

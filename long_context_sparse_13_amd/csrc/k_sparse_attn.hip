@@ -29,17 +29,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int B, int T, int Hq,
     int Hkv, int topk, int window, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int r0, int nrows) {
   using GA = GroupAttn<D>;
   __shared__ __attribute__((aligned(16))) unsigned char vl[GA::LDS_BYTES];
 
   const int lane = threadIdx.x;
   const int n = lane & 15, grp = lane >> 4;
-  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * T * Hkv);
+  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * nrows * Hkv);
   if (item < 0) return;
   const int g = (int)(item % Hkv);
-  const int t = (int)((item / Hkv) % T);
-  const int b = (int)(item / ((int64_t)Hkv * T));
+  const int t = r0 + (int)((item / Hkv) % nrows);
+  const int b = (int)(item / ((int64_t)Hkv * nrows));
   const int G = Hq / Hkv;
   const int h = g * G + n;
   const bool hv = n < G;
@@ -97,7 +97,7 @@ template <int D, bool BF>
 __global__ __launch_bounds__(64) void sparse_attn_valu(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ idx, int B, int T, int Hq, int Hkv, int topk, int window,
-    float scale_log2, void* __restrict__ out, float* __restrict__ lse) {
+    float scale_log2, void* __restrict__ out, float* __restrict__ lse, int r0, int nrows) {
   constexpr int MAXE = 4096;              // G * D
   __shared__ float qs[MAXE];               // scaled queries of the group, [G][D]
   __shared__ float os[MAXE];               // output accumulators, [G][D]
@@ -106,11 +106,11 @@ __global__ __launch_bounds__(64) void sparse_attn_valu(
   __shared__ int keys[64];
 
   const int lane = threadIdx.x;
-  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * T * Hkv);
+  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * nrows * Hkv);
   if (item < 0) return;
   const int g = (int)(item % Hkv);
-  const int t = (int)((item / Hkv) % T);
-  const int b = (int)(item / ((int64_t)Hkv * T));
+  const int t = r0 + (int)((item / Hkv) % nrows);
+  const int b = (int)(item / ((int64_t)Hkv * nrows));
   const int G = Hq / Hkv;
   const int GD = G * D;
 
@@ -203,34 +203,37 @@ __global__ __launch_bounds__(64) void sparse_attn_valu(
 
 hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
                                   int B, int T, int Hq, int Hkv, int D, int topk, int window,
-                                  float scale, bool bf16, void* out, float* lse, hipStream_t st) {
+                                  float scale, bool bf16, void* out, float* lse, int row_begin,
+                                  int row_end, hipStream_t st) {
   const int G = Hq / Hkv;
   const float sl2 = scale * kLog2e;
-  const dim3 grid((unsigned)xcd_grid((int64_t)B * T * Hkv));
+  const int nrows = row_end - row_begin;
+  if (nrows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)xcd_grid((int64_t)B * nrows * Hkv));
   const dim3 block(64);
   if (bf16 && G <= 16) {
     if (D == 128)
       hipLaunchKernelGGL(sparse_attn_mfma<128>, grid, block, 0, st, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, idx, B, T, Hq, Hkv, topk, window,
-                         sl2, (uint16_t*)out, lse);
+                         sl2, (uint16_t*)out, lse, row_begin, nrows);
     else
       hipLaunchKernelGGL(sparse_attn_mfma<64>, grid, block, 0, st, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, idx, B, T, Hq, Hkv, topk, window,
-                         sl2, (uint16_t*)out, lse);
+                         sl2, (uint16_t*)out, lse, row_begin, nrows);
   } else if (bf16) {
     if (D == 128)
       hipLaunchKernelGGL((sparse_attn_valu<128, true>), grid, block, 0, st, q, k, v, idx, B, T, Hq,
-                         Hkv, topk, window, sl2, out, lse);
+                         Hkv, topk, window, sl2, out, lse, row_begin, nrows);
     else
       hipLaunchKernelGGL((sparse_attn_valu<64, true>), grid, block, 0, st, q, k, v, idx, B, T, Hq,
-                         Hkv, topk, window, sl2, out, lse);
+                         Hkv, topk, window, sl2, out, lse, row_begin, nrows);
   } else {
     if (D == 128)
       hipLaunchKernelGGL((sparse_attn_valu<128, false>), grid, block, 0, st, q, k, v, idx, B, T,
-                         Hq, Hkv, topk, window, sl2, out, lse);
+                         Hq, Hkv, topk, window, sl2, out, lse, row_begin, nrows);
     else
       hipLaunchKernelGGL((sparse_attn_valu<64, false>), grid, block, 0, st, q, k, v, idx, B, T, Hq,
-                         Hkv, topk, window, sl2, out, lse);
+                         Hkv, topk, window, sl2, out, lse, row_begin, nrows);
   }
   return hipGetLastError();
 }

@@ -173,15 +173,18 @@ int sa_indexer_topk(const void* qi, const void* ki, const float* w, int B, int T
   }
 }
 
-int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
-                       int T, int Hq, int Hkv, int D, int topk, int window, float scale,
-                       int dtype, void* out, float* lse, void* stream) {
+int sa_sparse_attn_fwd_rows(const void* q, const void* k, const void* v, const int32_t* idx,
+                            int B, int T, int Hq, int Hkv, int D, int topk, int window,
+                            float scale, int dtype, int row_begin, int row_end, void* out,
+                            float* lse, void* stream) {
   try {
     REQUIRE_PTR(q);
     REQUIRE_PTR(k);
     REQUIRE_PTR(v);
     REQUIRE_PTR(out);
     REQUIRE(B >= 1 && T >= 1, "B and T must be >= 1 (B=%d T=%d)", B, T);
+    REQUIRE(0 <= row_begin && row_begin <= row_end && row_end <= T,
+            "need 0 <= row_begin <= row_end <= T (got %d, %d, T=%d)", row_begin, row_end, T);
     REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
     REQUIRE(topk >= 0 && window >= 0 && topk + window >= 1,
             "need topk >= 0, window >= 0 and topk + window >= 1 (topk=%d window=%d)", topk, window);
@@ -197,12 +200,19 @@ int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_
     if (lse) REQUIRE(aligned16(lse), "lse is not 16-byte aligned");
     if (idx) REQUIRE(aligned16(idx), "idx is not 16-byte aligned");
     return hip_status(sa::launch_sparse_attn_fwd(q, k, v, idx, B, T, Hq, Hkv, D, topk, window,
-                                                 scale, dtype == SA_BF16, out, lse,
-                                                 as_stream(stream)),
+                                                 scale, dtype == SA_BF16, out, lse, row_begin,
+                                                 row_end, as_stream(stream)),
                       "sa_sparse_attn_fwd launch");
   } catch (...) {
     return fail(SA_ERR_INTERNAL, "sa_sparse_attn_fwd: unexpected exception");
   }
+}
+
+int sa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                       int T, int Hq, int Hkv, int D, int topk, int window, float scale,
+                       int dtype, void* out, float* lse, void* stream) {
+  return sa_sparse_attn_fwd_rows(q, k, v, idx, B, T, Hq, Hkv, D, topk, window, scale, dtype, 0,
+                                 T > 0 ? T : 0, out, lse, stream);
 }
 
 int sa_graph_attn_fwd(const void* cq, const void* ck, const void* v, const float* bias,

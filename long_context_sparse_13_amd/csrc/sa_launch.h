@@ -35,7 +35,8 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
 
 hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
                                   int B, int T, int Hq, int Hkv, int D, int topk, int window,
-                                  float scale, bool bf16, void* out, float* lse, hipStream_t st);
+                                  float scale, bool bf16, void* out, float* lse, int row_begin,
+                                  int row_end, hipStream_t st);
 
 hipError_t launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx,
                                   int B, int T, int Hq, int Hkv, int D, int topk, int window,

@@ -107,6 +107,16 @@ def test_attn_validation(L):
     assert f(P, P, P, P, 1, 8, 128, 1, 64, 4, 4, 0.1, 1, P, None, None) == 2    # G*D too big
 
 
+def test_attn_rows_validation(L):
+    f = L.sa_sparse_attn_fwd_rows
+    assert f(P, P, P, P, 1, 8, 4, 1, 64, 4, 4, 0.1, 1, -1, 4, P, None, None) == 1   # row_begin < 0
+    assert f(P, P, P, P, 1, 8, 4, 1, 64, 4, 4, 0.1, 1, 5, 4, P, None, None) == 1    # begin > end
+    assert f(P, P, P, P, 1, 8, 4, 1, 64, 4, 4, 0.1, 1, 0, 9, P, None, None) == 1    # end > T
+    assert "row_begin" in _err(L)
+    assert f(P, P, P, P, 1, 8, 4, 1, 96, 4, 4, 0.1, 1, 0, 8, P, None, None) == 2    # D
+    assert f(P, P, P, None, 1, 8, 4, 1, 64, 4, 4, 0.1, 1, 0, 8, P, None, None) == 1  # idx NULL
+
+
 def test_indexer_and_topk_validation(L):
     g = L.sa_indexer_scores
     assert g(P, P, P, 1, 16, 4, 64, 1, 0, 16, P, 15, None) == 1   # ld % 4

@@ -90,3 +90,34 @@ def test_deterministic():
     ref = sa.sa_sparse_attn_fwd(*args, 32, 0.08)
     for _ in range(4):
         assert torch.equal(sa.sa_sparse_attn_fwd(*args, 32, 0.08), ref)
+
+
+@pytest.mark.parametrize("dtype,G", [("bf16", 16), ("bf16", 32), ("f32", 4)])
+def test_row_ranges(dtype, G):
+    """sa_sparse_attn_fwd_rows over ragged row ranges that cover [0, T) writes what the
+    full call writes (bit for bit: same kernel, same per-row arithmetic), leaves every row
+    outside its range untouched, and matches the oracle; an empty range writes nothing."""
+    import torch
+    B, T, Hkv, D, topk, W = 2, 301, 1, 64, 24, 16
+    Hq = G * Hkv
+    note(f"sparse_attn_fwd_rows B={B} T={T} Hq={Hq} D={D} {dtype}")
+    x = sa_synth.attn_inputs(171, B, T, Hq, Hkv, D, dtype)
+    idx = sa_synth.random_topk_idx(172, B, T, topk, junk=True)
+    q, k, v = dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype)
+    di = dev(idx, "i32")
+    full, lfull = sa.sa_sparse_attn_fwd(q, k, v, di, W, 0.125, return_lse=True)
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((B, Hq, T), 7.0, dtype=torch.float32, device="cuda")
+    sa.sa_sparse_attn_fwd_rows(q, k, v, di, W, 0.125, 5, 5, out, lse)     # empty: no change
+    assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
+    sa.sa_sparse_attn_fwd_rows(q, k, v, di, W, 0.125, 40, 177, out, lse)
+    assert bool((out[:, :40] == 7.0).all()) and bool((out[:, 177:] == 7.0).all())
+    assert bool((lse[:, :, :40] == 7.0).all()) and bool((lse[:, :, 177:] == 7.0).all())
+    assert torch.equal(out[:, 40:177], full[:, 40:177])
+    for r0, r1 in ((0, 40), (177, 300), (300, 301)):
+        sa.sa_sparse_attn_fwd_rows(q, k, v, di, W, 0.125, r0, r1, out, lse)
+    assert torch.equal(out, full) and torch.equal(lse, lfull)
+    rows = [0, 39, 40, 176, 177, 299, 300]
+    O, _ = orc.sparse_attn(x["q"], x["k"], x["v"], idx, W, 0.125, rows)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    assert np.abs(host(out)[:, rows] - O).max() <= tol

@@ -159,15 +159,26 @@ __device__ __forceinline__ uint64_t pack_rank(uint32_t key, int pos) {
 }
 __device__ __forceinline__ int unpack_pos(uint64_t c) { return (int)(0xffffffffu - (uint32_t)c); }
 
-// Exact top-m of n packed entries in LDS (n a multiple of 8, padded with 0): an entry's
-// rank is the number of entries better than it; entries with rank < m are handed to
-// keep(rank, entry).  All threads read the same LDS words (broadcast), 8 per step.
+// Exact top-m of n packed entries in LDS (n a multiple of 8, padded with 0; comb 16-byte
+// aligned): an entry's rank is the number of entries better than it; entries with rank < m
+// are handed to keep(rank, entry).  All threads read the same LDS words (broadcast), 32
+// per batch so that one LDS round trip covers 32 comparisons.
 template <int NT, typename Keep>
 __device__ __forceinline__ void rank_select(const uint64_t* comb, int n, int m, Keep&& keep) {
+  typedef __attribute__((ext_vector_type(2))) unsigned long long u64x2;
+  const u64x2* c2 = reinterpret_cast<const u64x2*>(comb);
   for (int i = threadIdx.x; i < n; i += NT) {
     const uint64_t ci = comb[i];
     int rank = 0;
-    for (int j = 0; j < n; j += 8) {
+    int j = 0;
+    for (; j + 32 <= n; j += 32) {
+      u64x2 x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x[u] = c2[j / 2 + u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) rank += (x[u][0] > ci) + (x[u][1] > ci);
+    }
+    for (; j < n; j += 8) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) rank += comb[j + u] > ci;
     }
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ lens, int Lmax, int Hq, int Hkv, int block, int per_wg, int cpw,
     uint32_t* __restrict__ cand) {
-  __shared__ uint64_t scomb[kScoreChunk + kCandMax];
+  __shared__ __attribute__((aligned(16))) uint64_t scomb[kScoreChunk + kCandMax];
   __shared__ uint64_t best[kCandMax];
   __shared__ __attribute__((aligned(16))) uint16_t qrows[16 * D];  // the group's query rows
   // a row (D floats) is read by 8 lanes, C = D/8 consecutive floats each; 8 rows per
@@ -255,9 +266,11 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
       if ((lane & 7) == 0)
         scomb[wv * 64 + gi * 8 + (lane >> 3)] = pack_rank(order_key(part), j < j_end ? j : -1);
     }
-    if (tid < cpw) scomb[kScoreChunk + tid] = best[tid];  // running candidates compete
+    // from the second chunk on, the running candidates compete with the new scores
+    const bool first = c0 == j_begin;
+    if (!first && tid < cpw) scomb[kScoreChunk + tid] = best[tid];
     __syncthreads();
-    rank_select<kScoreThreads>(scomb, kScoreChunk + cpw, cpw,
+    rank_select<kScoreThreads>(scomb, kScoreChunk + (first ? 0 : cpw), cpw,
                                [&](int rank, uint64_t c) { best[rank] = c; });
     __syncthreads();
   }

@@ -207,14 +207,21 @@ __global__ __launch_bounds__(256) void graph_attn_block(
       }
     }
 
-  // ---- stage: V^T of the band, coordinates; P cleared
+  // ---- stage: V^T of the band, coordinates; P cleared.  A lane writes its 8 values
+  // (features d0 .. d0+7 of one band row) in an order rotated by its chunk index, so that
+  // at each step the lanes of different chunks write rows d0 + q with distinct q mod 8:
+  // with a row pitch of 17 x 16 bytes those fall in distinct LDS banks (rows 8 apart
+  // would share one).
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const int e = tid + 256 * i, r = e / DC, d0 = (e - r * DC) * 8;
+    const int e = tid + 256 * i, r = e / DC, c = e - r * DC, d0 = c * 8;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      vt[d0 + 2 * k][r] = (uint16_t)(vb[i][k] & 0xffffu);
-      vt[d0 + 2 * k + 1][r] = (uint16_t)(vb[i][k] >> 16);
+    for (int k = 0; k < 8; ++k) {
+      const int qv = (k + c) & 7;
+      const uint32_t w01 = (qv & 2) ? vb[i][1] : vb[i][0];
+      const uint32_t w23 = (qv & 2) ? vb[i][3] : vb[i][2];
+      const uint32_t wv = (qv & 4) ? w23 : w01;
+      vt[d0 + qv][r] = (uint16_t)((qv & 1) ? (wv >> 16) : (wv & 0xffffu));
     }
   }
 #pragma unroll

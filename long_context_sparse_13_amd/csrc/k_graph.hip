@@ -13,7 +13,8 @@
 // [t0 - local, t0 + 64) hold every neighbour at offset <= local of every token of the
 // block, so V^T of the band is staged once in LDS and the band part of P.V runs on the
 // 16x16x32 bf16 MFMA (probabilities rounded to bf16, the normaliser summed from the
-// same rounded values).  The far neighbours (offsets 2^j > local) are one row per
+// same rounded values).  Four workgroups per CU (the LDS allows four; at D = 64 the
+// register cap of four wavefronts per SIMD costs a 12-byte spill and gains 11 %).  The far neighbours (offsets 2^j > local) are one row per
 // token and offset; their contributions are added on the vector units from coalesced
 // row loads.  Logits and softmax are float32.  Items are handed to the XCDs in
 // contiguous (block, head) ranges, so the rows a block shares with the blocks just
@@ -126,7 +127,7 @@ constexpr int kGFar = 8;   // far offsets (2^j > local) handled: n_pow2 - #{2^j 
 constexpr int kGLoc = 17;  // band logits per thread: (local + 1) / 4 rounded up, local <= 64
 
 template <int D>
-__global__ __launch_bounds__(256) void graph_attn_block(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void graph_attn_block(
     const uint16_t* __restrict__ cq, const uint16_t* __restrict__ ck,
     const uint16_t* __restrict__ v, const float* __restrict__ bias, float tau_log2, int B, int T,
     int H, int local, int n_pow2, uint16_t* __restrict__ out, float* __restrict__ lse) {

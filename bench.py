@@ -617,12 +617,17 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         ws0 = torch.zeros(sa.sa_sparse_decode_workspace(p["B"], p["L"], p["Hq"], p["Hkv"], p["D"],
                                                         p["block"], p["top_blocks"], 0, 0),
                           dtype=torch.uint8, device=dev)
+        # the compressed range (L/64 = 2048 rows) split over 8 workgroups per sequence
+        ns_c = 8
+        ws_c = torch.zeros(sa.sa_nsa_decode_branch_workspace(p["B"], p["Hq"], p["Hkv"], p["D"], ns_c),
+                           dtype=torch.uint8, device=dev)
         ocd, osd, owd, ond = (torch.empty_like(qd) for _ in range(4))
         gd = torch.rand((p["B"], 1, p["Hq"], 3), generator=torch.Generator(device=dev).manual_seed(1005),
                         device=dev, dtype=torch.float32)
         dparts = {
             "compressed": lambda: sa.sa_nsa_decode_branch(qd, kb16, vb16, lens, 1, p["block"],
-                                                          p["window"], p["scale"], out=ocd),
+                                                          p["window"], p["scale"], out=ocd,
+                                                          n_splits=ns_c, workspace=ws_c),
             "selected": lambda: sa.sa_sparse_decode(qd, kc, vc, kbar, lens, p["block"], p["top_blocks"],
                                                     0, p["scale"], workspace=ws0, out=osd),
             "window": lambda: sa.sa_nsa_decode_branch(qd, kc, vc, lens, 0, p["block"], p["window"],
@@ -634,6 +639,7 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         t_nd = timed(lambda: [fn() for fn in dparts.values()], 20)
         rows["nsa_decode_b32_128k"] = {
             "us_per_step": t_nd * 1e3, "tokens_per_s": p["B"] / (t_nd * 1e-3), "parts_us": dpart_us,
+            "compressed_splits": ns_c,
             "bf16_meanpool_ms_once_per_cache": t_pool16,
         }
         del kb16, vb16, ws0, ocd, osd, owd, ond, gd

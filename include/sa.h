@@ -331,12 +331,18 @@ int sa_block_meanpool_bf16(const void* kcache, const int32_t* lens, int B, int L
  *   lse[b, h]    = log sum exp (natural log; -inf and out = 0 for an empty range)
  * The selected branch is sa_sparse_decode with window 0 (all tokens of the chosen blocks).
  * q, out [B, Hq, D] bf16; lens [B] int32 on the device; lse [B, Hq] float32 or NULL.
+ * n_splits (1..64) workgroups share each (sequence, KV head)'s range, their partial softmaxes
+ * merged by log-sum-exp [STAR paragraph 3]; with n_splits > 1, workspace holds at least
+ * sa_nsa_decode_branch_workspace(B, Hq, Hkv, D, n_splits) bytes, ZERO-FILLED before its first
+ * use (every call leaves its counters at zero again; calls sharing a workspace must be
+ * ordered on one stream).  workspace may be NULL with n_splits = 1.
  * Requires bf16, D in {64, 128}, Hq/Hkv <= 16, block in {16, 32, 64, 128}.
  */
 int sa_nsa_decode_branch(const void* q, const void* keys, const void* vals,
                          const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D, int kind,
                          int block, int window, float scale, int dtype, void* out, float* lse,
-                         void* stream);
+                         int n_splits, void* workspace, size_t ws_bytes, void* stream);
+size_t sa_nsa_decode_branch_workspace(int B, int Hq, int Hkv, int D, int n_splits);
 
 /*
  * NSA gated combine.  [NSA] "Puntos Clave" (three branches) -- the page does not say how

@@ -75,7 +75,9 @@ _SIGS = {
                                         _c_int, _c_int, _c_void_p, _c_void_p]),
     "sa_nsa_decode_branch": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
-                                      _c_int, _c_void_p, _c_void_p, _c_void_p]),
+                                      _c_int, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_size_t,
+                                      _c_void_p]),
+    "sa_nsa_decode_branch_workspace": (_c_size_t, [_c_int] * 5),
     "sa_nsa_combine": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                 _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "sa_status_str": (ctypes.c_char_p, [_c_int]),
@@ -443,10 +445,16 @@ def sa_block_meanpool_bf16(kcache, lens, block: int, kbar=None):
     return kbar
 
 
+def sa_nsa_decode_branch_workspace(B, Hq, Hkv, D, n_splits) -> int:
+    return int(lib().sa_nsa_decode_branch_workspace(B, Hq, Hkv, D, n_splits))
+
+
 def sa_nsa_decode_branch(q, keys, vals, lens, kind: int, block: int, window: int, scale: float,
-                         out=None, lse=None, want_lse: bool = False):
+                         out=None, lse=None, want_lse: bool = False, n_splits: int = 1,
+                         workspace=None):
     """kind 0: q [B,Hq,D] over the window of the caches keys/vals [B,Lmax,Hkv,D];
-    kind 1: over the complete blocks of the bf16 block means [B,Lmax/block,Hkv,D]."""
+    kind 1: over the complete blocks of the bf16 block means [B,Lmax/block,Hkv,D].
+    n_splits > 1 needs a zero-filled workspace (allocated here, zeroed, when not given)."""
     torch = _torch()
     _dev(q, "q"); _dev(keys, "keys", q.dtype); _dev(vals, "vals", q.dtype)
     _dev(lens, "lens", torch.int32)
@@ -456,9 +464,16 @@ def sa_nsa_decode_branch(q, keys, vals, lens, kind: int, block: int, window: int
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if n_splits > 1:
+        if workspace is None:
+            workspace = torch.zeros(max(sa_nsa_decode_branch_workspace(B, Hq, Hkv, D, n_splits),
+                                        256), dtype=torch.uint8, device=q.device)
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().sa_nsa_decode_branch(_p(q), _p(keys), _p(vals), _p(lens), B, Lrows, Hq, Hkv, D,
                                     kind, block, window, float(scale), _dtype_code(q), _p(out),
-                                    _p(lse), _stream(q.device))
+                                    _p(lse), n_splits, _p(workspace), ws_bytes, _stream(q.device))
     _check("sa_nsa_decode_branch", rc)
     return (out, lse) if want_lse else out
 

@@ -22,8 +22,10 @@
 //    the row's index list (ascending, -1 padded) for sa_sparse_attn_fwd.
 //  * nsa_decode_range<D>: decode attention of each sequence's query over one contiguous
 //    row range of a bf16 cache: the window of the token cache, or the complete blocks of
-//    the pooled cache (the compressed branch); 8 wavefronts per (sequence, KV head), merged
-//    by log-sum-exp in LDS.  The selected branch of decode is sa_sparse_decode with window 0.
+//    the pooled cache (the compressed branch); per (sequence, KV head) n_splits workgroups
+//    of 8 wavefronts, each taking a share of the range's 32-row tiles, merged by
+//    log-sum-exp in LDS; with several splits each publishes its partial with agent-scope
+//    stores and the last one (a counter) merges them.  The selected branch of decode is sa_sparse_decode with window 0.
 //  * nsa_combine: O = g0 * O_cmp + g1 * O_slc + g2 * O_win, 8 elements per thread.
 #include "attn_tile.h"
 #include "sa_launch.h"
@@ -372,24 +374,32 @@ __global__ __launch_bounds__(64 * kRangeWaves) void nsa_decode_range(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ keys,
     const uint16_t* __restrict__ vals, const int32_t* __restrict__ lens, int B, int Lrows,
     int Hq, int Hkv, int kind, int block, int window, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int n_splits,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
   using GA = GroupAttn<D>;
+  constexpr int PS = D + 4;  // floats per (split, head) partial: o[D], m, l, 2 pad
   __shared__ __attribute__((aligned(16))) unsigned char vl[kRangeWaves][GA::LDS_BYTES];
+  __shared__ int last;
   __shared__ float pacc[kRangeWaves][16][D];  // unnormalised O per wave and head
   __shared__ float pm[kRangeWaves][16], pl[kRangeWaves][16];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, grp = lane >> 4;
-  const int b = (int)blockIdx.x / Hkv, g = (int)blockIdx.x % Hkv;
+  const int bg = (int)blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int split = (int)blockIdx.y;
   const int G = Hq / Hkv;
   const int h = g * G + n;
   const bool hv = n < G;
   const int L = lens[b];
   const int lo = kind == 0 ? max(0, L - window) : 0;
   const int hi = kind == 0 ? L : L / block;
-  const int ntiles = (hi - lo + 31) / 32;
-  const int per = (ntiles + kRangeWaves - 1) / kRangeWaves;
-  const int tb = min(ntiles, wv * per), te = min(ntiles, tb + per);
+  // tiles of the range: this split's share, then this wavefront's share of that
+  const int ntiles_all = (hi - lo + 31) / 32;
+  const int ps = (ntiles_all + n_splits - 1) / n_splits;
+  const int sb = min(ntiles_all, split * ps), se = min(ntiles_all, sb + ps);
+  const int per = (se - sb + kRangeWaves - 1) / kRangeWaves;
+  const int tb = min(se, sb + wv * per), te = min(se, tb + per);
 
   GA ga;
   ga.init(hv ? q + ((int64_t)b * Hq + h) * D : nullptr, grp);
@@ -432,25 +442,103 @@ __global__ __launch_bounds__(64 * kRangeWaves) void nsa_decode_range(
       }
     }
     const int64_t oh = (int64_t)b * Hq + g * G + hh;
+    if (n_splits == 1) {
+      out[oh * D + d] = (uint16_t)f32_to_bf16_bits(lsum > 0.f ? o / lsum : 0.f);
+      if (lse && d == 0) lse[oh] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+      continue;
+    }
+    // this split's partial, with agent-scope stores that go to the memory side
+    float* pp = partials + (((int64_t)bg * n_splits + split) * G + hh) * PS;
+    __hip_atomic_store(pp + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(pp + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pp + D + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (n_splits == 1) return;
+
+  // ---- the last split of this (sequence, KV head) merges all splits
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&counters[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)(n_splits - 1);
+  __syncthreads();
+  if (!last) return;
+  const float* pb = partials + (int64_t)bg * n_splits * G * PS;
+  auto ald = [](const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int e = threadIdx.x; e < G * D; e += 64 * kRangeWaves) {
+    const int hh = e / D, d = e % D;
+    float M = -INFINITY, lsum = 0.f, o = 0.f;
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {  // 8 splits' loads in flight, online rescale
+      float ms[8], ls[8], os[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ms[u] = -INFINITY;
+        ls[u] = 0.f;
+        os[u] = 0.f;
+        if (s0 + u < n_splits) {
+          const float* ps2 = pb + ((int64_t)(s0 + u) * G + hh) * PS;
+          ms[u] = ald(ps2 + D);
+          ls[u] = ald(ps2 + D + 1);
+          os[u] = ald(ps2 + d);
+        }
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, ms[u]);
+      if (Mn > -INFINITY) {
+        const float a = exp2f(M - Mn);  // 0 while M is -inf
+        lsum *= a;
+        o *= a;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float f = exp2f(ms[u] - Mn);  // 0 for empty splits
+          lsum += f * ls[u];
+          o += f * os[u];
+        }
+        M = Mn;
+      }
+    }
+    const int64_t oh = (int64_t)b * Hq + g * G + hh;
     out[oh * D + d] = (uint16_t)f32_to_bf16_bits(lsum > 0.f ? o / lsum : 0.f);
     if (lse && d == 0) lse[oh] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
+  if (threadIdx.x == 0) __hip_atomic_store(&counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+size_t nsa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int n_splits) {
+  const size_t G = (size_t)(Hq / Hkv);
+  const size_t part = ((size_t)B * Hkv * n_splits * G * (D + 4) * 4 + 255) / 256 * 256;
+  return part + ((size_t)B * Hkv * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_nsa_decode_range(const void* q, const void* keys, const void* vals,
                                    const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D,
                                    int kind, int block, int window, float scale, void* out,
-                                   float* lse, hipStream_t st) {
-  const dim3 grid((unsigned)(B * Hkv));
+                                   float* lse, int n_splits, void* workspace, hipStream_t st) {
+  const dim3 grid((unsigned)(B * Hkv), (unsigned)n_splits);
   const float sl2 = scale * 1.4426950408889634f;
+  float* partials = nullptr;
+  uint32_t* counters = nullptr;
+  if (n_splits > 1) {
+    const size_t G = (size_t)(Hq / Hkv);
+    const size_t part = ((size_t)B * Hkv * n_splits * G * (D + 4) * 4 + 255) / 256 * 256;
+    partials = static_cast<float*>(workspace);
+    counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + part);
+  }
   if (D == 128)
     hipLaunchKernelGGL(nsa_decode_range<128>, grid, dim3(64 * kRangeWaves), 0, st,
                        (const uint16_t*)q, (const uint16_t*)keys, (const uint16_t*)vals, lens, B,
-                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse);
+                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse, n_splits,
+                       partials, counters);
   else
     hipLaunchKernelGGL(nsa_decode_range<64>, grid, dim3(64 * kRangeWaves), 0, st,
                        (const uint16_t*)q, (const uint16_t*)keys, (const uint16_t*)vals, lens, B,
-                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse);
+                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse, n_splits,
+                       partials, counters);
   return hipGetLastError();
 }
 

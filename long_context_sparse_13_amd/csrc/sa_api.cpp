@@ -420,7 +420,7 @@ int sa_block_select(const void* q, const float* kbar, int B, int T, int Hq, int 
 int sa_nsa_decode_branch(const void* q, const void* keys, const void* vals,
                          const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D, int kind,
                          int block, int window, float scale, int dtype, void* out, float* lse,
-                         void* stream) {
+                         int n_splits, void* workspace, size_t ws_bytes, void* stream) {
   try {
     REQUIRE_PTR(q);
     REQUIRE_PTR(keys);
@@ -439,13 +439,29 @@ int sa_nsa_decode_branch(const void* q, const void* keys, const void* vals,
     SUPPORT(dtype == SA_BF16, "the decode branches take bf16 tensors (dtype=%d)", dtype);
     SUPPORT(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
     SUPPORT(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+    REQUIRE(n_splits >= 1 && n_splits <= 64, "n_splits must be in [1, 64] (got %d)", n_splits);
+    if (n_splits > 1) {
+      const size_t need = sa::nsa_decode_workspace_bytes(B, Hq, Hkv, D, n_splits);
+      if (!workspace || ws_bytes < need)
+        return fail(SA_ERR_WORKSPACE,
+                    "sa_nsa_decode_branch: workspace of %zu bytes needed for %d splits (got %zu)",
+                    need, n_splits, workspace ? ws_bytes : (size_t)0);
+      REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    }
     return hip_status(sa::launch_nsa_decode_range(q, keys, vals, lens, B, Lrows, Hq, Hkv, D, kind,
-                                                  block, window, scale, out, lse,
-                                                  as_stream(stream)),
+                                                  block, window, scale, out, lse, n_splits,
+                                                  workspace, as_stream(stream)),
                       "sa_nsa_decode_branch launch");
   } catch (...) {
     return fail(SA_ERR_INTERNAL, "sa_nsa_decode_branch: unexpected exception");
   }
+}
+
+size_t sa_nsa_decode_branch_workspace(int B, int Hq, int Hkv, int D, int n_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) || n_splits < 1 ||
+      n_splits > 64)
+    return 0;
+  return sa::nsa_decode_workspace_bytes(B, Hq, Hkv, D, n_splits);
 }
 
 int sa_nsa_combine(const void* o_cmp, const void* o_slc, const void* o_win, const float* gates,

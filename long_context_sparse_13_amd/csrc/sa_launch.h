@@ -92,7 +92,8 @@ hipError_t launch_block_select(const void* q, const float* kbar, int B, int T, i
 hipError_t launch_nsa_decode_range(const void* q, const void* keys, const void* vals,
                                    const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D,
                                    int kind, int block, int window, float scale, void* out,
-                                   float* lse, hipStream_t st);
+                                   float* lse, int n_splits, void* workspace, hipStream_t st);
+size_t nsa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int n_splits);
 hipError_t launch_nsa_combine(const void* oc, const void* os, const void* ow, const float* gates,
                               int B, int T, int Hq, int D, void* out, hipStream_t st);
 

@@ -191,11 +191,17 @@ def test_nsa_validation(L):
     assert m(P, P, P, P, 1, 64, 16, 12, 1, P, None) == 1                           # D % 8
     assert m(P, P, None, P, 1, 64, 16, 128, 1, P, None) == 1
     d = L.sa_nsa_decode_branch
-    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 2, 64, 512, 0.1, 1, P, None, None) == 1   # kind
-    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, -1, 0.1, 1, P, None, None) == 1    # window
-    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 0, P, None, None) == 2   # f32
-    assert d(P, P, P, P, 2, 1024, 16, 1, 96, 0, 64, 512, 0.1, 1, P, None, None) == 2    # D
-    assert d(P, P, P, None, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, None) == 1
+    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 2, 64, 512, 0.1, 1, P, None, 1, None, 0, None) == 1   # kind
+    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, -1, 0.1, 1, P, None, 1, None, 0, None) == 1    # window
+    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 0, P, None, 1, None, 0, None) == 2   # f32
+    assert d(P, P, P, P, 2, 1024, 16, 1, 96, 0, 64, 512, 0.1, 1, P, None, 1, None, 0, None) == 2    # D
+    assert d(P, P, P, None, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, 1, None, 0, None) == 1
+    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, 0, None, 0, None) == 1   # splits
+    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, 65, None, 0, None) == 1
+    wsd = L.sa_nsa_decode_branch_workspace(2, 16, 1, 128, 4)
+    assert wsd > 0 and L.sa_nsa_decode_branch_workspace(2, 16, 1, 96, 4) == 0
+    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, 4, None, 0, None) == 3   # no workspace
+    assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, 4, P, wsd - 1, None) == 3
     mb = L.sa_block_meanpool_bf16
     assert mb(P, P, 1, 1024, 1, 128, 48, 1, P, None) == 1                              # block
     assert mb(P, P, 1, 1024, 1, 128, 64, 2, P, None) == 2                              # E4M3

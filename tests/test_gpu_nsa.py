@@ -185,3 +185,40 @@ def test_nsa_decode_vs_oracle(Hq, Hkv, D, block, top, W):
     assert np.abs(host(osl) - ws_).max() < BF16_TOL
     assert np.abs(host(out) - want).max() < BF16_TOL
     assert not host(oc)[3].any()  # one token: no complete block
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 1), (64, 8, 2)])
+def test_nsa_decode_branch_splits(D, Hq, Hkv):
+    """Both decode range branches with the range split over several workgroups (partials
+    merged by log-sum-exp, the last split merging) against the oracle, lse included, on
+    ragged lengths (the 1-token sequence has no complete block: out 0, lse -inf), twice on
+    one workspace (the counters return to zero)."""
+    import torch
+    block, W = 32, 300
+    lens_h = [1500, 999, 64, 1]
+    x = sa_synth.decode_inputs(871 + D, 4, 1500, Hq, Hkv, D, "bf16", lens=lens_h)
+    scale = D ** -0.5
+    q, kc, vc = dev(x["q"], "bf16"), dev(x["kcache"], "bf16"), dev(x["vcache"], "bf16")
+    lens = dev(np.asarray(lens_h, np.int32), "i32")
+    kb16 = sa.sa_block_meanpool_bf16(kc, lens, block)
+    vb16 = sa.sa_block_meanpool_bf16(vc, lens, block)
+    gates = np.zeros((4, Hq, 3), np.float32)
+    _, (wc, _, ww), _ = orc.nsa_decode(x["q"], x["kcache"], x["vcache"], np.asarray(lens_h),
+                                       gates, block, 1, W, scale)
+    for ns in (2, 5, 7):
+        ws = torch.zeros(sa.sa_nsa_decode_branch_workspace(4, Hq, Hkv, D, ns), dtype=torch.uint8,
+                         device="cuda")
+        for rep in range(2):
+            note(f"nsa decode branches, {ns} splits, D={D} Hq={Hq} Hkv={Hkv}, call {rep}")
+            oc, lc = sa.sa_nsa_decode_branch(q, kb16, vb16, lens, 1, block, W, scale, want_lse=True,
+                                             n_splits=ns, workspace=ws)
+            ow, lw = sa.sa_nsa_decode_branch(q, kc, vc, lens, 0, block, W, scale, want_lse=True,
+                                             n_splits=ns, workspace=ws)
+            o1, l1 = sa.sa_nsa_decode_branch(q, kb16, vb16, lens, 1, block, W, scale, want_lse=True)
+            assert np.abs(host(oc) - wc).max() < BF16_TOL
+            assert np.abs(host(ow) - ww).max() < BF16_TOL
+            assert not host(oc)[3].any() and np.isneginf(host(lc)[3]).all()
+            assert np.abs(host(lc)[:3] - host(l1)[:3]).max() < 1e-4
+            # the per-(sequence, KV head) counters after the partials are back at zero
+            part = (4 * Hkv * ns * (Hq // Hkv) * (D + 4) * 4 + 255) // 256 * 256
+            assert not bool(ws[part: part + 4 * Hkv * 4].any())

@@ -56,10 +56,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void c
     const uint16_t* __restrict__ vb, int B, int T, int Hq, int Hkv, int nb, int block,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int KS = D / 32, DT = D / 16, CH = D * 2 / 16;  // 16-byte chunks per row
-  constexpr int LROW = D * 2 + 16;                          // padded LDS row (bytes)
+  constexpr int LROW = D * 2 + 16;                          // padded LDS row of K (bytes)
+  constexpr int VP = 72;  // bytes per V^T row (32 keys of one feature, 8 bytes of pad)
   constexpr int TPG = 8;                                    // tokens per workgroup
   __shared__ __attribute__((aligned(16))) unsigned char kt[32 * LROW];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[32 * LROW];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[D * VP];  // V^T [d][key]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int ntg = (T + TPG - 1) / TPG;
@@ -109,16 +110,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void c
   };
   if (ntiles > 0) ldtile(0);
 
-  const unsigned char* vrow[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (j < 4) ? grp * 4 + j : 16 + grp * 4 + (j - 4);
-    vrow[j] = vt + r * LROW + n * 2;
-  }
   for (int tile = 0; tile < ntiles; ++tile) {
     if (ldr) {
       st16(kt + r_ld * LROW + c_ld * 16, kr);
-      st16(vt + r_ld * LROW + c_ld * 16, vr);
+      // V transposed: value q of this thread's chunk is feature 8 c + q of key r; the order
+      // is rotated by the chunk so that a wavefront's lanes write distinct LDS banks
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int qv = (k + c_ld) & 7;
+        const uint32_t w01 = (qv & 2) ? vr[1] : vr[0];
+        const uint32_t w23 = (qv & 2) ? vr[3] : vr[2];
+        const uint32_t wv = (qv & 4) ? w23 : w01;
+        *reinterpret_cast<uint16_t*>(vt + (c_ld * 8 + qv) * VP + r_ld * 2) =
+            (uint16_t)((qv & 1) ? (wv >> 16) : (wv & 0xffffu));
+      }
     }
     __syncthreads();
     if (tile + 1 < ntiles) ldtile(tile + 1);  // in flight while this tile is used
@@ -167,18 +172,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void c
       const u32x4 pw = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                         pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
       const bf16x8 pB = as_bf16x8(pw);
-      // ---- O^T += V^T . P^T (V^T read transposed from LDS)
+      // ---- O^T += V^T . P^T: the lane's reduction slots (grp, j) are keys grp*4 + j and
+      // 16 + grp*4 + j - 4, two runs of 4 keys of feature row dt*16 + n of V^T
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        uint32_t a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(vrow[2 * j] + dt * 32);
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(vrow[2 * j + 1] + dt * 32);
-          a[j] = lo | (hi << 16);
-        }
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{a[0], a[1], a[2], a[3]}),
-                                                          pB, acc[dt], 0, 0, 0);
+        const unsigned char* vrow = vt + (dt * 16 + n) * VP;
+        const u32x2 a0 = ld8(vrow + grp * 8);
+        const u32x2 a1 = ld8(vrow + 32 + grp * 8);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}), pB, acc[dt], 0, 0, 0);
       }
     }
     __syncthreads();  // the tile's LDS rows are rewritten next

@@ -212,6 +212,26 @@ def sparse_attn(q, k, v, idx, window: int, scale: float, rows=None):
     return O, LSE
 
 
+def sparse_attn_row(q_row, k_seq, v_seq, idx_row, t: int, window: int, scale: float):
+    """One row of ``sparse_attn`` from explicit arrays: q_row [Hq, D] (the queries of row t),
+    k_seq, v_seq [>= t+1, Hkv, D] (the sequence's keys and values), idx_row (its listed
+    positions).  Returns (O [Hq, D], LSE [Hq]); the same dense masked softmax, for checks at
+    sizes where whole query tensors do not fit the host."""
+    Hq = q_row.shape[0]
+    Hkv = k_seq.shape[1]
+    G = Hq // Hkv
+    mask = selected_mask_row(t, idx_row, window)
+    O = np.zeros((Hq, q_row.shape[1]))
+    LSE = np.zeros(Hq)
+    for g in range(Hkv):
+        qh = _f64(q_row[g * G:(g + 1) * G])
+        logits = scale * np.matmul(qh, _f64(k_seq[: t + 1, g]).T)
+        o, lse = _masked_softmax_attend(logits, mask, _f64(v_seq[: t + 1, g]))
+        O[g * G:(g + 1) * G] = o
+        LSE[g * G:(g + 1) * G] = lse
+    return O, LSE
+
+
 def sparse_attn_bwd(q, k, v, idx, window: int, scale: float, dout):
     """Gradients of ``sparse_attn`` with respect to q, k and v for the upstream gradient
     dout [B,T,Hq,D], on the same mask: with P[t,h,s] = softmax_s over S_t and

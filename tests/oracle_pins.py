@@ -536,6 +536,19 @@ def pin_attn_bwd_finite_differences(orc):
             assert abs((up - dn) / (2 * eps) - grad[pos]) < 1e-7, (which, pos)
 
 
+def pin_attn_row_form(orc):
+    """The single-row form (explicit query row, key/value sequence, index row) equals the
+    batched attention row by row, GQA with two groups, junk and in-window indices."""
+    B, T, Hq, Hkv, D, k, W = 2, 37, 4, 2, 8, 5, 3
+    x = sa_synth.attn_inputs(101, B, T, Hq, Hkv, D, "f32")
+    idx = sa_synth.random_topk_idx(102, B, T, k, junk=True)
+    O, L = orc.sparse_attn(x["q"], x["k"], x["v"], idx, W, 0.3)
+    for b in range(B):
+        for t in (0, 1, 4, 20, 36):
+            o, l = orc.sparse_attn_row(x["q"][b, t], x["k"][b], x["v"][b], idx[b, t], t, W, 0.3)
+            assert np.abs(o - O[b, t]).max() < 1e-12 and np.abs(l - L[b, :, t]).max() < 1e-12
+
+
 def pin_attn_bwd_sampled_rows_and_keys(orc):
     """The sampled forms (dQ of chosen rows over S_t only; dK and dV of chosen keys summed
     over the rows that hold them) equal the full backward on a case with two sequences,

@@ -121,3 +121,31 @@ def test_row_ranges(dtype, G):
     O, _ = orc.sparse_attn(x["q"], x["k"], x["v"], idx, W, 0.125, rows)
     tol = BF16_TOL if dtype == "bf16" else F32_TOL
     assert np.abs(host(out)[:, rows] - O).max() <= tol
+
+
+@pytest.mark.slow
+def test_mfma_offsets_beyond_32_bits():
+    """T = 2^21 + 5 tokens with 16 query heads of dim 128: query, output and index offsets
+    pass 2^32 elements (bytes for idx); sampled rows (early, middle, late, last) against the
+    oracle's single-row form.  Inputs are drawn on the GPU (seeded), listed keys are distinct
+    positions spread over [0, t - W - 1]."""
+    import torch
+    T, Hq, Hkv, D, topk, W = (1 << 21) + 5, 16, 1, 128, 64, 32
+    note(f"sparse_attn T={T} Hq={Hq} D={D} topk={topk} W={W} (offsets past 2^32)")
+    g = torch.Generator(device="cuda").manual_seed(181)
+    q = torch.randn((1, T, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    t = torch.arange(T, device="cuda")[:, None]
+    j = torch.arange(topk, device="cuda")[None, :]
+    key = t - W - 1 - j * torch.clamp((t - W) // (topk + 1), min=1)
+    idx = torch.where(key >= 0, key, -1).to(torch.int32)[None].contiguous()
+    del t, j, key
+    scale = D ** -0.5
+    out, lse = sa.sa_sparse_attn_fwd(q, k, v, idx, W, scale, return_lse=True)
+    assert (1 * T * Hq * D) > (1 << 32)
+    kh, vh = host(k)[0], host(v)[0]
+    for r in (0, 100, 70000, T // 2 + 3, T - 2, T - 1):
+        o, l = orc.sparse_attn_row(host(q[0, r]), kh, vh, host(idx[0, r]), r, W, scale)
+        assert np.abs(host(out[0, r]) - o).max() <= BF16_TOL, r
+        assert np.abs(host(lse[0, :, r]) - l).max() <= 2e-3, r

@@ -15,6 +15,9 @@
 // The reduction (K) slot (grp, j) of the P.V product is mapped to the key
 // kmap(grp, j) = grp*4 + j (j < 4) or 16 + grp*4 + j - 4 (j >= 4): exactly the keys
 // whose scores the lane already holds from the two S^T tiles, so P needs no shuffle.
+// The V^T operand of a d tile is two transposing LDS reads of the row-major staged V
+// rows (keys grp*4 .. grp*4+3, then 16 + grp*4 ..); a row pitch of 2D + 32 bytes puts the
+// 8 rows read by each half wavefront on distinct banks.
 #pragma once
 
 #include "sa_device.h"
@@ -26,7 +29,7 @@ struct GroupAttn {
   static constexpr int KS = D / 32;        // 32-wide k-steps of Q.K
   static constexpr int DT = D / 16;        // 16-wide d tiles of the output
   static constexpr int CH = D * 2 / 16;    // 16-byte chunks per bf16 row
-  static constexpr int LROW = D * 2 + 16;  // LDS bytes per staged V row (padded)
+  static constexpr int LROW = D * 2 + 32;  // LDS bytes per staged V row (padded)
   static constexpr int LDS_BYTES = 32 * LROW;
 
   bf16x8 qB[KS];
@@ -132,11 +135,11 @@ struct GroupAttn {
     mt = fmaxf(mt, shfl_xor_f(mt, 16));
     mt = fmaxf(mt, shfl_xor_f(mt, 32));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = exp2_hw(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      x[j] = exp2f(x[j] - m_new);
+      x[j] = exp2_hw(x[j] - m_new);
       psum += x[j];
     }
     l_run = l_run * alpha + psum;
@@ -152,23 +155,14 @@ struct GroupAttn {
 
     wave_lds_sync();  // V rows written by other lanes are visible
 
-    // ---- O^T += V^T . P^T
-    const unsigned char* vrow[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = (j < 4) ? grp * 4 + j : 16 + grp * 4 + (j - 4);
-      vrow[j] = vl + r * LROW + n * 2;
-    }
+    // ---- O^T += V^T . P^T; lane (n, grp) names row grp*4 + n/4 (then 16 + grp*4 + n/4),
+    // columns dt*16 + 4*(n%4) .. +3, and receives V[kmap(grp, j)][dt*16 + n], j = 0..7
+    const unsigned char* tr = vl + (grp * 4 + (n >> 2)) * LROW + (n & 3) * 8;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      uint32_t a[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(vrow[2 * j] + dt * 32);
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(vrow[2 * j + 1] + dt * 32);
-        a[j] = lo | (hi << 16);
-      }
-      const u32x4 aw = {a[0], a[1], a[2], a[3]};
+      const u32x2 lo = lds_read_tr16(tr + dt * 32);
+      const u32x2 hi = lds_read_tr16(tr + 16 * LROW + dt * 32);
+      const u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw), pB, acc[dt], 0, 0, 0);
     }
 

@@ -89,8 +89,8 @@ __global__ __launch_bounds__(64) void graph_attn(const void* __restrict__ cq,
       }
     }
     const float mn = fmaxf(m, lg);
-    const float al = exp2f(m - mn);
-    const float p = exp2f(lg - mn);
+    const float al = exp2_hw(m - mn);
+    const float p = exp2_hw(lg - mn);
     l = l * al + p;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = acc[i] * al + p * vv[i];
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
 #pragma unroll
   for (int i = 0; i < kGLoc; ++i) {
     if (lb[i] != -INFINITY) {
-      const float p = exp2f(lb[i] - mx);
+      const float p = exp2_hw(lb[i] - mx);
       const uint32_t pbits = f32_to_bf16_bits(p);
       sum += bf16_to_f32((uint16_t)pbits);
       sume += p;
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
   float pfar[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    pfar[u] = lf[u] != -INFINITY ? exp2f(lf[u] - mx) : 0.f;
+    pfar[u] = lf[u] != -INFINITY ? exp2_hw(lf[u] - mx) : 0.f;
     sum += pfar[u];
     sume += pfar[u];
   }

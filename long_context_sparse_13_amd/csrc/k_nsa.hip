@@ -156,11 +156,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void c
       mt = fmaxf(mt, shfl_xor_f(mt, 16));
       mt = fmaxf(mt, shfl_xor_f(mt, 32));
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = exp2_hw(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        x[j] = exp2f(x[j] - m_new);
+        x[j] = exp2_hw(x[j] - m_new);
         psum += x[j];
       }
       l_run = l_run * alpha + psum;

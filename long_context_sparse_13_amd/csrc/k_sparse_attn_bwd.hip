@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
       for (int i = 0; i < 4; ++i) {
         const int sk = c2 * 16 + grp * 4 + i;
         const bool on = hv && ((vm >> sk) & 1u);
-        const float p = on ? exp2f(s[c2][i] * scale_log2 - lse2) : 0.f;
+        const float p = on ? exp2_hw(s[c2][i] * scale_log2 - lse2) : 0.f;
         pv[c2 * 4 + i] = p;
         dsv[c2 * 4 + i] = p * (dp[c2][i] - delta);
         pl[sk][n] = (uint16_t)f32_to_bf16_bits(p);

@@ -45,6 +45,23 @@ __device__ __forceinline__ int ld_nt(const int* p) { return __builtin_nontempora
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950).  Every lane names 8 bytes (four
+// 16-bit values); within each block of 16 lanes, lane i receives, for j = 0..3, value
+// i % 4 of the 8 bytes named by lane 4j + i / 4 of the same block (layout checked on the
+// device).  So if lane 4j + q names row j, columns 4q..4q+3 of a 16-bit matrix, lane i
+// receives column i of rows 0..3.  p must point into LDS, 8-byte aligned.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)const_cast<void*>(p)));
+}
+
+// 2^x on the hardware's exponential unit (one v_exp_f32, about 1 ulp).  The library's
+// exp2f adds a rescaling step so that results below 2^-126 come out as denormals; the
+// softmax weights never need those (they are below 2^-126 of the row maximum).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- cross-lane
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ int shfl_i(int v, int src) { return __shfl(v, src, kWave); }

@@ -24,7 +24,10 @@
 
 namespace sa {
 
-template <int D>
+// OFS32: every row this wavefront reads lies less than 4 GB past kbase / vbase, so row
+// addresses are a wave-uniform base plus a 32-bit byte offset (the loads' scalar-base
+// form, slightly cheaper for the memory pipeline than 64-bit per-lane addresses).
+template <int D, bool OFS32 = false>
 struct GroupAttn {
   static constexpr int KS = D / 32;        // 32-wide k-steps of Q.K
   static constexpr int DT = D / 16;        // 16-wide d tiles of the output
@@ -74,10 +77,14 @@ struct GroupAttn {
       const int kr = shfl_i(key, slot);
       const bool ok = (vm >> slot) & 1u;
       const uint16_t* kp = kbase + (int64_t)kr * stride + grp * 8;
+      const uint32_t kofs = (uint32_t)kr * ((uint32_t)stride * 2u) + grp * 16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (ok) w = ld16(kp + ks * 32);
+        if (ok) {
+          if constexpr (OFS32) w = ld16(reinterpret_cast<const char*>(kbase) + (kofs + ks * 64));
+          else w = ld16(kp + ks * 32);
+        }
         tl.kA[c2][ks] = w;
       }
     }
@@ -88,7 +95,12 @@ struct GroupAttn {
       const int c = lane % CH;
       const int vr = shfl_i(key, r);
       u32x4 w = {0u, 0u, 0u, 0u};
-      if ((vm >> r) & 1u) w = ld16(vbase + (int64_t)vr * stride + c * 8);
+      if ((vm >> r) & 1u) {
+        if constexpr (OFS32)
+          w = ld16(reinterpret_cast<const char*>(vbase) +
+                   ((uint32_t)vr * ((uint32_t)stride * 2u) + c * 16));
+        else w = ld16(vbase + (int64_t)vr * stride + c * 8);
+      }
       tl.vw[i] = w;
     }
   }

@@ -7,11 +7,14 @@
 // of a KV group.
 //
 // Two kernels:
-//  * sparse_attn_mfma<D>: bf16, up to 16 query heads per KV head.  One wavefront per
-//    (batch, token, KV head); keys are streamed 32 at a time through GroupAttn (MFMA
+//  * sparse_attn_mfma<D, OFS32>: bf16, up to 16 query heads per KV head.  One wavefront
+//    per (batch, token, KV head); keys are streamed 32 at a time through GroupAttn (MFMA
 //    over the grouped heads, online softmax).  Held to 3 wavefronts per SIMD (<= 168
-//    registers): the kernel is bound by gathered-row latency, so more resident
-//    wavefronts beat a deeper per-wavefront pipeline.  Q and the index row are read
+//    registers).  The kernel is bound by the vector memory pipeline (the texture
+//    addresser is ~80 % busy; with every gathered row an L2 hit it runs ~15 % faster, and
+//    halving its VALU instructions gains nothing), so more resident wavefronts beat a
+//    deeper per-wavefront pipeline, and OFS32 (one KV head's rows of a batch within
+//    4 GB) addresses rows as a uniform base plus a 32-bit offset.  Q and the index row are read
 //    with non-temporal loads so they do not evict gathered K/V rows (O is written with
 //    ordinary stores, which L2 combines into whole lines).  The listed indices are visited first
 //    (positions inside the window or outside [0, t] are masked out, so each key is
@@ -24,13 +27,13 @@
 
 namespace sa {
 
-template <int D>
+template <int D, bool OFS32>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int B, int T, int Hq,
     int Hkv, int topk, int window, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int r0, int nrows) {
-  using GA = GroupAttn<D>;
+  using GA = GroupAttn<D, OFS32>;
   __shared__ __attribute__((aligned(16))) unsigned char vl[GA::LDS_BYTES];
 
   const int lane = threadIdx.x;
@@ -212,14 +215,15 @@ hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, c
   const dim3 grid((unsigned)xcd_grid((int64_t)B * nrows * Hkv));
   const dim3 block(64);
   if (bf16 && G <= 16) {
-    if (D == 128)
-      hipLaunchKernelGGL(sparse_attn_mfma<128>, grid, block, 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, idx, B, T, Hq, Hkv, topk, window,
-                         sl2, (uint16_t*)out, lse, row_begin, nrows);
-    else
-      hipLaunchKernelGGL(sparse_attn_mfma<64>, grid, block, 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, idx, B, T, Hq, Hkv, topk, window,
-                         sl2, (uint16_t*)out, lse, row_begin, nrows);
+    // 32-bit row offsets when one KV head's rows of a batch span less than 4 GB
+    const bool ofs32 = (int64_t)T * Hkv * D * 2 < (int64_t)UINT32_MAX;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint16_t*)q, (const uint16_t*)k,
+                         (const uint16_t*)v, idx, B, T, Hq, Hkv, topk, window, sl2,
+                         (uint16_t*)out, lse, row_begin, nrows);
+    };
+    if (D == 128) ofs32 ? go(sparse_attn_mfma<128, true>) : go(sparse_attn_mfma<128, false>);
+    else ofs32 ? go(sparse_attn_mfma<64, true>) : go(sparse_attn_mfma<64, false>);
   } else if (bf16) {
     if (D == 128)
       hipLaunchKernelGGL((sparse_attn_valu<128, true>), grid, block, 0, st, q, k, v, idx, B, T, Hq,

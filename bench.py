@@ -96,9 +96,9 @@ def write_traffic(base: str) -> dict:
     ff = 1048576.0 / max(vals(fa, fn, fg, "copyBuffer"))
     wf = 1048576.0 / max(vals(wa, wn, wg, "copyBuffer"))
     # the full 64K attention launches
-    af = statistics.mean(vals(fa, fn, fg, "sparse_attn_mfma<128>", True))
-    aw = statistics.mean(vals(wa, wn, wg, "sparse_attn_mfma<128>", True))
-    t = {"kernel": "sparse_attn_mfma<128>", "workload": "dsa-prefill-bf16-64k",
+    af = statistics.mean(vals(fa, fn, fg, "sparse_attn_mfma<128, true>", True))
+    aw = statistics.mean(vals(wa, wn, wg, "sparse_attn_mfma<128, true>", True))
+    t = {"kernel": "sparse_attn_mfma<128, true>", "workload": "dsa-prefill-bf16-64k",
          "source_sha256": attn_sources_hash(), "fetch_kib_per_launch": af,
          "write_kib_per_launch": aw, "fetch_factor": ff, "write_factor": wf,
          "bytes_per_launch": af * 1024 * ff + aw * 1024 * wf,
@@ -351,7 +351,7 @@ def main():
         "sparse_attn_query_tokens_per_s": T / (attn_avg_ms * 1e-3) if attn_n else None,
         "two_streams": two_streams,
         "roofline": {
-            "kernel": "sparse_attn_mfma<128>",
+            "kernel": "sparse_attn_mfma<128, true>",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void indexer_mfma(const uint8_t* __restrict__ 
   const int t_last = min(t0 + IW::ROWS, row_end) - 1;
   const int j_last = t_last >> sshift;               // last slot any row of the wave reads
   const int wave_chunks = j_last / chunk + 1;        // chunks that meet this wave's rows
+  if (group >= wave_chunks) return;                  // none of them is this workgroup's
   float* st = stage[wv];
 
   IW iw;

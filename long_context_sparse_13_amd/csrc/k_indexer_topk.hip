@@ -215,7 +215,10 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
   const int t0 = row_begin + strip * kIdxStrip + wv * IW::ROWS;
   if (t0 >= row_end) return;
   const int t_last = min(t0 + IW::ROWS, row_end) - 1;
-  if (t_last < k) return;  // every row of this wavefront keeps all its positions
+  // every row of this wavefront keeps all its positions, or no chunk meets its rows (the
+  // condition is wave-uniform; readfirstlane says so to the compiler, whose backend
+  // otherwise fails on this kernel)
+  if (__builtin_amdgcn_readfirstlane((int)(t_last < k || group > t_last / kIdxChunk))) return;
   const int wave_chunks = t_last / kIdxChunk + 1;
 
   IW iw;

@@ -149,3 +149,34 @@ def test_mfma_offsets_beyond_32_bits():
         o, l = orc.sparse_attn_row(host(q[0, r]), kh, vh, host(idx[0, r]), r, W, scale)
         assert np.abs(host(out[0, r]) - o).max() <= BF16_TOL, r
         assert np.abs(host(lse[0, :, r]) - l).max() <= 2e-3, r
+
+
+@pytest.mark.slow
+def test_mfma_row_offsets_beyond_4gb():
+    """T = 2^21 + 3 tokens with 8 KV heads of dim 128: one KV head's rows span more than
+    4 GB of bytes, so the kernel addresses rows with 64-bit offsets (below that it uses a
+    uniform base plus a 32-bit offset).  Sampled rows of the first and last KV head
+    against the oracle's single-row form on that head's keys and values.  Inputs are drawn
+    on the GPU (seeded), listed keys are distinct positions spread over [0, t - W - 1]."""
+    import torch
+    T, Hq, Hkv, D, topk, W = (1 << 21) + 3, 8, 8, 128, 32, 32
+    note(f"sparse_attn T={T} Hq={Hq} Hkv={Hkv} D={D} topk={topk} W={W} (row offsets past 4 GB)")
+    assert T * Hkv * D * 2 >= (1 << 32)
+    g = torch.Generator(device="cuda").manual_seed(183)
+    q = torch.randn((1, T, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    t = torch.arange(T, device="cuda")[:, None]
+    j = torch.arange(topk, device="cuda")[None, :]
+    key = t - W - 1 - j * torch.clamp((t - W) // (topk + 1), min=1)
+    idx = torch.where(key >= 0, key, -1).to(torch.int32)[None].contiguous()
+    del t, j, key
+    scale = D ** -0.5
+    out, lse = sa.sa_sparse_attn_fwd(q, k, v, idx, W, scale, return_lse=True)
+    for h in (0, Hkv - 1):  # query head h reads KV head h (one query head per group)
+        kh, vh = host(k[0, :, h:h + 1]), host(v[0, :, h:h + 1])
+        for r in ((0, 70001, T - 1) if h else (100, T // 2 + 1)):
+            o, l = orc.sparse_attn_row(host(q[0, r, h:h + 1]), kh, vh, host(idx[0, r]), r, W, scale)
+            assert np.abs(host(out[0, r, h]) - o[0]).max() <= BF16_TOL, (h, r)
+            assert abs(float(host(lse[0, h, r])) - l[0]) <= 2e-3, (h, r)
+        del kh, vh

@@ -17,8 +17,9 @@
 //     GroupAttn (MFMA over the grouped heads); the workgroup merges its wavefronts in LDS
 //     and the last workgroup of each (sequence, KV head) merges the splits.
 // The kernel boundary makes the candidates visible to kernel 2.  Inside kernel 2 the
-// split partials travel through agent-scope atomic stores/loads and one counter per
-// (sequence, KV head), avoiding a device-wide cache flush per workgroup.  The counters
+// split partials travel through 16-byte stores and loads with the cache policy of
+// agent-scope atomics (sc1) and one counter per (sequence, KV head), avoiding a
+// device-wide cache flush per workgroup.  The counters
 // return to zero at the end of every call.
 #include "attn_tile.h"
 #include "sa_launch.h"
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
 // slice of U = selected blocks' tokens before the window followed by the window, gives one
 // sub-slice to each wavefront, merges the wavefronts' partial softmaxes in LDS and
 // publishes the split's partial.  The last split to finish (a counter) merges all splits
-// into the output.  Partials are written and read with agent-scope atomic accesses, which
+// into the output.  Partials are written and read with the agent-scope (sc1) policy, which
 // go straight to the memory side, so no cache flush is needed between workgroups.
 template <int D, int W>
 __global__ __launch_bounds__(64 * W) void decode_split_attn(
@@ -436,14 +437,20 @@ __global__ __launch_bounds__(64 * W) void decode_split_attn(
         lse[(int64_t)b * Hq + g * G + hh] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
       continue;
     }
-    float* pp = partials + pbase + (int64_t)hh * PS;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __hip_atomic_store(pp + dd + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (dd == 0) {
-      __hip_atomic_store(pp + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pp + D + 1, lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // 16-byte stores with the cache policy of agent-scope atomic stores (sc1), so the
+    // partial is visible to the other splits' workgroups on any XCD
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(partials + pbase, 0, G * PS * 4, 0x00020000);
+    const uint32_t po = (uint32_t)(hh * PS + dd) * 4u;
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
+        prs, po, 0, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
+        prs, po + 16u, 0, kSc1);
+    if (dd == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(M), __float_as_uint(lt)}, prs,
+                                           (uint32_t)(hh * PS + D) * 4u, 0, kSc1);
   }
 
   if (n_splits == 1) return;
@@ -455,10 +462,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_attn(
            (uint32_t)(n_splits - 1);
   __syncthreads();
   if (!last) return;
-  const float* pb = partials + (int64_t)bg * n_splits * G * PS;
-  auto ald = [](const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      partials + (int64_t)bg * n_splits * G * PS, 0, n_splits * G * PS * 4, 0x00020000);
   for (int it = tid; it < G * (D / 4); it += 64 * W) {
     const int hh = it / (D / 4), dd = (it % (D / 4)) * 4;
     float M = -INFINITY, lt = 0.f;
@@ -470,12 +475,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_attn(
         ms[u] = -INFINITY;
         ls[u] = 0.f;
         os[u][0] = os[u][1] = os[u][2] = os[u][3] = 0.f;
-        if (s0 + u < n_splits) {
-          const float* ps = pb + ((int64_t)(s0 + u) * G + hh) * PS;
-          ms[u] = ald(ps + D);
-          ls[u] = ald(ps + D + 1);
+        if (s0 + u < n_splits) {  // loads with the agent-scope cache policy (sc1)
+          const uint32_t ps = (uint32_t)(((s0 + u) * G + hh) * PS) * 4u;
+          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(mrs, ps + D * 4, 0, kSc1);
+          const u32x4 ov = __builtin_amdgcn_raw_buffer_load_b128(mrs, ps + dd * 4, 0, kSc1);
+          ms[u] = __uint_as_float(ml[0]);
+          ls[u] = __uint_as_float(ml[1]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) os[u][i] = ald(ps + dd + i);
+          for (int i = 0; i < 4; ++i) os[u][i] = __uint_as_float(ov[i]);
         }
       }
       float Mn = M;

@@ -36,6 +36,10 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
+// Cache-policy operand of buffer loads and stores: sc1, the policy agent-scope atomic
+// accesses compile to on gfx950 (data written so is seen by workgroups on other XCDs).
+constexpr int kSc1 = 16;
+
 // Streaming (non-temporal) accesses for data touched once, so that it does not push
 // reused data (gathered K/V rows) out of the caches.
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {

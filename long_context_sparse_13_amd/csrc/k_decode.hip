@@ -232,9 +232,8 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
   // the group's query rows (G x D bf16, one 16-byte piece per thread) through LDS
   {
     const int pieces = G * D / 8;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (tid < pieces) x = ld16(q + ((int64_t)b * Hq + g * G) * D + tid * 8);
-    if (tid < pieces) *reinterpret_cast<u32x4*>(&qrows[tid * 8]) = x;
+    for (int pc = tid; pc < pieces; pc += kScoreThreads)
+      *reinterpret_cast<u32x4*>(&qrows[pc * 8]) = ld16(q + ((int64_t)b * Hq + g * G) * D + pc * 8);
   }
   __syncthreads();
   float qb[C];
@@ -285,8 +284,9 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
 // slice of U = selected blocks' tokens before the window followed by the window, gives one
 // sub-slice to each wavefront, merges the wavefronts' partial softmaxes in LDS and
 // publishes the split's partial.  The last split to finish (a counter) merges all splits
-// into the output.  Partials are written and read with the agent-scope (sc1) policy, which
-// go straight to the memory side, so no cache flush is needed between workgroups.
+// into the output.  Partials are written and read with the agent-scope (sc1) policy:
+// those accesses go straight to the memory side, so no cache flush is needed between
+// workgroups.
 template <int D, int W>
 __global__ __launch_bounds__(64 * W) void decode_split_attn(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,

@@ -181,52 +181,27 @@ struct GroupAttn {
     wave_lds_sync();  // the staging area may be overwritten by the next tile
   }
 
-  // Streams `ntiles` tiles with the loads of tile i+1 in flight while tile i is
-  // computed.  fetch(i) returns this lane's raw key of tile i (it may issue a load, which
-  // is started two tiles ahead); finish(i, raw, key, vm) turns it into the slot key and
+  // Streams `ntiles` tiles, one loaded and computed at a time (fewer registers, so more
+  // wavefronts per SIMD, which beats a deeper pipeline in each wavefront); empty tiles are
+  // skipped.  fetch(i) returns this lane's raw key of tile i (it may issue a load, which
+  // is started one tile ahead); finish(i, raw, key, vm) turns it into the slot key and
   // the tile's slot mask.
-  // With PIPE = false one tile is loaded and computed at a time (half the registers, so
-  // twice the wavefronts per SIMD).
-  template <bool PIPE, typename Fetch, typename Finish>
+  template <typename Fetch, typename Finish>
   __device__ __forceinline__ void run(int ntiles, Fetch&& fetch, Finish&& finish,
                                       const uint16_t* __restrict__ kbase,
                                       const uint16_t* __restrict__ vbase, int64_t stride,
                                       unsigned char* vl, float scale_log2, int lane) {
     if (ntiles <= 0) return;
-    if constexpr (!PIPE) {
-      Tile A;
-      int key;
-      uint32_t vm;
-      int r = fetch(0);
-      for (int i = 0; i < ntiles; ++i) {
-        finish(i, r, key, vm);
-        if (i + 1 < ntiles) r = fetch(i + 1);  // the next raw key is in flight meanwhile
-        if (vm == 0u) continue;
-        load(A, kbase, vbase, stride, key, vm, lane);
-        compute(A, vl, scale_log2, lane);
-      }
-      return;
-    }
-    Tile A, B;
+    Tile A;
     int key;
     uint32_t vm;
-    int r1 = ntiles > 1 ? fetch(1) : 0;
-    finish(0, fetch(0), key, vm);
-    load(A, kbase, vbase, stride, key, vm, lane);
-    for (int i = 0; i < ntiles; i += 2) {
-      const int r2 = i + 2 < ntiles ? fetch(i + 2) : 0;
-      if (i + 1 < ntiles) {
-        finish(i + 1, r1, key, vm);
-        load(B, kbase, vbase, stride, key, vm, lane);
-      }
+    int r = fetch(0);
+    for (int i = 0; i < ntiles; ++i) {
+      finish(i, r, key, vm);
+      if (i + 1 < ntiles) r = fetch(i + 1);  // the next raw key is in flight meanwhile
+      if (vm == 0u) continue;
+      load(A, kbase, vbase, stride, key, vm, lane);
       compute(A, vl, scale_log2, lane);
-      if (i + 1 >= ntiles) break;
-      r1 = i + 3 < ntiles ? fetch(i + 3) : 0;
-      if (i + 2 < ntiles) {
-        finish(i + 2, r2, key, vm);
-        load(A, kbase, vbase, stride, key, vm, lane);
-      }
-      compute(B, vl, scale_log2, lane);
     }
   }
 

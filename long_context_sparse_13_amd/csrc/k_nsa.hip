@@ -415,7 +415,7 @@ __global__ __launch_bounds__(64 * kRangeWaves) void nsa_decode_range(
     vm = (uint32_t)ballot(ok);
     key = ok ? raw : lo;
   };
-  ga.template run<false>(te - tb, fetch, finish, kbase, vbase, stride, vl[wv], scale_log2, lane);
+  ga.run(te - tb, fetch, finish, kbase, vbase, stride, vl[wv], scale_log2, lane);
 
   const float lt = ga.total_l();
   if (grp == 0) {

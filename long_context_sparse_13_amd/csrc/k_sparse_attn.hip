@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     vm = (uint32_t)ballot(ok);
     key = ok ? raw : 0;
   };
-  ga.template run<false>(n_idx + n_win, fetch, finish, kbase, vbase, stride, vl, scale_log2, lane);
+  ga.run(n_idx + n_win, fetch, finish, kbase, vbase, stride, vl, scale_log2, lane);
 
   const float l = ga.total_l();
   const float inv = l > 0.f ? 1.f / l : 0.f;

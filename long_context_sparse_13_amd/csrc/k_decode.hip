@@ -385,8 +385,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_attn(
     key = raw >= 0 ? raw : 0;
   };
   __syncthreads();  // the candidate area in vl[0] is reused as staging
-  ga.run((u_hi - u_lo + 31) / 32, fetch, finish, kbase, vbase, stride, vl[wv],
-                         scale_log2, lane);
+  ga.run((u_hi - u_lo + 31) / 32, fetch, finish, kbase, vbase, stride, vl[wv], scale_log2, lane);
 
   // ---- merge the wavefronts' partials in LDS (the staging areas are free now)
   const float lw = ga.total_l();

@@ -73,6 +73,12 @@ def test_split_count_invariance():
     assert np.abs(a - b).max() <= 2e-2 and np.abs(a - c).max() <= 2e-2
 
 
+def test_many_splits_mostly_empty():
+    # 64 splits (the limit) over |U| <= 4 blocks + 128 window tokens: most split workgroups
+    # get no tokens and publish an empty partial (max -inf, sum 0) that the merge must skip
+    _decode(607, 2, 1000, 16, 1, 128, 64, 4, 128, lens=[1000, 333], n_splits=64, reps=2)
+
+
 def test_splits_across_xcds():
     # 3 x 1 (sequence, KV head) pairs and 5 splits: a sequence's split workgroups land on
     # different XCDs, so the partials must travel through coherent memory

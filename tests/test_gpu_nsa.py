@@ -205,7 +205,7 @@ def test_nsa_decode_branch_splits(D, Hq, Hkv):
     gates = np.zeros((4, Hq, 3), np.float32)
     _, (wc, _, ww), _ = orc.nsa_decode(x["q"], x["kcache"], x["vcache"], np.asarray(lens_h),
                                        gates, block, 1, W, scale)
-    for ns in (2, 5, 7):
+    for ns in (2, 5, 7, 64):  # 64 (the limit): most splits of the short ranges are empty
         ws = torch.zeros(sa.sa_nsa_decode_branch_workspace(4, Hq, Hkv, D, ns), dtype=torch.uint8,
                          device="cuda")
         for rep in range(2):

@@ -142,6 +142,66 @@ def pin_topk_invariants(orc):
             assert row[sel].min() >= row[uns].max()
 
 
+def _boundary_by_counting(row, k):
+    """The k-th and (k+1)-th largest values by counting: the j-th largest value is the
+    largest v in the row with #{s : row[s] >= v} >= j.  None when the row has <= k
+    entries."""
+    vals = [float(v) + 0.0 for v in row]
+    if len(vals) <= k:
+        return None
+
+    def jth(j):
+        return max(v for v in vals if sum(1 for u in vals if u >= v) >= j)
+
+    return jth(k), jth(k + 1)
+
+
+def pin_topk_boundary_hand(orc):
+    """Hand-worked rows: the k-th and (k+1)-th largest scores (ties counted with their
+    multiplicity), None when there is no (k+1)-th."""
+    row = [3.0, 1.0, 3.0, 0.0, 2.0, 3.0, 0.0]
+    for k, want in ((1, (3.0, 3.0)), (2, (3.0, 3.0)), (3, (3.0, 2.0)), (4, (2.0, 1.0)),
+                    (5, (1.0, 0.0)), (6, (0.0, 0.0)), (7, None), (9, None)):
+        got = orc.topk_boundary(np.array(row), k)
+        assert (got is None) == (want is None), (k, got)
+        if want is not None:
+            assert tuple(got) == want, (k, got, want)
+    assert orc.topk_boundary(np.array([5.0, 4.0]), 1) == (5.0, 4.0)        # n = k + 1
+    assert orc.topk_boundary(np.array([4.0, 5.0]), 1) == (5.0, 4.0)
+    assert orc.topk_boundary(np.array([2.5] * 6), 4) == (2.5, 2.5)           # all equal
+    assert orc.topk_boundary(np.array([-1.0, -3.0, -2.0]), 2) == (-2.0, -3.0)
+    assert orc.topk_boundary(np.array([1.0]), 1) is None                    # n = k
+    bd = orc.topk_boundary(np.array([0.0, -0.0, 0.0, -1.0]), 3)             # -0 == +0
+    assert bd[0] == 0.0 and bd[1] == -1.0
+
+
+def pin_topk_boundary_counting_and_selection(orc):
+    """Random and tie-heavy rows: the boundary equals the counting definition, and it
+    brackets the selected set: a = min score of topk_select_row's set, b = max score of
+    the rest (topk_select_row is pinned by brute force on its own)."""
+    g = sa_synth.rng(23)
+    for it in range(400):
+        n = int(g.integers(1, 30))
+        k = int(g.integers(1, 32))
+        if it % 3 == 0:
+            row = g.integers(-2, 3, size=n).astype(np.float64)
+        elif it % 3 == 1:
+            row = g.standard_normal(n)
+        else:
+            row = np.full(n, float(g.integers(-2, 3)))
+        got = orc.topk_boundary(row, k)
+        want = _boundary_by_counting(row.tolist(), k)
+        assert (got is None) == (want is None), (row, k, got)
+        if got is None:
+            assert n <= k
+            continue
+        assert tuple(float(v) for v in got) == want, (row, k, got, want)
+        sel = orc.topk_select_row(row, k)
+        chosen = np.zeros(n, dtype=bool)
+        chosen[sel[sel >= 0]] = True
+        assert row[chosen].min() == got[0] and row[~chosen].max() == got[1], (row, k)
+
+
 # ------------------------------------------------------------------------------ sparse attention
 
 def pin_attn_hand(orc):
@@ -403,18 +463,35 @@ def pin_decode_window_covers(orc):
 # ------------------------------------------------------------------------------ index reuse
 
 def pin_indexcache(orc):
-    """F,S,S,S: one indexer evaluation; each S layer equals sparse attention with the F
-    layer's indices (the 3 skipped evaluations are the '75%' of the IndexCache page)."""
-    T = 40
-    x = sa_synth.indexer_inputs(61, 1, T, 2, 8, "f32")
+    """F,S,S,S: one indexer evaluation; each S layer is sparse attention over the F layer's
+    selection.  The expected selection is brute force here: exact rational scores of
+    integer indexer inputs (many ties) ranked by a full stable sort; each layer's output is
+    float64 SDPA under the explicit mask (that selection united with the window).  The 3
+    skipped evaluations are the '75%' of the IndexCache page (body paragraphs 2-4)."""
+    T, k, W, scale = 40, 6, 3, 0.3
+    x = sa_synth.integer_indexer_inputs(61, 1, T, 2, 4)
+    qi, ki, w = x["qi"], x["ki"], x["w"]
     layers = [sa_synth.attn_inputs(62 + l, 1, T, 2, 1, 8, "f32") for l in range(4)]
-    outs, n_index = orc.indexcache_prefill(x["qi"], x["ki"], x["w"], layers, "FSSS", 6, 3, 0.3)
+    outs, n_index = orc.indexcache_prefill(qi, ki, w, layers, "FSSS", k, W, scale)
     assert n_index == 1
-    sc = orc.indexer_scores(x["qi"], x["ki"], x["w"])
-    idx = orc.topk_select(sc, 6, 1, T)
-    for lay, (O, _) in zip(layers, outs):
-        want, _ = orc.sparse_attn(lay["q"], lay["k"], lay["v"], idx, 3, 0.3)
-        assert np.array_equal(O, want)
+    sel = []
+    for t in range(T):
+        row = []
+        for s in range(t + 1):
+            sc = Fraction(0)
+            for h in range(2):
+                dot = sum(Fraction(int(qi[0, t, h, d])) * int(ki[0, s, d]) for d in range(4))
+                sc += Fraction(float(w[h])) * max(dot, Fraction(0))
+            row.append(sc)
+        order = sorted(range(t + 1), key=lambda s_: (-row[s_], s_))
+        sel.append(set(order[:k]))
+    for lay, (O, L) in zip(layers, outs):
+        for t in range(T):
+            m = np.zeros(t + 1, dtype=bool)
+            m[sorted(sel[t] | set(range(max(0, t - W + 1), t + 1)))] = True
+            want = _mask_attend64(lay["q"][0, t], lay["k"][0, : t + 1, 0], lay["v"][0, : t + 1, 0],
+                                  scale, m)
+            assert np.abs(O[0, t] - want).max() < 1e-12, t
 
 
 def pin_e4m3_closed_forms(orc):

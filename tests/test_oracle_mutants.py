@@ -76,6 +76,14 @@ MUTANTS = [
      "dK[b, : t + 1, g] += scale * np.matmul(ds.T, do)"),
     ("bwd_dv_transposed", "dV[b, : t + 1, g] += np.matmul(p.T, do)",
      "dV[b, : t + 1, g] += np.matmul(p.T, qh)"),
+    ("boundary_off_by_one", "return float(srt[k - 1]), float(srt[k])",
+     "return float(srt[k]), float(srt[k + 1]) if n > k + 1 else float(srt[k])"),
+    ("boundary_ascending_sort", "srt = np.sort(s)[::-1]", "srt = np.sort(s)"),
+    ("boundary_kth_twice", "return float(srt[k - 1]), float(srt[k])",
+     "return float(srt[k - 1]), float(srt[k - 1])"),
+    ("boundary_when_n_equals_k", "    if n <= k:\n        return None\n    srt",
+     "    if n < k:\n        return None\n    srt"),
+    ("boundary_distinct_values", "srt = np.sort(s)[::-1]", "srt = np.unique(s)[::-1]"),
     ("nsa_decode_window_without_self", "m_win[max(0, L - window): L] = True",
      "m_win[max(0, L - window): L - 1] = True"),
 ]
@@ -93,10 +101,11 @@ def _load_mutant(orig, new):
 @pytest.mark.parametrize("name,orig,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(name, orig, new):
     mod = _load_mutant(orig, new)
-    failed = []
+    caught_by = None
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(mod)
         except Exception:          # AssertionError, or the mutant crashing on a pin's input
-            failed.append(pin.__name__)
-    assert failed, f"mutant {name} passes every pin"
+            caught_by = pin.__name__
+            break
+    assert caught_by, f"mutant {name} passes every pin"

@@ -167,6 +167,22 @@ def _dev(t, name: str, dtype=None):
     return t
 
 
+def _shape(t, name: str, *dims):
+    """Raise ValueError unless t.shape matches dims (None matches any extent)."""
+    if t is None:
+        return
+    if len(t.shape) != len(dims) or any(d is not None and int(e) != int(d)
+                                        for e, d in zip(t.shape, dims)):
+        want = "[" + ", ".join("*" if d is None else str(d) for d in dims) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
+def _same_device(name: str, ref, *ts):
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name}: every tensor must be on {ref.device}, got {t.device}")
+
+
 def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -185,13 +201,19 @@ def sa_indexer_scores(qi, ki, w, row_begin: int = 0, row_end: int | None = None,
     [B, row_end-row_begin, ld] f32 (entries s > t untouched / uninitialised)."""
     torch = _torch()
     _dev(qi, "qi"); _dev(ki, "ki", qi.dtype); _dev(w, "w", torch.float32)
+    _shape(qi, "qi", None, None, None, None)
     B, T, H, DI = qi.shape
+    _shape(ki, "ki", B, T, DI); _shape(w, "w", H)
     row_end = T if row_end is None else row_end
     ld = ld if ld is not None else ((row_end + 3) // 4) * 4
     R = row_end - row_begin
     if scores is None:
         scores = torch.empty((B, R, ld), dtype=torch.float32, device=qi.device)
     _dev(scores, "scores", torch.float32)
+    _shape(scores, "scores", B, R, None)
+    if ld > scores.shape[2]:
+        raise ValueError(f"ld={ld} exceeds the scores row length {scores.shape[2]}")
+    _same_device("sa_indexer_scores", qi, ki, w, scores)
     rc = lib().sa_indexer_scores(_p(qi), _p(ki), _p(w), B, T, H, DI, _dtype_code(qi), row_begin,
                                  row_end, _p(scores), ld, _stream(qi.device))
     _check("sa_indexer_scores", rc)
@@ -204,12 +226,19 @@ def sa_topk_select(scores, k: int, T: int, row_begin: int = 0, row_end: int | No
     ``scores`` is [B, row_end-row_begin, ld] f32; ``idx`` is [B, T, k] int32."""
     torch = _torch()
     _dev(scores, "scores", torch.float32)
+    _shape(scores, "scores", None, None, None)
     B, R, ld0 = scores.shape
     ld = ld0 if ld is None else ld
     row_end = row_begin + R if row_end is None else row_end
+    if row_end - row_begin != R:
+        raise ValueError(f"scores holds {R} rows but row_end - row_begin = {row_end - row_begin}")
+    if ld > ld0:
+        raise ValueError(f"ld={ld} exceeds the scores row length {ld0}")
     if idx is None:
         idx = torch.full((B, T, k), -1, dtype=torch.int32, device=scores.device)
     _dev(idx, "idx", torch.int32)
+    _shape(idx, "idx", B, T, k)
+    _same_device("sa_topk_select", scores, idx)
     rc = lib().sa_topk_select(_p(scores), ld, B, T, row_begin, row_end, k, _p(idx),
                               _stream(scores.device))
     _check("sa_topk_select", rc)
@@ -228,7 +257,9 @@ def sa_indexer_topk(qi, ki, w, k: int, row_begin: int = 0, row_end: int | None =
     initialisation needed) is allocated when not given."""
     torch = _torch()
     _dev(qi, "qi"); _dev(ki, "ki", qi.dtype); _dev(w, "w", torch.float32)
+    _shape(qi, "qi", None, None, None, None)
     B, T, H, DI = qi.shape
+    _shape(ki, "ki", B, T, DI); _shape(w, "w", H)
     row_end = T if row_end is None else row_end
     need = sa_indexer_topk_workspace(B, T, H, DI, row_begin, row_end, k)
     if workspace is None:
@@ -237,11 +268,32 @@ def sa_indexer_topk(qi, ki, w, k: int, row_begin: int = 0, row_end: int | None =
     if idx is None:
         idx = torch.full((B, T, k), -1, dtype=torch.int32, device=qi.device)
     _dev(idx, "idx", torch.int32)
+    _shape(idx, "idx", B, T, k)
+    _same_device("sa_indexer_topk", qi, ki, w, idx, workspace)
     rc = lib().sa_indexer_topk(_p(qi), _p(ki), _p(w), B, T, H, DI, _dtype_code(qi), row_begin,
                                row_end, k, _p(idx), _p(workspace), workspace.numel(),
                                _stream(qi.device))
     _check("sa_indexer_topk", rc)
     return idx
+
+
+def _attn_shapes(q, k, v, idx):
+    """(B, T, Hq, D, Hkv, topk) of an attention call, after checking that k and v are
+    [B,T,Hkv,D] with Hq a multiple of Hkv and idx (if any) is [B,T,topk] int32."""
+    torch = _torch()
+    _shape(q, "q", None, None, None, None)
+    B, T, Hq, D = q.shape
+    _shape(k, "k", B, T, None, D)
+    Hkv = k.shape[2]
+    _shape(v, "v", B, T, Hkv, D)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    topk = 0
+    if idx is not None:
+        _dev(idx, "idx", torch.int32)
+        _shape(idx, "idx", B, T, None)
+        topk = idx.shape[-1]
+    return B, T, Hq, D, Hkv, topk
 
 
 def sa_sparse_attn_fwd(q, k, v, idx, window: int, scale: float, out=None, lse=None,
@@ -250,19 +302,17 @@ def sa_sparse_attn_fwd(q, k, v, idx, window: int, scale: float, out=None, lse=No
     (or None with topk = 0).  Returns out (and lse [B,Hq,T] f32 if asked)."""
     torch = _torch()
     _dev(q, "q"); _dev(k, "k", q.dtype); _dev(v, "v", q.dtype)
-    B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
-    topk = 0
-    if idx is not None:
-        _dev(idx, "idx", torch.int32)
-        topk = idx.shape[-1]
+    B, T, Hq, D, Hkv, topk = _attn_shapes(q, k, v, idx)
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
+    _shape(out, "out", B, T, Hq, D)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", B, Hq, T)
+    _same_device("sa_sparse_attn_fwd", q, k, v, idx, out, lse)
     rc = lib().sa_sparse_attn_fwd(_p(q), _p(k), _p(v), _p(idx), B, T, Hq, Hkv, D, topk, window,
                                   float(scale), _dtype_code(q), _p(out), _p(lse),
                                   _stream(q.device))
@@ -276,14 +326,12 @@ def sa_sparse_attn_fwd_rows(q, k, v, idx, window: int, scale: float, row_begin: 
     out (and lse); other rows are not touched."""
     torch = _torch()
     _dev(q, "q"); _dev(k, "k", q.dtype); _dev(v, "v", q.dtype); _dev(out, "out", q.dtype)
-    B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
-    topk = 0
-    if idx is not None:
-        _dev(idx, "idx", torch.int32)
-        topk = idx.shape[-1]
+    B, T, Hq, D, Hkv, topk = _attn_shapes(q, k, v, idx)
+    _shape(out, "out", B, T, Hq, D)
     if lse is not None:
         _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", B, Hq, T)
+    _same_device("sa_sparse_attn_fwd_rows", q, k, v, idx, out, lse)
     rc = lib().sa_sparse_attn_fwd_rows(_p(q), _p(k), _p(v), _p(idx), B, T, Hq, Hkv, D, topk,
                                        window, float(scale), _dtype_code(q), row_begin, row_end,
                                        _p(out), _p(lse), _stream(q.device))
@@ -296,10 +344,15 @@ def sa_graph_attn_fwd(cq, ck, v, bias, tau: float, local: int, n_pow2: int, out=
     """Fixed-graph distance attention; cq/ck [B,T,H,3], v [B,T,H,D] (same dtype), bias [H] f32."""
     torch = _torch()
     _dev(cq, "cq", v.dtype); _dev(ck, "ck", v.dtype); _dev(v, "v"); _dev(bias, "bias", torch.float32)
+    _shape(v, "v", None, None, None, None)
     B, T, H, D = v.shape
+    _shape(cq, "cq", B, T, H, 3); _shape(ck, "ck", B, T, H, 3); _shape(bias, "bias", H)
     if out is None:
         out = torch.empty_like(v)
+    _dev(out, "out", v.dtype)
+    _shape(out, "out", B, T, H, D)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device) if return_lse else None
+    _same_device("sa_graph_attn_fwd", v, cq, ck, bias, out)
     rc = lib().sa_graph_attn_fwd(_p(cq), _p(ck), _p(v), _p(bias), float(tau), B, T, H, D, local,
                                  n_pow2, _dtype_code(v), _p(out), _p(lse), _stream(v.device))
     _check("sa_graph_attn_fwd", rc)
@@ -310,10 +363,14 @@ def sa_block_meanpool(kcache, lens, block: int, kbar=None):
     """kbar [B, Lmax//block, Hkv, D] f32 of complete blocks (others untouched)."""
     torch = _torch()
     _dev(kcache, "kcache"); _dev(lens, "lens", torch.int32)
+    _shape(kcache, "kcache", None, None, None, None)
     B, Lmax, Hkv, D = kcache.shape
+    _shape(lens, "lens", B)
     if kbar is None:
         kbar = torch.zeros((B, Lmax // block, Hkv, D), dtype=torch.float32, device=kcache.device)
     _dev(kbar, "kbar", torch.float32)
+    _shape(kbar, "kbar", B, Lmax // block, Hkv, D)
+    _same_device("sa_block_meanpool", kcache, lens, kbar)
     rc = lib().sa_block_meanpool(_p(kcache), _p(lens), B, Lmax, Hkv, D, block,
                                  _dtype_code(kcache), _p(kbar), _stream(kcache.device))
     _check("sa_block_meanpool", rc)
@@ -338,14 +395,24 @@ def sa_sparse_decode(q, kcache, vcache, kbar, lens, block: int, top_blocks: int,
     torch = _torch()
     _dev(q, "q"); _dev(kcache, "kcache", q.dtype); _dev(vcache, "vcache", q.dtype)
     _dev(kbar, "kbar", torch.float32); _dev(lens, "lens", torch.int32)
+    _shape(q, "q", None, None, None)
     B, Hq, D = q.shape
+    _shape(kcache, "kcache", B, None, None, D)
     _, Lmax, Hkv, _ = kcache.shape
+    _shape(vcache, "vcache", B, Lmax, Hkv, D)
+    _shape(kbar, "kbar", B, Lmax // block, Hkv, D)
+    _shape(lens, "lens", B)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
     need = sa_sparse_decode_workspace(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits)
     if workspace is None:
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
     if out is None:
         out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _shape(out, "out", B, Hq, D)
+    _same_device("sa_sparse_decode", q, kcache, vcache, kbar, lens, workspace, out)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
     sel = (torch.empty((B, Hkv, top_blocks), dtype=torch.int32, device=q.device)
            if return_sel else None)
@@ -373,13 +440,22 @@ def sa_cmp_attn_fwd(q, kbar, vbar, block: int, scale: float, out=None, lse=None,
     [B,T/block,Hkv,D] f32.  Returns out (and lse [B,Hq,T] f32 when asked)."""
     torch = _torch()
     _dev(q, "q"); _dev(kbar, "kbar", torch.float32); _dev(vbar, "vbar", torch.float32)
+    _shape(q, "q", None, None, None, None)
     B, T, Hq, D = q.shape
+    _shape(kbar, "kbar", B, T // block, None, D)
     Hkv = kbar.shape[2]
+    _shape(vbar, "vbar", B, T // block, Hkv, D)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
+    _shape(out, "out", B, T, Hq, D)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", B, Hq, T)
     if workspace is None:
         workspace = torch.empty(max(sa_cmp_attn_workspace(B, T, Hkv, D, block), 256),
                                 dtype=torch.uint8, device=q.device)
@@ -400,12 +476,17 @@ def sa_block_select(q, kbar, block: int, top_blocks: int, row_begin: int = 0,
     idx [B, T, top_blocks*block] int32 (rows [row_begin, row_end))."""
     torch = _torch()
     _dev(q, "q"); _dev(kbar, "kbar", torch.float32)
+    _shape(q, "q", None, None, None, None)
     B, T, Hq, D = q.shape
+    _shape(kbar, "kbar", B, T // block, None, D)
     Hkv = kbar.shape[2]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
     row_end = T if row_end is None else row_end
     if idx is None:
         idx = torch.full((B, T, top_blocks * block), -1, dtype=torch.int32, device=q.device)
     _dev(idx, "idx", torch.int32)
+    _shape(idx, "idx", B, T, top_blocks * block)
     if workspace is None:
         workspace = torch.empty(max(sa_block_select_workspace(B, T, Hkv, D, block, row_begin,
                                                               row_end), 256),
@@ -422,9 +503,14 @@ def sa_nsa_combine(o_cmp, o_slc, o_win, gates, out=None):
     torch = _torch()
     _dev(o_cmp, "o_cmp"); _dev(o_slc, "o_slc", o_cmp.dtype); _dev(o_win, "o_win", o_cmp.dtype)
     _dev(gates, "gates", torch.float32)
+    _shape(o_cmp, "o_cmp", None, None, None, None)
     B, T, Hq, D = o_cmp.shape
+    _shape(o_slc, "o_slc", B, T, Hq, D); _shape(o_win, "o_win", B, T, Hq, D)
+    _shape(gates, "gates", B, T, Hq, 3)
     if out is None:
         out = torch.empty_like(o_cmp)
+    _dev(out, "out", o_cmp.dtype)
+    _shape(out, "out", B, T, Hq, D)
     rc = lib().sa_nsa_combine(_p(o_cmp), _p(o_slc), _p(o_win), _p(gates), B, T, Hq, D,
                               _dtype_code(o_cmp), _p(out), _stream(o_cmp.device))
     _check("sa_nsa_combine", rc)
@@ -435,10 +521,14 @@ def sa_block_meanpool_bf16(kcache, lens, block: int, kbar=None):
     """Block means rounded to bf16: [B, Lmax//block, Hkv, D] (complete blocks only)."""
     torch = _torch()
     _dev(kcache, "kcache"); _dev(lens, "lens", torch.int32)
+    _shape(kcache, "kcache", None, None, None, None)
     B, Lmax, Hkv, D = kcache.shape
+    _shape(lens, "lens", B)
     if kbar is None:
         kbar = torch.zeros((B, Lmax // block, Hkv, D), dtype=torch.bfloat16, device=kcache.device)
     _dev(kbar, "kbar", torch.bfloat16)
+    _shape(kbar, "kbar", B, Lmax // block, Hkv, D)
+    _same_device("sa_block_meanpool_bf16", kcache, lens, kbar)
     rc = lib().sa_block_meanpool_bf16(_p(kcache), _p(lens), B, Lmax, Hkv, D, block,
                                       _dtype_code(kcache), _p(kbar), _stream(kcache.device))
     _check("sa_block_meanpool_bf16", rc)
@@ -458,12 +548,23 @@ def sa_nsa_decode_branch(q, keys, vals, lens, kind: int, block: int, window: int
     torch = _torch()
     _dev(q, "q"); _dev(keys, "keys", q.dtype); _dev(vals, "vals", q.dtype)
     _dev(lens, "lens", torch.int32)
+    _shape(q, "q", None, None, None)
     B, Hq, D = q.shape
+    _shape(keys, "keys", B, None, None, D)
     _, Lrows, Hkv, _ = keys.shape
+    _shape(vals, "vals", B, Lrows, Hkv, D)
+    _shape(lens, "lens", B)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
     if out is None:
         out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _shape(out, "out", B, Hq, D)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", B, Hq)
     ws_bytes = 0
     if n_splits > 1:
         if workspace is None:
@@ -492,16 +593,18 @@ def sa_sparse_attn_bwd(q, k, v, idx, window: int, scale: float, out, lse, dout, 
     torch = _torch()
     _dev(q, "q"); _dev(k, "k", q.dtype); _dev(v, "v", q.dtype)
     _dev(out, "out", q.dtype); _dev(dout, "dout", q.dtype); _dev(lse, "lse", torch.float32)
-    B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
-    topk = 0
-    if idx is not None:
-        _dev(idx, "idx", torch.int32)
-        topk = idx.shape[2]
+    B, T, Hq, D, Hkv, topk = _attn_shapes(q, k, v, idx)
+    _shape(out, "out", B, T, Hq, D); _shape(dout, "dout", B, T, Hq, D)
+    _shape(lse, "lse", B, Hq, T)
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty((B, T, Hq, D), **f32) if dq is None else dq
     dk = torch.empty((B, T, Hkv, D), **f32) if dk is None else dk
     dv = torch.empty((B, T, Hkv, D), **f32) if dv is None else dv
+    for t_, n_, shp in ((dq, "dq", (B, T, Hq, D)), (dk, "dk", (B, T, Hkv, D)),
+                        (dv, "dv", (B, T, Hkv, D))):
+        _dev(t_, n_, torch.float32)
+        _shape(t_, n_, *shp)
+    _same_device("sa_sparse_attn_bwd", q, k, v, idx, out, lse, dout, dq, dk, dv)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace")

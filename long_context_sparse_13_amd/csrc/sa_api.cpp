@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "sa_launch.h"
@@ -53,6 +54,27 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 constexpr int64_t kMaxElems = (int64_t)1 << 46;  // sanity bound on tensor sizes
+
+// SA_VALIDATE set to anything but "" or "0" turns on the debug checks (read on every call).
+bool validate_mode() {
+  const char* e = std::getenv("SA_VALIDATE");
+  return e && e[0] && std::strcmp(e, "0") != 0;
+}
+
+// The index contract: no position counted twice in a row (debug mode; synchronises).
+int check_idx_unique(const char* fn, const int32_t* idx, int B, int T, int topk, int window,
+                     int row_begin, int row_end, hipStream_t st) {
+  long long bad = -1;
+  const hipError_t e = sa::validate_idx_unique(idx, B, T, topk, window, row_begin, row_end,
+                                               &bad, st);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "%s: SA_VALIDATE index check: %s", fn,
+                                   hipGetErrorString(e));
+  if (bad >= 0)
+    return fail(SA_ERR_INVALID_ARG,
+                "%s: SA_VALIDATE: idx row (b=%lld, t=%lld) lists a position in [0, t - window] "
+                "more than once", fn, bad / T, bad % T);
+  return SA_OK;
+}
 
 }  // namespace
 
@@ -199,6 +221,11 @@ int sa_sparse_attn_fwd_rows(const void* q, const void* k, const void* v, const i
     SUPPORT(G <= 64 && G * D <= 4096, "Hq/Hkv=%d with D=%d is not supported", G, D);
     if (lse) REQUIRE(aligned16(lse), "lse is not 16-byte aligned");
     if (idx) REQUIRE(aligned16(idx), "idx is not 16-byte aligned");
+    if (topk > 0 && validate_mode()) {
+      const int rc = check_idx_unique("sa_sparse_attn_fwd", idx, B, T, topk, window, row_begin,
+                                      row_end, as_stream(stream));
+      if (rc != SA_OK) return rc;
+    }
     return hip_status(sa::launch_sparse_attn_fwd(q, k, v, idx, B, T, Hq, Hkv, D, topk, window,
                                                  scale, dtype == SA_BF16, out, lse, row_begin,
                                                  row_end, as_stream(stream)),
@@ -319,6 +346,11 @@ int sa_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_
         return fail(SA_ERR_WORKSPACE,
                     "sa_sparse_attn_bwd: workspace of at least %zu bytes needed (got %zu)",
                     sa::sparse_attn_bwd_workspace_bytes(B, T, Hkv, D, topk, window, 1), ws_bytes);
+    }
+    if (topk > 0 && validate_mode()) {
+      const int rc = check_idx_unique("sa_sparse_attn_bwd", idx, B, T, topk, window, 0, T,
+                                      as_stream(stream));
+      if (rc != SA_OK) return rc;
     }
     return hip_status(sa::launch_sparse_attn_bwd(q, k, v, idx, B, T, Hq, Hkv, D, topk, window,
                                                  scale, out, lse, dout, dq, dk, dv, workspace,
@@ -514,26 +546,38 @@ int sa_sparse_decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_bl
   return sa::decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window);
 }
 
+// Arguments shared by both decode entry points; *ns = the split count used.
+static int decode_args(const void* q, const void* kcache, const void* vcache, const float* kbar,
+                       const int32_t* lens, int B, int Lmax, int Hq, int Hkv, int D, int block,
+                       int top_blocks, int window, int n_splits, int dtype, const void* out,
+                       int* ns) {
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kcache);
+  REQUIRE_PTR(vcache);
+  REQUIRE_PTR(kbar);
+  REQUIRE(lens, "lens is NULL");
+  REQUIRE_PTR(out);
+  REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
+          dtype);
+  SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
+  const int rc = decode_check_sizes(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits);
+  if (rc != SA_OK) return rc;
+  SUPPORT(dtype == SA_BF16, "the decode supports bf16 only");
+  REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
+  *ns = n_splits ? n_splits : sa::decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window);
+  return SA_OK;
+}
+
 int sa_sparse_decode(const void* q, const void* kcache, const void* vcache, const float* kbar,
                      const int32_t* lens, int B, int Lmax, int Hq, int Hkv, int D, int block,
                      int top_blocks, int window, int n_splits, float scale, int dtype, void* out,
                      float* lse, int32_t* sel_blocks, void* workspace, size_t ws_bytes,
                      void* stream) {
   try {
-    REQUIRE_PTR(q);
-    REQUIRE_PTR(kcache);
-    REQUIRE_PTR(vcache);
-    REQUIRE_PTR(kbar);
-    REQUIRE(lens, "lens is NULL");
-    REQUIRE_PTR(out);
-    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d",
-            dtype);
-    SUPPORT(dtype != SA_FP8_E4M3, "E4M3 inputs are taken by the indexer entry points only");
-    const int rc = decode_check_sizes(B, Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits);
+    int ns = 0;
+    const int rc = decode_args(q, kcache, vcache, kbar, lens, B, Lmax, Hq, Hkv, D, block,
+                               top_blocks, window, n_splits, dtype, out, &ns);
     if (rc != SA_OK) return rc;
-    SUPPORT(dtype == SA_BF16, "sa_sparse_decode supports bf16 only");
-    REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
-    const int ns = n_splits ? n_splits : sa::decode_auto_splits(B, Lmax, Hkv, block, top_blocks, window);
     const size_t need = sa::decode_workspace_bytes(B, Lmax, Hq, Hkv, D, block, top_blocks, ns);
     if (!workspace || !aligned16(workspace))
       return fail(SA_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");

@@ -38,6 +38,11 @@ hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, c
                                   float scale, bool bf16, void* out, float* lse, int row_begin,
                                   int row_end, hipStream_t st);
 
+// SA_VALIDATE: the first row (b * T + t) of [row_begin, row_end) that lists a position
+// 0 <= s <= t - window more than once, or -1; synchronises the stream.
+hipError_t validate_idx_unique(const int32_t* idx, int B, int T, int topk, int window,
+                               int row_begin, int row_end, long long* bad_row, hipStream_t st);
+
 hipError_t launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const int32_t* idx,
                                   int B, int T, int Hq, int Hkv, int D, int topk, int window,
                                   float scale, const void* out, const float* lse,

@@ -15,6 +15,13 @@
  * returns SA_ERR_HIP with the HIP error text; faults inside a kernel surface at the
  * caller's next synchronisation.  No C++ exception crosses this boundary.
  *
+ * Debug mode: with the environment variable SA_VALIDATE set (to anything but "" or "0",
+ * read on every call), sa_sparse_attn_fwd, sa_sparse_attn_fwd_rows and sa_sparse_attn_bwd
+ * also check the index contract on the device before they launch: no row may list a
+ * position 0 <= s <= t - window more than once.  A violation returns SA_ERR_INVALID_ARG
+ * naming the first such row (b, t), and nothing is launched.  This check synchronises
+ * the stream (it hands its result to the host); without SA_VALIDATE nothing synchronises.
+ *
  * Notation: B batch, T tokens, Hq query heads, Hkv key/value heads (Hq % Hkv == 0,
  * query head h reads KV head h / (Hq / Hkv)), D head dimension.  "bf16" tensors are
  * stored as bfloat16 and accumulated in float32; "f32" tensors are float32.
@@ -142,7 +149,8 @@ size_t sa_indexer_topk_workspace(int B, int T, int H_I, int D_I, int row_begin, 
  *
  * Each key counts once: listed positions inside the window, -1 and any value outside
  * [0, t] are ignored.  Listed positions must be distinct (duplicates are a caller
- * error and are counted twice).  An empty S_t gives out = 0 and lse = -inf.
+ * error: they are counted twice, or rejected with SA_ERR_INVALID_ARG under SA_VALIDATE).
+ * An empty S_t gives out = 0 and lse = -inf.
  *
  * q   [B, T, Hq, D]  dtype        k, v [B, T, Hkv, D] dtype
  * idx [B, T, topk]   int32        (topk may be 0 with idx == NULL)
@@ -249,9 +257,8 @@ int sa_block_meanpool(const void* kcache, const int32_t* lens, int B, int Lmax, 
  * lens [B] int32 on the device; out [B, Hq, D] dtype; lse [B, Hq] float32 or NULL;
  * sel_blocks [B, Hkv, top_blocks] int32 or NULL.
  * n_splits: 0 = automatic, else 1..64.  workspace: device memory of at least
- * sa_sparse_decode_workspace(...) bytes, ZERO-FILLED before its first use; every call
- * leaves its counters at zero again.  Calls that share a workspace must be ordered on
- * one stream.
+ * sa_sparse_decode_workspace(...) bytes, any contents (the call clears what it needs).
+ * Calls that share a workspace must be ordered on one stream.
  * Requires D in {64, 128}, bf16, Hq/Hkv <= 16, block in {16, 32, 64, 128},
  * 1 <= top_blocks <= 64, window >= 0.
  */
@@ -330,7 +337,9 @@ int sa_block_meanpool_bf16(const void* kcache, const int32_t* lens, int B, int L
  *   out[b, h, :] = sum_{s in range} softmax_s(scale * q[b,h,:] . keys[b,s,g,:]) vals[b,s,g,:]
  *   lse[b, h]    = log sum exp (natural log; -inf and out = 0 for an empty range)
  * The selected branch is sa_sparse_decode with window 0 (all tokens of the chosen blocks).
- * q, out [B, Hq, D] bf16; lens [B] int32 on the device; lse [B, Hq] float32 or NULL.
+ * q, out [B, Hq, D] bf16; lens [B] int32 on the device, 0 <= lens[b] <= Lmax (values
+ * outside are clamped to [0, Lrows] for kind 0 and [0, Lrows * block] for kind 1);
+ * lse [B, Hq] float32 or NULL.
  * n_splits (1..64) workgroups share each (sequence, KV head)'s range, their partial softmaxes
  * merged by log-sum-exp [STAR paragraph 3]; with n_splits > 1, workspace holds at least
  * sa_nsa_decode_branch_workspace(B, Hq, Hkv, D, n_splits) bytes, ZERO-FILLED before its first

@@ -19,8 +19,8 @@
 // The kernel boundary makes the candidates visible to kernel 2.  Inside kernel 2 the
 // split partials travel through 16-byte stores and loads with the cache policy of
 // agent-scope atomics (sc1) and one counter per (sequence, KV head), avoiding a
-// device-wide cache flush per workgroup.  The counters
-// return to zero at the end of every call.
+// device-wide cache flush per workgroup.  Kernel 1 clears the counters (so the workspace
+// needs no initialisation) and kernel 2 returns them to zero at its end.
 #include "attn_tile.h"
 #include "sa_launch.h"
 #include "select.h"
@@ -196,7 +196,7 @@ template <int D>
 __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ lens, int Lmax, int Hq, int Hkv, int block, int per_wg, int cpw,
-    uint32_t* __restrict__ cand) {
+    uint32_t* __restrict__ cand, uint32_t* __restrict__ counters) {
   __shared__ __attribute__((aligned(16))) uint64_t scomb[kScoreChunk + kCandMax];
   __shared__ uint64_t best[kCandMax];
   __shared__ __attribute__((aligned(16))) uint16_t qrows[16 * D];  // the group's query rows
@@ -212,6 +212,10 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
   const int L = min(max(lens[b], 0), Lmax);  // lengths outside [0, Lmax] are clamped
   const int nfull = L / block;
 
+  // the merge counter of this (sequence, KV head) starts kernel 2 at zero (same policy as
+  // kernel 2's own accesses to it)
+  if (blockIdx.y == 0 && tid == 0)
+    __hip_atomic_store(&counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int d0 = (lane & 7) * C;
   const int j_begin = blockIdx.y * per_wg;
   const int j_end = min(j_begin + per_wg, nfull);
@@ -523,7 +527,7 @@ static void launch_decode_d(const void* q, const void* kcache, const void* vcach
   const dim3 g1((unsigned)(B * Hkv), (unsigned)nwg);
   const dim3 g2((unsigned)(B * Hkv), (unsigned)n_splits);
   hipLaunchKernelGGL(decode_block_scores<D>, g1, dim3(kScoreThreads), 0, st, (const uint16_t*)q,
-                     kbar, lens, Lmax, Hq, Hkv, block, per_wg, cpw, ws.cand);
+                     kbar, lens, Lmax, Hq, Hkv, block, per_wg, cpw, ws.cand, ws.counters);
   if (n_splits == 1)
     hipLaunchKernelGGL((decode_split_attn<D, kWholeWaves>), g2, dim3(64 * kWholeWaves), 0, st,
                        (const uint16_t*)q, (const uint16_t*)kcache, (const uint16_t*)vcache, lens,

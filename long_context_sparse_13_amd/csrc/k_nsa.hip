@@ -393,7 +393,10 @@ __global__ __launch_bounds__(64 * kRangeWaves) void nsa_decode_range(
   const int G = Hq / Hkv;
   const int h = g * G + n;
   const bool hv = n < G;
-  const int L = lens[b];
+  // lengths outside the cache are clamped to it: [0, Lrows] cache rows for the window
+  // branch, [0, Lrows * block] tokens (Lrows complete blocks) for the compressed one
+  const int64_t lcap = kind == 0 ? (int64_t)Lrows : (int64_t)Lrows * block;
+  const int L = (int)min((int64_t)max(lens[b], 0), lcap);
   const int lo = kind == 0 ? max(0, L - window) : 0;
   const int hi = kind == 0 ? L : L / block;
   // tiles of the range: this split's share, then this wavefront's share of that

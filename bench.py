@@ -3,20 +3,26 @@
 
 One step = the whole DSA-style prefill hot path on the 64K workload (T = 65,536 tokens,
 16 query heads on 1 KV head of dim 128, bf16; indexer of 4 heads x 64; top-2048 per query
-united with a 128-token window): sa_indexer_scores + sa_topk_select over row chunks, then
-sa_sparse_attn_fwd.  Inputs are seeded synthetic tensors (sa_synth), resident in HBM
-before the timed region.  ``value`` is query tokens per second of the whole step.
+united with a 128-token window): the fused indexer -> top-k (sa_indexer_topk) over two
+32,768-row chunks, then sa_sparse_attn_fwd (``--indices two-step`` builds the indices with
+sa_indexer_scores + sa_topk_select instead).  Inputs are seeded synthetic tensors
+(sa_synth), resident in HBM before the timed region.  ``value`` is query tokens per second
+of the whole step.
 
-The JSON line also carries the roofline of the dominant kernel (sparse attention; bytes
-gathered per launch / its average HIP-event duration / 8 TB/s), the float64 CPU oracle
-timed on a bounded row sample, and the other hot-path rows: the sparse-attention backward
-(64K), E4M3 indexer inputs (64K), NSA's three branches (prefill 64K, decode 32 x 128K),
-fixed-graph attention (16K, 64K, 128K), block-sparse decode (32 x 128K) and cross-layer
-index reuse (128K, F,S,S,S).
+The JSON line also carries the roofline of the dominant kernel (the sparse attention: its
+algorithmic bytes per launch, K/V rows gathered plus Q, O and the index rows, over its
+average HIP-event duration, against the aggregate L2 read bandwidth, the level that serves
+the gathered rows; its HBM side from the byte counters beside it), a read probe of the
+memory hierarchy (L2-, Infinity-Cache- and HBM-resident buffers), the float64 CPU oracle
+timed on every workload (full runs or bounded, labelled samples), and the other hot-path
+rows, each timed cold (a 1 GiB buffer rewritten before every call) with the warm figure
+beside: the sparse-attention backward (64K), E4M3 indexer inputs (64K), NSA's three
+branches (prefill 64K, decode 32 x 128K), fixed-graph attention (16K, 64K, 128K),
+block-sparse decode (32 x 128K) and cross-layer index reuse (128K, F,S,S,S).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk ROWS] [--no-extra]
        [--no-cpu] [--only attn|prefill] [--extra all|bwd,e4m3,nsa,graph,decode,reuse]
-       [--bwd-rows N]
+       [--bwd-rows N] [--cpu all|3]
        python bench.py --traffic-from DIR   (profiles/traffic.json from counter runs)
 """
 
@@ -31,6 +37,10 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+# Aggregate L2 read bandwidth: 8 XCDs x 16 L2 channels x 128 bytes per clock per channel
+# (the per-XCD L2 organisation AMD documents for CDNA 3 and keeps in CDNA 4: 4 MB of L2
+# per XCD) x 2.4 GHz.
+L2_PEAK_GBS = 8 * 16 * 128 * 2.4
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCES = ("k_sparse_attn.hip", "attn_tile.h", "sa_device.h")
@@ -109,6 +119,43 @@ def write_traffic(base: str) -> dict:
     return t
 
 
+def memory_probe(torch, dev):
+    """Read bandwidth of three buffers with the probe kernel of libsa_probe.so (16-byte
+    loads, 1 KB contiguous per wavefront instruction), in GB/s: 16 MiB split in eight 2 MiB
+    slices, each re-read by the workgroups of one XCD (L2-resident); 128 MiB streamed by
+    every XCD (larger than the L2s, inside the 256 MB Infinity Cache); 4 GiB (HBM)."""
+    import ctypes
+    path = os.path.join(ROOT, "long_context_sparse_13_amd", "libsa_probe.so")
+    L = ctypes.CDLL(path)
+    f = L.sa_probe_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    cases = (("l2", 16 << 20, 8, 2000, 2048), ("infinity_cache", 128 << 20, 1, 40, 2048),
+             ("hbm", 4 << 30, 1, 1, 8192))
+    out = {}
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device=dev)
+    for name, nbytes, slices, passes, wgs in cases:
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        ms = []
+        for it in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = f(ctypes.c_void_p(buf.data_ptr()), nbytes, slices, passes, wgs,
+                   ctypes.c_void_p(sink.data_ptr()), st)
+            e1.record()
+            if rc != 0:
+                raise RuntimeError(f"read probe launch failed ({rc})")
+            torch.cuda.synchronize()
+            if it:
+                ms.append(e0.elapsed_time(e1))
+        out[name + "_GBps"] = nbytes * passes / (min(ms) * 1e-3) / 1e9
+        del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +177,9 @@ def parse():
                     help="query rows per chunk of the backward's partial-row workspace")
     ap.add_argument("--only", choices=["attn", "prefill"], default=None,
                     help="time only one part (for profiling runs)")
+    ap.add_argument("--cpu", default="all", choices=["all", "3"],
+                    help="the CPU oracle on every workload, or on the 64K one only")
+    ap.add_argument("--no-probe", action="store_true", help="skip the memory read probe")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="first copy MB megabytes 3 times with torch (a plain copy kernel of "
                          "known size, to calibrate the HBM byte counters)")
@@ -329,6 +379,12 @@ def main():
     fused_ms = fsrc.ms("indexer_topk")[0] / nsteps_f
     n_recomputed = int(ws[:4].view(torch.int32).item()) if fused_ms else None
     n_pairs = T * (T + 1) // 2
+    probe = None if args.no_probe else memory_probe(torch, dev)
+    if probe:
+        log("read probe: " + ", ".join(f"{k} {v:.0f}" for k, v in probe.items()))
+    traffic = measured_traffic()
+    bytes_hbm = T * Hkv * D * 2 * 2 + bytes_qo + bytes_idx   # K, V once; Q, O; idx
+    l2_frac = achieved / L2_PEAK_GBS if achieved else None
     res = {
         "metric": "sparse-attn fwd query-tokens/s at 64K ctx, top-k=2048; % HBM/MFMA roofline",
         "value": T / (ms_step * 1e-3),
@@ -352,17 +408,42 @@ def main():
         "two_streams": two_streams,
         "roofline": {
             "kernel": "sparse_attn_mfma<128, true>",
-            "bound": "hbm",
+            # the gathered K/V rows (33.5 MB of keys and values, re-read ~2,100 times) are
+            # served by the L2 and the Infinity Cache, not by HBM: the bound is the
+            # aggregate L2 read bandwidth
+            "bound": "l2",
             "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
+            "peak": L2_PEAK_GBS,
             "unit": "GB/s",
-            "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-            "traffic": measured_traffic(),
+            "frac": l2_frac,
+            "traffic": traffic,
+            "peak_source": "8 XCDs x 16 L2 channels x 128 B/clk x 2.4 GHz (CDNA 3/4 L2 "
+                           "organisation); checked by the read probe (l2_probe_GBps)",
             "algorithmic_bytes_per_launch": attn_bytes,
             "selected_keys_per_launch": n_sel,
             "avg_launch_ms": attn_avg_ms,
-            "mfma_tflops": attn_flops / (attn_avg_ms * 1e-3) / 1e12 if attn_n else None,
+            "l2_probe_GBps": probe["l2_GBps"] if probe else None,
+            "frac_of_l2_probe": (achieved / probe["l2_GBps"]) if probe and achieved else None,
+            "hbm": {
+                "compulsory_bytes": bytes_hbm,
+                "compulsory_GBps": bytes_hbm / (attn_avg_ms * 1e-3) / 1e9 if attn_n else None,
+                "compulsory_frac": (bytes_hbm / (attn_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                if attn_n else None,
+                "past_l2_bytes": traffic,
+                "past_l2_GBps": traffic / (attn_avg_ms * 1e-3) / 1e9 if traffic and attn_n
+                else None,
+                "past_l2_frac": traffic / (attn_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+                if traffic and attn_n else None,
+                "note": "past_l2 = FETCH_SIZE + WRITE_SIZE (copy-calibrated): L2 misses, "
+                        "which include Infinity Cache hits; compulsory = K, V once + Q + O + idx",
+            },
+            "mfma": {
+                "tflops": attn_flops / (attn_avg_ms * 1e-3) / 1e12 if attn_n else None,
+                "frac": attn_flops / (attn_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+                if attn_n else None,
+            },
         },
+        "memory_probe": probe,
         "indexer_topk": {
             "avg_ms_per_step": fused_ms,
             "effective_tflops": (n_pairs * 2 * HI * DI) / (fused_ms * 1e-3) / 1e12
@@ -392,15 +473,22 @@ def main():
     del scores, ws
     torch.cuda.empty_cache()
 
+    keep = {}  # host inputs of the decode and reuse workloads, for the CPU oracle
+    want_host = not args.no_cpu and args.cpu == "all"
     if not args.no_extra:
-        res["rows"] = extra_rows(torch, np, sa, sa_synth, to_dev, args, q, k, v, idx)
+        res["rows"] = extra_rows(torch, np, sa, sa_synth, to_dev, args, q, k, v, idx,
+                                 keep if want_host else None)
+    del q, k, v, idx, qi, ki, w, out
+    torch.cuda.empty_cache()
 
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(np, sa_synth, x, p, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(np, sa_synth, x, p, args.cpu_seconds, args.cpu, keep)
     print(json.dumps(res), flush=True)
 
 
-def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
+def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64, keep=None):
+    """The other hot-path rows.  ``keep`` (a dict, or None) receives the host inputs of the
+    decode and index-reuse workloads for the CPU oracle."""
     dev = q64.device
     rows = {}
     reps = 20
@@ -410,6 +498,7 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         return groups is None or name in groups
 
     def timed(fn, n):
+        """Warm: n calls back to back on the same inputs (caches keep what fits)."""
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -420,6 +509,26 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
+
+    # 1 GiB (four times the Infinity Cache, far more than the L2s) read and rewritten
+    # before each cold call
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed_cold(fn, n):
+        """Cold: the median of n calls, each timed alone right after the flush."""
+        fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(n):
+            flush.add_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return ts[len(ts) // 2]
 
     # ---- the backward of the 64K sparse attention (same q, k, v, indices; a seeded bf16
     # upstream gradient), with the forward timed beside it
@@ -528,10 +637,12 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
             "window": lambda: sa.sa_sparse_attn_fwd(q64, k64, v64, None, nwin, scale3, out=ow3),
             "combine": lambda: sa.sa_nsa_combine(oc3, os3, ow3, gates3, out=on3),
         }
-        part_ms = {name: timed(fn, 3) for name, fn in parts.items()}
-        t_nsa = timed(lambda: [fn() for fn in parts.values()], 3)
+        part_ms = {name: timed_cold(fn, 3) for name, fn in parts.items()}
+        t_nsa = timed_cold(lambda: [fn() for fn in parts.values()], 3)
+        t_nsa_warm = timed(lambda: [fn() for fn in parts.values()], 3)
         rows["nsa_prefill_64k"] = {
-            "ms_per_step": t_nsa, "query_tokens_per_s": T3 / (t_nsa * 1e-3), "parts_ms": part_ms,
+            "ms_per_step": t_nsa, "warm_ms_per_step": t_nsa_warm, "timing": "cold",
+            "query_tokens_per_s": T3 / (t_nsa * 1e-3), "parts_ms": part_ms,
             "block": nblk, "top_blocks": ntop, "window": nwin,
             "selected_keys_per_query": ntop * nblk,
         }
@@ -552,14 +663,17 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
                                 to_dev(g["v"], "bf16"), to_dev(g["bias"], "f32"))
             del g
             og = torch.empty_like(vg)
-            ms = timed(lambda: sa.sa_graph_attn_fwd(cq, ck, vg, bias, p["tau"], p["local"],
-                                                    p["n_pow2"], out=og), reps)
+            gfn = lambda: sa.sa_graph_attn_fwd(cq, ck, vg, bias, p["tau"], p["local"],  # noqa: E731
+                                               p["n_pow2"], out=og)
+            ms = timed_cold(gfn, reps)
+            ms_warm = timed(gfn, reps)
             edges = sum(min(t, p["local"]) + 1 + sum(1 for j in range(p["n_pow2"])
                                                       if (1 << j) > p["local"] and (1 << j) <= t)
                         for t in range(T2))
             comp = T2 * H2 * (2 * D2 * 2 + 2 * 3 * 2)
             rows[name] = {
-                "ms": ms, "query_tokens_per_s": T2 / (ms * 1e-3),
+                "ms": ms, "warm_ms": ms_warm, "timing": "cold",
+                "query_tokens_per_s": T2 / (ms * 1e-3),
                 "compulsory_bytes": comp, "compulsory_GBps": comp / (ms * 1e-3) / 1e9,
                 "edge_bytes": edges * H2 * (D2 * 2 + 6),
                 "edge_GBps": edges * H2 * (D2 * 2 + 6) / (ms * 1e-3) / 1e9,
@@ -576,6 +690,8 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         qd = to_dev(dx["q"], "bf16")
         kc = to_dev(dx["kcache"], "bf16")
         vc = to_dev(dx["vcache"], "bf16")
+        if keep is not None:
+            keep["w5"] = dx
         del dx
         lens = torch.full((p["B"],), p["L"], dtype=torch.int32, device=dev)
         t_pool = timed(lambda: sa.sa_block_meanpool(kc, lens, p["block"]), 3)
@@ -584,8 +700,11 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
                                              p["top_blocks"], p["window"], 0)
         ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         od = torch.empty_like(qd)
-        ms = timed(lambda: sa.sa_sparse_decode(qd, kc, vc, kbar, lens, p["block"], p["top_blocks"],
-                                               p["window"], p["scale"], workspace=ws, out=od), 50)
+        dfn = lambda: sa.sa_sparse_decode(qd, kc, vc, kbar, lens, p["block"],  # noqa: E731
+                                          p["top_blocks"], p["window"], p["scale"],
+                                          workspace=ws, out=od)
+        ms = timed_cold(dfn, 30)
+        ms_warm = timed(dfn, 50)
         _, sel = sa.sa_sparse_decode(qd, kc, vc, kbar, lens, p["block"], p["top_blocks"], p["window"],
                                      p["scale"], workspace=ws, return_sel=True)
         wstart = p["L"] - p["window"]
@@ -599,7 +718,9 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         nb = p["L"] // p["block"]
         dbytes = p["B"] * nb * p["D"] * 4 + u_tok * 2 * p["D"] * 2 + p["B"] * p["Hq"] * p["D"] * 2 * 2
         rows["sparse_decode_b32_128k"] = {
-            "us_per_step": ms * 1e3, "tokens_per_s": p["B"] / (ms * 1e-3),
+            "us_per_step": ms * 1e3, "warm_us_per_step": ms_warm * 1e3, "timing": "cold",
+            "warm_hbm_frac": dbytes / (ms_warm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": p["B"] / (ms * 1e-3),
             "algorithmic_bytes_per_step": dbytes, "achieved_GBps": dbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "n_splits": sa.sa_sparse_decode_auto_splits(p["B"], p["L"], p["Hkv"], p["block"],
@@ -635,10 +756,12 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
             "combine": lambda: sa.sa_nsa_combine(ocd[:, None], osd[:, None], owd[:, None], gd,
                                                  out=ond[:, None]),
         }
-        dpart_us = {name: timed(fn, 20) * 1e3 for name, fn in dparts.items()}
-        t_nd = timed(lambda: [fn() for fn in dparts.values()], 20)
+        dpart_us = {name: timed_cold(fn, 20) * 1e3 for name, fn in dparts.items()}
+        t_nd = timed_cold(lambda: [fn() for fn in dparts.values()], 20)
+        t_nd_warm = timed(lambda: [fn() for fn in dparts.values()], 20)
         rows["nsa_decode_b32_128k"] = {
-            "us_per_step": t_nd * 1e3, "tokens_per_s": p["B"] / (t_nd * 1e-3), "parts_us": dpart_us,
+            "us_per_step": t_nd * 1e3, "warm_us_per_step": t_nd_warm * 1e3, "timing": "cold",
+            "tokens_per_s": p["B"] / (t_nd * 1e-3), "parts_us": dpart_us,
             "compressed_splits": ns_c,
             "bf16_meanpool_ms_once_per_cache": t_pool16,
         }
@@ -658,7 +781,11 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
         for l in range(4):
             lx = sa_synth.attn_inputs(sa_synth.layer_seed(l), 1, T, p["Hq"], p["Hkv"], p["D"], "bf16")
             layers.append(tuple(to_dev(lx[n], "bf16") for n in ("q", "k", "v")))
+            if keep is not None:
+                keep.setdefault("w4_layers", []).append(lx)
             del lx
+        if keep is not None:
+            keep["w4_index"] = xi
         chunk = 32768
         ws = torch.empty(sa.sa_indexer_topk_workspace(1, T, p["H_I"], p["D_I"], T - chunk, T,
                                                       p["topk"]), dtype=torch.uint8, device=dev)
@@ -674,38 +801,68 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64):
             qq, kk, vv = layers[l]
             sa.sa_sparse_attn_fwd(qq, kk, vv, idx, p["window"], p["scale"], out=o4)
 
-        t_index = timed(index_once, 2)
-        t_attn = [timed(lambda l=l: attn(l), 3) for l in range(4)]
+        t_index = timed_cold(index_once, 3)
+        t_attn = [timed_cold(lambda l=l: attn(l), 3) for l in range(4)]
         reuse = t_index + sum(t_attn)
         no_reuse = 4 * t_index + sum(t_attn)
         rows["indexcache_FSSS_128k"] = {
-            "index_ms": t_index, "attn_ms_per_layer": t_attn,
+            "timing": "cold", "index_ms": t_index, "attn_ms_per_layer": t_attn,
             "four_layers_ms_with_reuse": reuse, "four_layers_ms_indexing_every_layer": no_reuse,
             "indexer_time_saved_ms": 3 * t_index, "saved_frac": 3 * t_index / no_reuse,
             "attn_query_tokens_per_s": T / (sum(t_attn) / 4 * 1e-3),
         }
         del ws, idx, layers, qi, ki, w, o4
         torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
     return rows
 
 
-def cpu_baseline(np, sa_synth, x, p, seconds):
-    """The float64 oracle, as it stands, on a bounded sample of the 64K workload: rows
-    drawn uniformly from [k + W, T), each through indexer scores, exact top-k and
-    dense-masked attention.  Scaled to query tokens per second."""
-    import oracle.reference as orc
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = os.cpu_count()
+        return os.cpu_count()
+
+
+def cpu_baseline(np, sa_synth, x, p, seconds, which="all", host=None):
+    """The float64 oracle, as it stands, on the machine's host cores.  The headline entry is
+    the 64K workload on rows drawn uniformly from [0, T) (each through indexer scores,
+    exact top-k and dense-masked attention), for about ``seconds`` s, scaled to query
+    tokens per second.  ``workloads`` holds every workload: the 2K top-k prefill and the
+    32 x 128K decode run in full; the 16K graph attention and the 128K index reuse
+    (indexer + top-k once, four attention layers) on uniformly sampled rows, their
+    whole-workload seconds extrapolated from the rate and labelled so.  ``host`` may
+    hold the host inputs of workloads 4 and 5 already drawn for the GPU rows."""
+    import oracle.reference as orc
+    host = host or {}
+    threads = _blas_threads()
     T, k, W = p["T"], p["topk"], p["window"]
+
+    def entry(name, n, el, unit_n, unit, total, extrapolated, sample):
+        rate = unit_n / el
+        return {"workload": name, "value": rate, "unit": unit, "seconds": el, "units_timed": unit_n,
+                "whole_workload_seconds": total / rate, "extrapolated": extrapolated,
+                "sample": sample}
+
     g = sa_synth.rng(4242)
     done = 0
     idx = np.full((1, T, k), -1, np.int32)
     t0 = time.perf_counter()
     while True:
-        rows = sorted(g.integers(k + W, T, size=8).tolist())
+        rows = sorted(g.integers(0, T, size=8).tolist())
         for t in rows:
             idx[0, t] = orc.topk_select_row(orc.indexer_scores_row(x["qi"], x["ki"], x["w"], 0, t), k)
         orc.sparse_attn(x["q"], x["k"], x["v"], idx, W, p["scale"], rows)
@@ -713,9 +870,91 @@ def cpu_baseline(np, sa_synth, x, p, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": done / el, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} rows drawn uniformly from [k+W, T) of the 64K prefill workload "
-                      f"(indexer row + exact top-k + dense-masked float64 attention), {el:.1f} s"}
+    del idx
+    w3 = entry(sa_synth.WORKLOADS[3].name, done, el, done, "query-tokens/s", T, True,
+               f"{done} rows drawn uniformly from [0, T) of the 64K prefill workload "
+               f"(indexer row + exact top-k + dense-masked float64 attention), {el:.1f} s")
+    res = {"value": w3["value"], "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": w3["sample"], "cpu_model": _cpu_model(), "blas_threads": threads,
+           "workloads": {"3": w3}}
+    if which != "all":
+        return res
+
+    log("CPU oracle: workload 1 (all 2048 rows)")
+    W1 = sa_synth.WORKLOADS[1]
+    p1 = W1.params
+    x1 = sa_synth.prefill_inputs(W1.seed, 1, p1["T"], p1["Hq"], p1["Hkv"], p1["D"], p1["H_I"],
+                                 p1["D_I"], "f32")
+    t0 = time.perf_counter()
+    sc = orc.indexer_scores(x1["qi"], x1["ki"], x1["w"])
+    idx1 = orc.topk_select(sc, p1["topk"], 1, p1["T"])
+    orc.sparse_attn(x1["q"], x1["k"], x1["v"], idx1, p1["window"], p1["scale"])
+    el = time.perf_counter() - t0
+    res["workloads"]["1"] = entry(W1.name, p1["T"], el, p1["T"], "query-tokens/s", p1["T"], False,
+                                  "every row: indexer scores, exact top-k, dense-masked attention")
+    del x1, sc, idx1
+
+    log("CPU oracle: workload 2 (sampled rows)")
+    W2 = sa_synth.WORKLOADS[2]
+    p2 = W2.params
+    x2 = sa_synth.graph_inputs(W2.seed, 1, p2["T"], p2["H"], p2["D"], "bf16")
+    g2 = sa_synth.rng(4243)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        rows = sorted(g2.integers(0, p2["T"], size=16).tolist())
+        orc.graph_attn(x2["cq"], x2["ck"], x2["v"], x2["bias"], p2["tau"], p2["local"],
+                       p2["n_pow2"], rows)
+        done += len(rows)
+        el = time.perf_counter() - t0
+        if el >= 8.0:
+            break
+    res["workloads"]["2"] = entry(W2.name, done, el, done, "query-tokens/s", p2["T"], True,
+                                  f"{done} rows drawn uniformly from [0, T) (dense logits over "
+                                  f"s <= t under the fixed-graph mask), {el:.1f} s")
+    del x2
+
+    log("CPU oracle: workload 4 (1024 sampled rows, four layers)")
+    W4 = sa_synth.WORKLOADS[4]
+    p4 = W4.params
+    T4 = p4["T"]
+    xi = host.get("w4_index") or sa_synth.indexer_inputs(W4.seed, 1, T4, p4["H_I"], p4["D_I"],
+                                                         "bf16")
+    layers = host.get("w4_layers") or [
+        sa_synth.attn_inputs(sa_synth.layer_seed(l), 1, T4, p4["Hq"], p4["Hkv"], p4["D"], "bf16")
+        for l in range(4)]
+    g4 = sa_synth.rng(4244)
+    rows4 = sorted(g4.integers(0, T4, size=1024).tolist())
+    idx4 = np.full((1, T4, p4["topk"]), -1, np.int32)
+    t0 = time.perf_counter()
+    for i in range(0, len(rows4), 128):
+        rows = rows4[i:i + 128]
+        for t in rows:
+            idx4[0, t] = orc.topk_select_row(orc.indexer_scores_row(xi["qi"], xi["ki"], xi["w"], 0, t),
+                                             p4["topk"])
+        for lay in layers:
+            orc.sparse_attn(lay["q"], lay["k"], lay["v"], idx4, p4["window"], p4["scale"], rows)
+        log(f"  workload 4: {i + len(rows)} rows, {time.perf_counter() - t0:.1f} s")
+    el = time.perf_counter() - t0
+    res["workloads"]["4"] = entry(W4.name, len(rows4), el, len(rows4), "query-tokens/s", T4, True,
+                                  f"{len(rows4)} rows drawn uniformly from [0, T): indexer row + "
+                                  f"exact top-k once, then dense-masked attention in each of the "
+                                  f"4 layers (F,S,S,S), {el:.1f} s; whole-workload seconds "
+                                  f"extrapolated as T / rate")
+    del xi, layers, idx4
+
+    log("CPU oracle: workload 5 (all 32 sequences)")
+    W5 = sa_synth.WORKLOADS[5]
+    p5 = W5.params
+    dx = host.get("w5") or sa_synth.decode_inputs(W5.seed, p5["B"], p5["L"], p5["Hq"], p5["Hkv"],
+                                                  p5["D"], "bf16")
+    t0 = time.perf_counter()
+    orc.sparse_decode(dx["q"], dx["kcache"], dx["vcache"], dx["lens"], p5["block"],
+                      p5["top_blocks"], p5["window"], p5["scale"])
+    el = time.perf_counter() - t0
+    res["workloads"]["5"] = entry(W5.name, p5["B"], el, p5["B"], "tokens/s", p5["B"], False,
+                                  "all 32 sequences: block means, block scores and top-16, "
+                                  "dense-masked attention over the 131,072-token cache")
+    return res
 
 
 if __name__ == "__main__":

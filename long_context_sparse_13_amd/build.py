@@ -1,4 +1,5 @@
-"""Compile the HIP kernels and the C ABI into long_context_sparse_13_amd/libsa.so (gfx950).
+"""Compile the HIP kernels and the C ABI into long_context_sparse_13_amd/libsa.so (gfx950),
+and the memory read probe that bench.py times into libsa_probe.so.
 
 Run ``python -m long_context_sparse_13_amd.build`` (or ``__graft_entry__.build()``).
 Objects go to ``_build/`` at the repository root; the shared library is written
@@ -17,6 +18,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsa.so")
+# the memory-hierarchy read probe that bench.py times (measurement only, not libsa)
+PROBE = os.path.join(PKG, "probe")
+PROBE_OUT = os.path.join(PKG, "libsa_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("SA_OFFLOAD_ARCH", "gfx950")
 
@@ -64,19 +68,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+def probe_sources():
+    return sorted(os.path.join(PROBE, f) for f in os.listdir(PROBE) if f.endswith(".hip"))
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, psrcs = sources(), probe_sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[: len(srcs)], OUT)
+    _link(objs[len(srcs):], PROBE_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PROBE_OUT}")
     return OUT
 
 

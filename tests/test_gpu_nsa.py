@@ -134,14 +134,15 @@ def test_nsa_prefill_pipeline_vs_oracle():
     rows = list(range(0, 200, 3)) + list(range(200, T, 17)) + [T - 1]
     want, _, sel = orc.nsa_prefill(x["q"], x["k"], x["v"], gates, block, top, W, scale, rows)
     gi = host(idx)[0]
-    bad = 0
+    okb, _ = _oracle_pool(x, T, block)
+    # every row's block set is exact or a near tie of its boundary block scores
+    n_exempt = _check_blocks(gi, sel[0], x["q"][0], okb[0], block, top, rows)
+    assert n_exempt <= 2
     for r, t in enumerate(rows):
         wb = sorted(int(j) for j in sel[0, r] if j >= 0)
         if sorted(set(int(s) // block for s in gi[t] if s >= 0)) != wb:
-            bad += 1  # a near tie between blocks: the branch legitimately differs
-            continue
+            continue  # an exempt near tie: the selected branch legitimately differs
         assert np.abs(out[0, t] - want[0, r]).max() < BF16_TOL, t
-    assert bad <= 2
 
 
 # ------------------------------------------------------------------------------ decode

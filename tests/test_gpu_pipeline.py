@@ -91,3 +91,44 @@ def test_bf16_prefill_64k_sampled():
                       + g.integers(k + W, T, size=48).tolist() + list(range(T - 4, T))))
     n_ok, n_ex, err = compare(x, "bf16", k, W, p["scale"], idx, out, rows)
     print(f"exact rows {n_ok}, exempt rows {n_ex}, max err {err:.3g}")
+
+
+@pytest.mark.slow
+def test_bench_step_64k_fused_vs_oracle():
+    """The step bench.py times, in its launch configuration: the 64K DSA workload (seed
+    1003), indices from sa_indexer_topk over two 32,768-row chunks sharing one workspace
+    sized for the last (longest) chunk, then sa_sparse_attn_fwd over all 65,536 rows.
+    Indices on every row t < k + W and on sampled rows (the chunk boundary 32,767 / 32,768,
+    a seeded uniform draw, the last rows) against the oracle's top-k (bit-exact outside
+    near ties); outputs on the sampled rows within the bf16 tolerance; no row needed the
+    full recompute."""
+    import torch
+    p = sa_synth.WORKLOADS[3].params
+    T, k, W, scale = p["T"], p["topk"], p["window"], p["scale"]
+    HI, DI = p["H_I"], p["D_I"]
+    chunk = 32768
+    note("bench step: fused indices (2 x 32768 rows) + sparse attention, T=65536 seed 1003")
+    x = sa_synth.prefill_inputs(1003, 1, T, p["Hq"], p["Hkv"], p["D"], HI, DI, "bf16")
+    qi, ki, w = dev(x["qi"], "bf16"), dev(x["ki"], "bf16"), dev(x["w"], "f32")
+    ws = torch.empty(sa.sa_indexer_topk_workspace(1, T, HI, DI, T - chunk, T, k),
+                     dtype=torch.uint8, device="cuda")
+    idx = torch.full((1, T, k), -1, dtype=torch.int32, device="cuda")
+    recomputed = []
+    for r0 in range(0, T, chunk):
+        sa.sa_indexer_topk(qi, ki, w, k, r0, min(T, r0 + chunk), idx, ws)
+        recomputed.append(int(ws[:4].view(torch.int32).item()))
+    del qi, ki, w, ws
+    out = sa.sa_sparse_attn_fwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"),
+                                idx, W, scale)
+    gi, go = host(idx), host(out)
+    assert recomputed == [0, 0], recomputed
+    # rows t < k + W: the first k rows select every earlier key; check them all
+    for t in range(k):
+        assert np.array_equal(gi[0, t, : t + 1], np.arange(t + 1)), t
+        assert (gi[0, t, t + 1:] == -1).all(), t
+    g = sa_synth.rng(78)
+    rows = sorted(set(list(range(0, k + W, 61)) + list(range(k - 2, k + W))[::9]
+                      + [k - 1, k, k + W - 1, chunk - 2, chunk - 1, chunk, chunk + 1]
+                      + g.integers(k + W, T, size=40).tolist() + list(range(T - 3, T))))
+    n_ok, n_ex, err = compare(x, "bf16", k, W, scale, gi, go, rows)
+    print(f"exact rows {n_ok}, exempt rows {n_ex}, max err {err:.3g}")

@@ -268,6 +268,27 @@ int sa_sparse_decode(const void* q, const void* kcache, const void* vcache, cons
                      float* lse, int32_t* sel_blocks, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/*
+ * sa_sparse_decode without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * sa_sparse_decode (the same kernels run); the workspace is instead a scratch array inside
+ * the library, one per GPU, of sa_sparse_decode_noalloc_max_scratch() bytes (16 MiB),
+ * held from the first call on that GPU until the process ends.  Sizes whose
+ * sa_sparse_decode_workspace(...) exceeds it return SA_ERR_UNSUPPORTED (nothing launched).
+ * The stream must belong to the current device.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap in time on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller; calls ordered on one stream are safe.
+ */
+int sa_sparse_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                             const float* kbar, const int32_t* lens, int B, int Lmax, int Hq,
+                             int Hkv, int D, int block, int top_blocks, int window, int n_splits,
+                             float scale, int dtype, void* out, float* lse, int32_t* sel_blocks,
+                             void* stream);
+
+/* Bytes of scratch sa_sparse_decode_noalloc holds per GPU (its size limit). */
+size_t sa_sparse_decode_noalloc_max_scratch(void);
+
 /* Workspace bytes sa_sparse_decode needs for these sizes (0 on invalid sizes). */
 size_t sa_sparse_decode_workspace(int B, int Lmax, int Hq, int Hkv, int D, int block,
                                   int top_blocks, int window, int n_splits);

@@ -21,7 +21,8 @@ __all__ = [
     "sa_indexer_scores", "sa_topk_select", "sa_sparse_attn_fwd", "sa_sparse_attn_fwd_rows",
     "sa_graph_attn_fwd",
     "sa_block_meanpool", "sa_sparse_decode", "sa_sparse_decode_workspace",
-    "sa_sparse_decode_auto_splits", "sa_version",
+    "sa_sparse_decode_auto_splits", "sa_sparse_decode_noalloc",
+    "sa_sparse_decode_noalloc_max_scratch", "sa_version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +62,11 @@ _SIGS = {
                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_float, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _c_size_t, _c_void_p]),
+    "sa_sparse_decode_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                          _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_float, _c_int, _c_void_p, _c_void_p,
+                                          _c_void_p, _c_void_p]),
+    "sa_sparse_decode_noalloc_max_scratch": (_c_size_t, []),
     "sa_sparse_decode_workspace": (_c_size_t, [_c_int] * 9),
     "sa_sparse_decode_auto_splits": (_c_int, [_c_int] * 6),
     "sa_cmp_attn_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
@@ -421,6 +427,56 @@ def sa_sparse_decode(q, kcache, vcache, kbar, lens, block: int, top_blocks: int,
                                 _dtype_code(q), _p(out), _p(lse), _p(sel), _p(workspace),
                                 workspace.numel(), _stream(q.device))
     _check("sa_sparse_decode", rc)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_sel:
+        res.append(sel)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def sa_sparse_decode_noalloc_max_scratch() -> int:
+    return int(lib().sa_sparse_decode_noalloc_max_scratch())
+
+
+def sa_sparse_decode_noalloc(q, kcache, vcache, kbar, lens, block: int, top_blocks: int,
+                             window: int, scale: float, n_splits: int = 0, out=None, lse=None,
+                             sel=None, return_lse: bool = False, return_sel: bool = False):
+    """sa_sparse_decode with the library's per-GPU scratch instead of a workspace: the C
+    entry point allocates nothing (outputs are allocated here when not given).  Calls that
+    overlap in time on one GPU race on the scratch."""
+    torch = _torch()
+    _dev(q, "q"); _dev(kcache, "kcache", q.dtype); _dev(vcache, "vcache", q.dtype)
+    _dev(kbar, "kbar", torch.float32); _dev(lens, "lens", torch.int32)
+    _shape(q, "q", None, None, None)
+    B, Hq, D = q.shape
+    _shape(kcache, "kcache", B, None, None, D)
+    _, Lmax, Hkv, _ = kcache.shape
+    _shape(vcache, "vcache", B, Lmax, Hkv, D)
+    _shape(kbar, "kbar", B, Lmax // block, Hkv, D)
+    _shape(lens, "lens", B)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _shape(out, "out", B, Hq, D)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", B, Hq)
+    if return_sel and sel is None:
+        sel = torch.empty((B, Hkv, top_blocks), dtype=torch.int32, device=q.device)
+    if sel is not None:
+        _dev(sel, "sel", torch.int32)
+        _shape(sel, "sel", B, Hkv, top_blocks)
+    _same_device("sa_sparse_decode_noalloc", q, kcache, vcache, kbar, lens, out, lse, sel)
+    rc = lib().sa_sparse_decode_noalloc(_p(q), _p(kcache), _p(vcache), _p(kbar), _p(lens), B,
+                                        Lmax, Hq, Hkv, D, block, top_blocks, window, n_splits,
+                                        float(scale), _dtype_code(q), _p(out), _p(lse), _p(sel),
+                                        _stream(q.device))
+    _check("sa_sparse_decode_noalloc", rc)
     res = [out]
     if return_lse:
         res.append(lse)

@@ -25,6 +25,7 @@
 #include "sa_launch.h"
 #include "select.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace sa {
@@ -538,6 +539,40 @@ static void launch_decode_d(const void* q, const void* kcache, const void* vcach
                        (const uint16_t*)q, (const uint16_t*)kcache, (const uint16_t*)vcache, lens,
                        Lmax, Hq, Hkv, block, top_blocks, window, n_splits, nwg * cpw, sl2,
                        ws.cand, ws.partials, ws.counters, sel_out, (uint16_t*)out, lse);
+}
+
+// ------------------------------------------------------------------------ no-alloc scratch
+// The workspace of sa_sparse_decode_noalloc: a file-scope device array (one copy per GPU,
+// held until the process ends) instead of caller memory.  Its device address is looked
+// up once per device with that device current, and that address, never the array's host
+// name, is what host code hands to kernels.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_sparse_decode(const void* q, const void* kcache, const void* vcache,

@@ -593,4 +593,36 @@ int sa_sparse_decode(const void* q, const void* kcache, const void* vcache, cons
   }
 }
 
+int sa_sparse_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                             const float* kbar, const int32_t* lens, int B, int Lmax, int Hq,
+                             int Hkv, int D, int block, int top_blocks, int window, int n_splits,
+                             float scale, int dtype, void* out, float* lse, int32_t* sel_blocks,
+                             void* stream) {
+  try {
+    int ns = 0;
+    const int rc = decode_args(q, kcache, vcache, kbar, lens, B, Lmax, Hq, Hkv, D, block,
+                               top_blocks, window, n_splits, dtype, out, &ns);
+    if (rc != SA_OK) return rc;
+    const size_t need = sa::decode_workspace_bytes(B, Lmax, Hq, Hkv, D, block, top_blocks, ns);
+    if (need > sa::decode_scratch_bytes())
+      return fail(SA_ERR_UNSUPPORTED,
+                  "sa_sparse_decode_noalloc: these sizes need %zu bytes of scratch, more than the "
+                  "%zu it holds (use sa_sparse_decode with a workspace)",
+                  need, sa::decode_scratch_bytes());
+    void* scratch = nullptr;
+    const hipError_t e = sa::decode_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "sa_sparse_decode_noalloc: scratch address");
+    const sa::DecodeWs ws = sa::decode_workspace_carve(scratch, B, Lmax, Hq, Hkv, D, block,
+                                                       top_blocks, ns);
+    return hip_status(sa::launch_sparse_decode(q, kcache, vcache, kbar, lens, B, Lmax, Hq, Hkv, D,
+                                               block, top_blocks, window, ns, scale, out, lse,
+                                               sel_blocks, ws, as_stream(stream)),
+                      "sa_sparse_decode_noalloc launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_sparse_decode_noalloc: unexpected exception");
+  }
+}
+
+size_t sa_sparse_decode_noalloc_max_scratch(void) { return sa::decode_scratch_bytes(); }
+
 }  // extern "C"

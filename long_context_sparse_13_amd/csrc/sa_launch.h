@@ -80,6 +80,10 @@ hipError_t launch_sparse_decode(const void* q, const void* kcache, const void* v
                                 int Hkv, int D, int block, int top_blocks, int window,
                                 int n_splits, float scale, void* out, float* lse,
                                 int32_t* sel_out, const DecodeWs& ws, hipStream_t st);
+// The no-alloc decode's scratch: its size, and its device address on the current device
+// (looked up once per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 
 // NSA branches (prefill) and the gated combine.
 size_t cmp_attn_workspace_bytes(int B, int T, int Hkv, int D, int block);

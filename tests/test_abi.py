@@ -227,3 +227,21 @@ def test_bwd_validation_and_workspace(L):
     assert "workspace" in _err(L)
     assert b(*args(ws=MIS, n=wall)) == 1                # alignment
     assert b(*args(T=(1 << 20) + 1, Hq=1, D=64, ws=P, n=1 << 40)) == 2
+
+
+def test_decode_noalloc_validation(L):
+    """The allocation-free decode refuses, on the host, sizes whose workspace exceeds its
+    per-GPU scratch, and validates like sa_sparse_decode."""
+    f = L.sa_sparse_decode_noalloc
+    cap = L.sa_sparse_decode_noalloc_max_scratch()
+    assert cap == 16 << 20
+    assert L.sa_sparse_decode_workspace(4096, 131072, 16, 1, 128, 64, 16, 512, 64) > cap
+    args = (P, P, P, P, P)
+    assert f(*args, 4096, 131072, 16, 1, 128, 64, 16, 512, 64, 0.1, 1, P, None, None, None) == 2
+    assert "scratch" in _err(L)
+    assert f(*args, 2, 1024, 16, 1, 96, 64, 16, 512, 0, 0.1, 1, P, None, None, None) == 2   # D
+    assert f(*args, 2, 1024, 16, 3, 128, 64, 16, 512, 0, 0.1, 1, P, None, None, None) == 1  # Hq % Hkv
+    assert f(*args, 2, 1024, 16, 1, 128, 64, 0, 512, 0, 0.1, 1, P, None, None, None) == 1   # top_blocks
+    assert f(*args, 2, 1024, 16, 1, 128, 64, 16, 512, 65, 0.1, 1, P, None, None, None) == 1  # splits
+    assert f(P, P, P, P, P, 2, 1024, 16, 1, 128, 64, 16, 512, 0, 0.1, 0, P, None, None, None) == 2  # f32
+    assert f(P, P, MIS, P, P, 2, 1024, 16, 1, 128, 64, 16, 512, 0, 0.1, 1, P, None, None, None) == 1

@@ -143,6 +143,21 @@ struct IdxWave {
     for (int c = 0; c < KV; ++c) bk.v[c] = ld_reg(kp + row_off(c, grp));
   }
 
+  // A block of consecutive key rows staged in LDS: row kk at kk * RB bytes, its 16-byte
+  // pieces XOR-swizzled by the row (piece p at p ^ (kk & SWM)), so that the row-wise
+  // writes of the cooperative load and the 16 rows read by each lane group's B operands
+  // land on distinct banks.
+  static constexpr int RB = DI * EB;                      // bytes per key row
+  static constexpr int SWM = (RB / 16 >= 8 ? 8 : RB / 16) - 1;
+  __device__ static int lds_off(int kk, int off) {
+    return kk * RB + (((off >> 4) ^ (kk & SWM)) << 4) + (off & 15);
+  }
+  // B operand registers for this lane from row kk of a staged block.
+  __device__ static void lds_keys(const unsigned char* blk, int kk, int grp, Keys& bk) {
+#pragma unroll
+    for (int c = 0; c < KV; ++c) bk.v[c] = ld_reg(blk + lds_off(kk, row_off(c, grp)));
+  }
+
   __device__ void scores(const Keys& bk, float (&sc)[NSC]) const {
     f32x4 acc[TM];
 #pragma unroll

@@ -235,9 +235,11 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
   for (int c = group; c < wave_chunks; c += kIdxGroups) {
     const int s_lo = c * kIdxChunk;
     const int s_hi = min(s_lo + kIdxChunk, t_last + 1);
-    uint32_t cnt_s[IW::ROWS];  // list length of row rr in this chunk so far (uniform)
+    // list lengths of this chunk so far (uniform; <= 256): rows 2i and 2i + 1 in the low and
+    // high halves of cnt2[i], so the 32 counts take 16 scalar registers
+    uint32_t cnt2[IW::ROWS / 2];
 #pragma unroll
-    for (int rr = 0; rr < IW::ROWS; ++rr) cnt_s[rr] = 0u;
+    for (int i = 0; i < IW::ROWS / 2; ++i) cnt2[i] = 0u;
     typename IW::Keys bk;
     IW::load_keys(kib, min(s_lo + n, T - 1), grp, bk);
     for (int j0 = s_lo; j0 < s_hi; j0 += SB) {
@@ -274,19 +276,21 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
           const float th = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr_v), rr));
           const bool hit = vals[rr] >= th && (!DIAG || s <= t0 + rr);
           const uint64_t m = ballot(hit);
-          const uint32_t at = (uint32_t)rr * rstride8 + (cnt_s[rr] + (uint32_t)lanes_below(m)) * 8u;
+          const uint32_t cnt = (cnt2[rr >> 1] >> (16 * (rr & 1))) & 0xffffu;
+          const uint32_t at = (uint32_t)rr * rstride8 + (cnt + (uint32_t)lanes_below(m)) * 8u;
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(vals[rr]), (uint32_t)s}, lists,
                                                hit ? at : 0xffffffffu, 0, 0);
-          cnt_s[rr] += (uint32_t)__popcll(m);
+          cnt2[rr >> 1] += (uint32_t)__popcll(m) << (16 * (rr & 1));
         }
       };
       if (j0 + SB - 1 > t0) compact(std::true_type{});  // some key follows some row
       else compact(std::false_type{});
       wave_lds_sync();
     }
-    uint32_t cnt_v = 0u;  // lane rr takes cnt_s[rr]
+    uint32_t cnt_v = 0u;  // lane rr takes the count of row rr
 #pragma unroll
-    for (int rr = 0; rr < IW::ROWS; ++rr) cnt_v = lane == rr ? cnt_s[rr] : cnt_v;
+    for (int rr = 0; rr < IW::ROWS; ++rr)
+      cnt_v = lane == rr ? (cnt2[rr >> 1] >> (16 * (rr & 1))) & 0xffffu : cnt_v;
     if (my_ok) counts[(row0 + lane) * nch + c] = (uint16_t)cnt_v;
   }
 }

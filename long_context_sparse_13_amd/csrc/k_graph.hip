@@ -11,14 +11,21 @@
 // graph_attn_block<D> (bf16, D in {64, 128}, local <= 64): one workgroup per (batch,
 // block of 64 tokens, head).  The block's local neighbourhoods form a band: the rows
 // [t0 - local, t0 + 64) hold every neighbour at offset <= local of every token of the
-// block, so V^T of the band is staged once in LDS and the band part of P.V runs on the
-// 16x16x32 bf16 MFMA (probabilities rounded to bf16, the normaliser summed from the
-// same rounded values).  Four workgroups per CU (the LDS allows four; at D = 64 the
-// register cap of four wavefronts per SIMD costs a 12-byte spill and gains 11 %).  The far neighbours (offsets 2^j > local) are one row per
-// token and offset; their contributions are added on the vector units from coalesced
-// row loads.  Logits and softmax are float32.  Items are handed to the XCDs in
-// contiguous (block, head) ranges, so the rows a block shares with the blocks just
-// before it are served from that XCD's L2.
+// block, so the band's V rows are staged once in LDS (row-major, 16-byte writes) and the
+// band part of P.V runs on the 16x16x32 bf16 MFMA, its V^T operand read with gfx950's
+// transposing LDS read (probabilities rounded to bf16, the normaliser summed from the
+// same rounded values).  The far neighbours (offsets 2^j > local) are one row per token
+// and offset; their weights are rounded to bf16 too and their contributions added two
+// offsets at a time with the bf16 dot-product instruction (v_dot2c_f32_bf16: exact bf16
+// products, float32 sums).  Logits and softmax are float32.  The kernel is bound by
+// instruction issue more than by memory, so its rows are read through buffer resources
+// (one per tensor, at this batch's and head's row 0) with 32-bit offsets — rows that do
+// not exist get an offset past the resource and read as zero, with no branch — and the
+// band loops run only as far as `local` needs.  At D = 64 four workgroups per CU (the
+// LDS allows four); at D = 128 the LDS holds two, so the register cap asks for two
+// wavefronts per SIMD only.  Items are handed to the XCDs in contiguous (block, head)
+// ranges, so the rows a block shares with the blocks just before it are served from that
+// XCD's L2.
 //
 // graph_attn<BF> (any dtype, D % 8 == 0, the general case): one wavefront per (batch,
 // token, group of 64 eight-element chunks of the token's H*D values).  A lane owns one
@@ -122,12 +129,20 @@ __global__ __launch_bounds__(64) void graph_attn(const void* __restrict__ cq,
 
 constexpr int kGTB = 64;   // tokens per block
 constexpr int kGBR = 128;  // band rows held (block + local, local <= 64)
-constexpr int kGPR = kGBR + 8;  // LDS row pitch of P and V^T (bf16), 16-byte multiple
+constexpr int kGPR = kGBR + 8;  // LDS row pitch of P (bf16), 16-byte multiple
 constexpr int kGFar = 8;   // far offsets (2^j > local) handled: n_pow2 - #{2^j <= local} <= 8
 constexpr int kGLoc = 17;  // band logits per thread: (local + 1) / 4 rounded up, local <= 64
+constexpr uint32_t kGOut = 0x80000000u;  // a buffer offset past every resource: loads give 0
+
+// Byte offset of row s in a buffer resource whose rows are `pitch` bytes apart, or kGOut
+// when the row does not exist (s < 0 or !ok).  Rows of one batch span less than 2 GB
+// (checked on the host), so kGOut plus any in-row offset stays out of range.
+__device__ __forceinline__ uint32_t g_row(int s, bool ok, int pitch) {
+  return ok && s >= 0 ? (uint32_t)s * (uint32_t)pitch : kGOut;
+}
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void graph_attn_block(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void graph_attn_block(
     const uint16_t* __restrict__ cq, const uint16_t* __restrict__ ck,
     const uint16_t* __restrict__ v, const float* __restrict__ bias, float tau_log2, int B, int T,
     int H, int local, int n_pow2, uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -135,136 +150,136 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
   constexpr int CPT = DC / 4;            // output chunks per thread (4 threads per token)
   constexpr int VPT = kGBR * DC / 256;   // band V chunks loaded per thread
   constexpr int PBYTES = kGTB * (D + 4) * 4 > kGTB * kGPR * 2 ? kGTB * (D + 4) * 4 : kGTB * kGPR * 2;
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D][kGPR];  // V^T of the band
+  // band V rows, row-major with a pitch of 2D + 32 bytes: the 4 rows x 8 bytes named by
+  // each 16 lanes of a transposing read fall on distinct banks
+  constexpr int VROW = 2 * D + 32;
+  __shared__ __attribute__((aligned(16))) unsigned char vrow[kGBR * VROW];
   // band probabilities (bf16, [token][kGPR]), then the band P.V (float, [token][D + 4])
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[PBYTES];
-  __shared__ float cqs[kGTB][3], cks[kGBR][3];
+  __shared__ f32x4 cqs[kGTB], cks[kGBR];  // coordinates (x, y, z, unused)
   uint16_t(*pb)[kGPR] = reinterpret_cast<uint16_t(*)[kGPR]>(pbuf);
   float* ob = reinterpret_cast<float*>(pbuf);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nblk = (T + kGTB - 1) / kGTB;
-  const int64_t item = xcd_item(blockIdx.x, (int64_t)B * nblk * H);
+  // items (block, head) of batch blockIdx.y, in contiguous ranges per XCD (fewer than
+  // 2^31 of them: checked on the host, so the index arithmetic is 32-bit)
+  const int item = (int)xcd_item(blockIdx.x, (int64_t)nblk * H);
   if (item < 0) return;
-  const int h = (int)(item % H);
-  const int blk = (int)((item / H) % nblk);
-  const int b = (int)(item / ((int64_t)H * nblk));
+  const int h = (int)((uint32_t)item % (uint32_t)H);
+  const int blk = (int)((uint32_t)item / (uint32_t)H);
+  const int b = blockIdx.y;
   const int t0 = blk * kGTB;
   const int nt = min(kGTB, T - t0);  // tokens of this block
   const int sb = t0 - local;         // position of band row 0
   const int nbr = nt + local;        // band rows in use
-  const int64_t tok0 = (int64_t)b * T;
   const float bl2 = bias[h] * kLog2e;
   int nf = 0;  // far offsets 2^j > local: j = jf0 .. n_pow2 - 1
   for (int j = 0; j < n_pow2; ++j) nf += (1 << j) > local;
   const int jf0 = n_pow2 - nf;
+  const int nlb = local / 4 + 1;     // band steps: offsets q + 4 i, i < nlb
   // this thread's token (4 threads per token) and its output chunks q + 4 i
   const int tt = tid >> 2, q = tid & 3;
   const int t = t0 + tt;
   const bool tok_ok = tt < nt;
 
+  // this (batch, head) of V, O and the coordinates as buffer resources: row s of V / O at
+  // byte s * vp, of a coordinate array at s * cp
+  const int vp = H * D * 2, cp = H * 6;
+  const int64_t hrow = (int64_t)b * T * H + h;
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(v + hrow * D), 0, T * vp - h * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      out + hrow * D, 0, T * vp - h * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(ck + hrow * 3), 0, T * cp - h * 6, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(cq + hrow * 3), 0, T * cp - h * 6, 0x00020000);
+  auto coord = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, int i) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * i, 0, 0));
+  };
+
   // ---- every global load first: band V and coordinates, far coordinates and far V rows
   u32x4 vb[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const int e = tid + 256 * i, r = e / DC, s = sb + r;
-    vb[i] = u32x4{0u, 0u, 0u, 0u};
-    if (r < nbr && s >= 0) vb[i] = ld16(v + ((tok0 + s) * H + h) * D + (e - r * DC) * 8);
+    const int e = tid + 256 * i, r = e / DC;
+    vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, g_row(sb + r, r < nbr, vp) + (e % DC) * 16, 0, 0);
   }
-  float ckv[2] = {0.f, 0.f};  // band coordinates: element tid and tid + 256 of [row][3]
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + 256 * i, r = e / 3, s = sb + r;
-    if (e < kGBR * 3 && r < nbr && s >= 0) ckv[i] = bf16_to_f32(ck[((tok0 + s) * H + h) * 3 + (e - r * 3)]);
+  f32x4 ckv = {0.f, 0.f, 0.f, 0.f};  // band row tid's coordinates
+  if (tid < kGBR) {
+    const uint32_t o = g_row(sb + tid, tid < nbr, cp);
+    ckv = f32x4{coord(rk, o, 0), coord(rk, o, 1), coord(rk, o, 2), 0.f};
   }
-  float cqv = 0.f;  // query coordinates: element tid of [token][3]
-  if (tid < kGTB * 3 && tid / 3 < nt)
-    cqv = bf16_to_f32(cq[((tok0 + t0 + tid / 3) * H + h) * 3 + tid % 3]);
+  f32x4 cqv = {0.f, 0.f, 0.f, 0.f};  // query coordinates of token tid
+  if (tid < kGTB) {
+    const uint32_t o = g_row(t0 + tid, tid < nt, cp);
+    cqv = f32x4{coord(rq, o, 0), coord(rq, o, 1), coord(rq, o, 2), 0.f};
+  }
   float fk[2][3];  // far coordinates: far offsets q and q + 4 of this thread's token
-  int fs[2];
+  bool fok[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int f = q + 4 * u;
-    fs[u] = (tok_ok && f < nf) ? t - (1 << (jf0 + f)) : -1;
-    fk[u][0] = fk[u][1] = fk[u][2] = 0.f;
-    if (fs[u] >= 0) {
-      const uint16_t* kp = ck + ((tok0 + fs[u]) * H + h) * 3;
-      fk[u][0] = bf16_to_f32(kp[0]);
-      fk[u][1] = bf16_to_f32(kp[1]);
-      fk[u][2] = bf16_to_f32(kp[2]);
-    }
+    const int s = tok_ok && f < nf ? t - (1 << (jf0 + f)) : -1;
+    fok[u] = s >= 0;
+    const uint32_t o = g_row(s, fok[u], cp);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) fk[u][i] = coord(rk, o, i);
   }
   // far V rows: this thread owns output chunks q + 4 c (c < CPT) of its token, and needs
   // every far offset's row for them
   u32x4 frow[kGFar][CPT];
 #pragma unroll
-  for (int f = 0; f < kGFar; ++f)
+  for (int f = 0; f < kGFar; ++f) {
+    const int s = tok_ok && f < nf ? t - (1 << (jf0 + f)) : -1;
+    const uint32_t o = g_row(s, true, vp) + q * 16;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      frow[f][c] = u32x4{0u, 0u, 0u, 0u};
-      if (tok_ok && f < nf) {
-        const int s = t - (1 << (jf0 + f));
-        if (s >= 0) frow[f][c] = ld16(v + ((tok0 + s) * H + h) * D + (q + 4 * c) * 8);
-      }
-    }
+    for (int c = 0; c < CPT; ++c) frow[f][c] = __builtin_amdgcn_raw_buffer_load_b128(rv, o + c * 64, 0, 0);
+  }
 
-  // ---- stage: V^T of the band, coordinates; P cleared.  A lane writes its 8 values
-  // (features d0 .. d0+7 of one band row) in an order rotated by its chunk index, so that
-  // at each step the lanes of different chunks write rows d0 + q with distinct q mod 8:
-  // with a row pitch of 17 x 16 bytes those fall in distinct LDS banks (rows 8 apart
-  // would share one).
+  // ---- stage: the band's V rows (row-major), coordinates; P cleared
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const int e = tid + 256 * i, r = e / DC, c = e - r * DC, d0 = c * 8;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int qv = (k + c) & 7;
-      const uint32_t w01 = (qv & 2) ? vb[i][1] : vb[i][0];
-      const uint32_t w23 = (qv & 2) ? vb[i][3] : vb[i][2];
-      const uint32_t wv = (qv & 4) ? w23 : w01;
-      vt[d0 + qv][r] = (uint16_t)((qv & 1) ? (wv >> 16) : (wv & 0xffffu));
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
     const int e = tid + 256 * i;
-    if (e < kGBR * 3) cks[e / 3][e % 3] = ckv[i];
+    st16(vrow + (e / DC) * VROW + (e % DC) * 16, vb[i]);
   }
-  if (tid < kGTB * 3) cqs[tid / 3][tid % 3] = cqv;
+  if (tid < kGBR) cks[tid] = ckv;
+  if (tid < kGTB) cqs[tid] = cqv;
   for (int i = tid; i < kGTB * kGPR / 8; i += 256)
     reinterpret_cast<u32x4*>(&pb[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   // ---- logits (log2 domain) and softmax: thread q of a token takes the band offsets
-  // o = q, q + 4, ... and the far offsets q and q + 4
-  const float qx = cqs[tt][0], qy = cqs[tt][1], qz = cqs[tt][2];
+  // o = q, q + 4, ... (<= local) and the far offsets q and q + 4
+  const f32x4 qc = cqs[tt];
   auto logit = [&](float kx, float ky, float kz) {
-    const float dx = qx - kx, dy = qy - ky, dz = qz - kz;
+    const float dx = qc[0] - kx, dy = qc[1] - ky, dz = qc[2] - kz;
     return bl2 - tau_log2 * (dx * dx + dy * dy + dz * dz);
   };
   float lb[kGLoc], lf[2];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kGLoc; ++i) {
+    if (i >= nlb) break;  // uniform
     const int o = q + 4 * i;
-    lb[i] = -INFINITY;
-    if (tok_ok && o <= local && t - o >= 0) {
-      const int r = tt + local - o;
-      lb[i] = logit(cks[r][0], cks[r][1], cks[r][2]);
-    }
+    const bool ok = tok_ok && o <= local && t - o >= 0;
+    const f32x4 kc = cks[ok ? tt + local - o : 0];
+    lb[i] = ok ? logit(kc[0], kc[1], kc[2]) : -INFINITY;
     mx = fmaxf(mx, lb[i]);
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    lf[u] = fs[u] >= 0 ? logit(fk[u][0], fk[u][1], fk[u][2]) : -INFINITY;
+    lf[u] = fok[u] ? logit(fk[u][0], fk[u][1], fk[u][2]) : -INFINITY;
     mx = fmaxf(mx, lf[u]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-  float sum = 0.f;   // normaliser of the weights as used (band weights rounded to bf16)
+  float sum = 0.f;   // normaliser of the weights as used (rounded to bf16)
   float sume = 0.f;  // unrounded normaliser, for the log-sum-exp
 #pragma unroll
   for (int i = 0; i < kGLoc; ++i) {
+    if (i >= nlb) break;  // uniform
     if (lb[i] != -INFINITY) {
       const float p = exp2_hw(lb[i] - mx);
       const uint32_t pbits = f32_to_bf16_bits(p);
@@ -273,12 +288,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       pb[tt][tt + local - (q + 4 * i)] = (uint16_t)pbits;
     }
   }
-  float pfar[2];
+  float pfar[2];  // far weights rounded to bf16 (the dot-product inputs)
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    pfar[u] = lf[u] != -INFINITY ? exp2_hw(lf[u] - mx) : 0.f;
+    const float p = lf[u] != -INFINITY ? exp2_hw(lf[u] - mx) : 0.f;
+    pfar[u] = bf16_to_f32((uint16_t)f32_to_bf16_bits(p));
     sum += pfar[u];
-    sume += pfar[u];
+    sume += p;
   }
   sum += __shfl_xor(sum, 1, 64);
   sum += __shfl_xor(sum, 2, 64);
@@ -290,18 +306,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
   for (int f = 0; f < kGFar; ++f) pall[f] = __shfl(pfar[f >> 2], (lane & ~3) | (f & 3), 64);
   __syncthreads();
 
-  // ---- band P.V on MFMA: wavefront w takes tokens 16w .. 16w+15, all D columns
+  // ---- band P.V on MFMA: wavefront w takes tokens 16w .. 16w+15, all D columns; band
+  // rows from nbr on have P = 0, so 32-row steps past them are skipped
   {
     const int n16 = lane & 15, grp = lane >> 4;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // B operand of band rows kk*32 + grp*8 .. +7, columns c*16 + n16: two transposing
+    // reads, lane (4j + q) of each 16 naming row j (then j + 4), columns 4q .. 4q+3
+    const unsigned char* tr = vrow + (grp * 8 + (n16 >> 2)) * VROW + (n16 & 3) * 8;
 #pragma unroll
     for (int kk = 0; kk < kGBR / 32; ++kk) {
+      if (kk * 32 >= nbr) break;  // uniform
       const u32x4 a = *reinterpret_cast<const u32x4*>(&pb[16 * w + n16][kk * 32 + grp * 8]);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(&vt[c * 16 + n16][kk * 32 + grp * 8]);
+        const u32x2 lo = lds_read_tr16(tr + (kk * 32) * VROW + c * 32);
+        const u32x2 hi = lds_read_tr16(tr + (kk * 32 + 4) * VROW + c * 32);
+        const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bv), acc[c],
                                                          0, 0, 0);
       }
@@ -317,23 +340,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
   // ---- far neighbours, normalisation, output
   if (tok_ok) {
     const float inv = 1.f / sum;
+    // far weights of offsets (2i, 2i + 1) packed as bf16 pairs
+    bf16x2 pp[kGFar / 2];
+#pragma unroll
+    for (int i = 0; i < kGFar / 2; ++i)
+      pp[i] = __builtin_bit_cast(bf16x2, pack_bf16x2(pall[2 * i], pall[2 * i + 1]));
+    const uint32_t orow = (uint32_t)t * (uint32_t)vp;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int d0 = (q + 4 * c) * 8;
-      float o[8];
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&ob[tt * (D + 4) + d0]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&ob[tt * (D + 4) + d0 + 4]);
+      float o[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) o[u] = ob[tt * (D + 4) + d0 + u];
-#pragma unroll
-      for (int f = 0; f < kGFar; ++f) {
+      for (int i = 0; i < kGFar / 2; ++i) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          o[2 * k] += pall[f] * bf16_lo(frow[f][c][k]);
-          o[2 * k + 1] += pall[f] * bf16_hi(frow[f][c][k]);
+          // (V_f[d], V_f+1[d]) and (V_f[d+1], V_f+1[d+1]) for d = d0 + 2k, f = 2i
+          const uint32_t a = frow[2 * i][c][k], b2 = frow[2 * i + 1][c][k];
+          const uint32_t lo = __builtin_amdgcn_perm(b2, a, 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(b2, a, 0x07060302u);
+          o[2 * k] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lo), pp[i],
+                                                     o[2 * k], false);
+          o[2 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), pp[i],
+                                                         o[2 * k + 1], false);
         }
       }
       const u32x4 wv = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
                         pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
-      st16(out + ((tok0 + t) * H + h) * D + d0, wv);
+      __builtin_amdgcn_raw_buffer_store_b128(wv, ro, orow + d0 * 2, 0, 0);
     }
     if (lse && q == 0) lse[((int64_t)b * H + h) * T + t] = (mx + __log2f(sume)) * kLn2;
   }
@@ -345,9 +380,12 @@ hipError_t launch_graph_attn_fwd(const void* cq, const void* ck, const void* v, 
   const float tl2 = tau * kLog2e;
   int n_far = 0;
   for (int j = 0; j < n_pow2; ++j) n_far += (1 << j) > local;
-  if (bf16 && (D == 64 || D == 128) && local <= kGBR - kGTB && n_far <= kGFar) {
+  // the block kernel addresses one batch's rows with 32-bit buffer offsets
+  const bool rows32 = (int64_t)T * H * D * 2 < ((int64_t)1 << 31);
+  if (bf16 && (D == 64 || D == 128) && local <= kGBR - kGTB && n_far <= kGFar && rows32 &&
+      B <= 65535) {
     const int nblk = (T + kGTB - 1) / kGTB;
-    const dim3 grid((unsigned)xcd_grid((int64_t)B * nblk * H));
+    const dim3 grid((unsigned)xcd_grid((int64_t)nblk * H), (unsigned)B);
     if (D == 64)
       hipLaunchKernelGGL(graph_attn_block<64>, grid, dim3(256), 0, st, (const uint16_t*)cq,
                          (const uint16_t*)ck, (const uint16_t*)v, bias, tl2, B, T, H, local,

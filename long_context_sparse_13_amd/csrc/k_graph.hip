@@ -132,14 +132,10 @@ constexpr int kGBR = 128;  // band rows held (block + local, local <= 64)
 constexpr int kGPR = kGBR + 8;  // LDS row pitch of P (bf16), 16-byte multiple
 constexpr int kGFar = 8;   // far offsets (2^j > local) handled: n_pow2 - #{2^j <= local} <= 8
 constexpr int kGLoc = 17;  // band logits per thread: (local + 1) / 4 rounded up, local <= 64
-constexpr uint32_t kGOut = 0x80000000u;  // a buffer offset past every resource: loads give 0
-
-// Byte offset of row s in a buffer resource whose rows are `pitch` bytes apart, or kGOut
-// when the row does not exist (s < 0 or !ok).  Rows of one batch span less than 2 GB
-// (checked on the host), so kGOut plus any in-row offset stays out of range.
-__device__ __forceinline__ uint32_t g_row(int s, bool ok, int pitch) {
-  return ok && s >= 0 ? (uint32_t)s * (uint32_t)pitch : kGOut;
-}
+// A buffer offset past every resource of the block kernel: loads there read zero.  Rows
+// of one batch span less than 2 GB (checked on the host), so this offset plus any in-row
+// offset stays out of range.
+constexpr uint32_t kGOut = 0x80000000u;
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void graph_attn_block(
@@ -151,12 +147,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
   constexpr int VPT = kGBR * DC / 256;   // band V chunks loaded per thread
   constexpr int PBYTES = kGTB * (D + 4) * 4 > kGTB * kGPR * 2 ? kGTB * (D + 4) * 4 : kGTB * kGPR * 2;
   // band V rows, row-major with a pitch of 2D + 32 bytes: the 4 rows x 8 bytes named by
-  // each 16 lanes of a transposing read fall on distinct banks
+  // each 16 lanes of a transposing read fall on distinct banks.  The 32 bytes past a row's
+  // values hold coordinates as float (x, y, z, 0): band row r's at 2D, the query token
+  // t0 + r's at 2D + 16 (r < 64).
   constexpr int VROW = 2 * D + 32;
   __shared__ __attribute__((aligned(16))) unsigned char vrow[kGBR * VROW];
   // band probabilities (bf16, [token][kGPR]), then the band P.V (float, [token][D + 4])
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[PBYTES];
-  __shared__ f32x4 cqs[kGTB], cks[kGBR];  // coordinates (x, y, z, unused)
   uint16_t(*pb)[kGPR] = reinterpret_cast<uint16_t(*)[kGPR]>(pbuf);
   float* ob = reinterpret_cast<float*>(pbuf);
 
@@ -166,8 +163,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
   // 2^31 of them: checked on the host, so the index arithmetic is 32-bit)
   const int item = (int)xcd_item(blockIdx.x, (int64_t)nblk * H);
   if (item < 0) return;
-  const int h = (int)((uint32_t)item % (uint32_t)H);
-  const int blk = (int)((uint32_t)item / (uint32_t)H);
+  const int h = (int)((uint32_t)item / (uint32_t)nblk);
+  const int blk = (int)((uint32_t)item % (uint32_t)nblk);
   const int b = blockIdx.y;
   const int t0 = blk * kGTB;
   const int nt = min(kGTB, T - t0);  // tokens of this block
@@ -195,45 +192,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
       const_cast<uint16_t*>(ck + hrow * 3), 0, T * cp - h * 6, 0x00020000);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(cq + hrow * 3), 0, T * cp - h * 6, 0x00020000);
-  auto coord = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, int i) {
-    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * i, 0, 0));
+  auto ld_c = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, int i) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * i, 0, 0);
   };
 
-  // ---- every global load first: band V and coordinates, far coordinates and far V rows
+  // ---- every global load first, with no branch between them (a load whose row does not
+  // exist gets an offset past its resource and reads zero), and none of their values
+  // used before the last is issued: band V and coordinates, query coordinates, far
+  // coordinates and far V rows
   u32x4 vb[VPT];
+  {
+    constexpr int RS = 256 / DC;   // band rows between this thread's loads
+    const int r0 = tid / DC, s0 = sb + r0;
+    const uint32_t o0 = (uint32_t)s0 * (uint32_t)vp + (uint32_t)(tid % DC) * 16u;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int e = tid + 256 * i, r = e / DC;
-    vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, g_row(sb + r, r < nbr, vp) + (e % DC) * 16, 0, 0);
+    for (int i = 0; i < VPT; ++i) {
+      const bool ok = r0 + i * RS < nbr && s0 + i * RS >= 0;
+      vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ok ? o0 + (uint32_t)(i * RS * vp) : kGOut, 0, 0);
+    }
   }
-  f32x4 ckv = {0.f, 0.f, 0.f, 0.f};  // band row tid's coordinates
-  if (tid < kGBR) {
-    const uint32_t o = g_row(sb + tid, tid < nbr, cp);
-    ckv = f32x4{coord(rk, o, 0), coord(rk, o, 1), coord(rk, o, 2), 0.f};
+  // coordinates (bf16 bits): threads 0..127 load band row tid, threads 128..191 query
+  // token t0 + tid - 128, each from its own tensor; the other load of a thread is out of
+  // range and reads zero, so the two combine with an OR
+  uint32_t crd[3];
+  {
+    const int s = sb + tid, tq = tid - kGBR;
+    const uint32_t o = tid < nbr && s >= 0 ? (uint32_t)s * (uint32_t)cp : kGOut;  // nbr <= kGBR
+    const uint32_t oq = tq >= 0 && tq < nt ? (uint32_t)(t0 + tq) * (uint32_t)cp : kGOut;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) crd[i] = ld_c(rk, o, i) | ld_c(rq, oq, i);
   }
-  f32x4 cqv = {0.f, 0.f, 0.f, 0.f};  // query coordinates of token tid
-  if (tid < kGTB) {
-    const uint32_t o = g_row(t0 + tid, tid < nt, cp);
-    cqv = f32x4{coord(rq, o, 0), coord(rq, o, 1), coord(rq, o, 2), 0.f};
-  }
-  float fk[2][3];  // far coordinates: far offsets q and q + 4 of this thread's token
+  // far rows of this thread's token: offset 2^(jf0 + f) for f < nf; row t - 2^j exists
+  // when t >= 2^j
+  const uint32_t tvo = (uint32_t)t * (uint32_t)vp + (uint32_t)q * 16u;
+  const uint32_t tco = (uint32_t)t * (uint32_t)cp;
+  uint32_t fkr[2][3];  // far coordinates: far offsets q and q + 4 (bf16 bits)
   bool fok[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int f = q + 4 * u;
-    const int s = tok_ok && f < nf ? t - (1 << (jf0 + f)) : -1;
-    fok[u] = s >= 0;
-    const uint32_t o = g_row(s, fok[u], cp);
+    const int sh = min(jf0 + f, 30);
+    fok[u] = tok_ok && f < nf && t >= (1 << sh);
+    const uint32_t o = fok[u] ? tco - ((uint32_t)cp << sh) : kGOut;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) fk[u][i] = coord(rk, o, i);
+    for (int i = 0; i < 3; ++i) fkr[u][i] = ld_c(rk, o, i);
   }
   // far V rows: this thread owns output chunks q + 4 c (c < CPT) of its token, and needs
   // every far offset's row for them
   u32x4 frow[kGFar][CPT];
 #pragma unroll
   for (int f = 0; f < kGFar; ++f) {
-    const int s = tok_ok && f < nf ? t - (1 << (jf0 + f)) : -1;
-    const uint32_t o = g_row(s, true, vp) + q * 16;
+    const int sh = min(jf0 + f, 30);
+    const bool ok = tok_ok && f < nf && t >= (1 << sh);
+    const uint32_t o = ok ? tvo - ((uint32_t)vp << sh) : kGOut;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) frow[f][c] = __builtin_amdgcn_raw_buffer_load_b128(rv, o + c * 64, 0, 0);
   }
@@ -244,15 +255,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     const int e = tid + 256 * i;
     st16(vrow + (e / DC) * VROW + (e % DC) * 16, vb[i]);
   }
-  if (tid < kGBR) cks[tid] = ckv;
-  if (tid < kGTB) cqs[tid] = cqv;
+  // every thread writes its coordinates (threads 192..255: zeros into the unused second
+  // half of rows 64..127's spare bytes), so no load waits behind a branch
+  {
+    const int slot = tid < kGBR ? tid * VROW + 2 * D : (tid - kGBR) * VROW + 2 * D + 16;
+    *reinterpret_cast<f32x4*>(vrow + slot) =
+        f32x4{bf16_to_f32((uint16_t)crd[0]), bf16_to_f32((uint16_t)crd[1]),
+              bf16_to_f32((uint16_t)crd[2]), 0.f};
+  }
   for (int i = tid; i < kGTB * kGPR / 8; i += 256)
     reinterpret_cast<u32x4*>(&pb[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   // ---- logits (log2 domain) and softmax: thread q of a token takes the band offsets
   // o = q, q + 4, ... (<= local) and the far offsets q and q + 4
-  const f32x4 qc = cqs[tt];
+  const f32x4 qc = *reinterpret_cast<const f32x4*>(vrow + tt * VROW + 2 * D + 16);
   auto logit = [&](float kx, float ky, float kz) {
     const float dx = qc[0] - kx, dy = qc[1] - ky, dz = qc[2] - kz;
     return bl2 - tau_log2 * (dx * dx + dy * dy + dz * dz);
@@ -264,13 +281,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     if (i >= nlb) break;  // uniform
     const int o = q + 4 * i;
     const bool ok = tok_ok && o <= local && t - o >= 0;
-    const f32x4 kc = cks[ok ? tt + local - o : 0];
+    const f32x4 kc = *reinterpret_cast<const f32x4*>(vrow + (ok ? tt + local - o : 0) * VROW + 2 * D);
     lb[i] = ok ? logit(kc[0], kc[1], kc[2]) : -INFINITY;
     mx = fmaxf(mx, lb[i]);
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    lf[u] = fok[u] ? logit(fk[u][0], fk[u][1], fk[u][2]) : -INFINITY;
+    lf[u] = fok[u] ? logit(bf16_to_f32((uint16_t)fkr[u][0]), bf16_to_f32((uint16_t)fkr[u][1]),
+                           bf16_to_f32((uint16_t)fkr[u][2]))
+                   : -INFINITY;
     mx = fmaxf(mx, lf[u]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 1, 64));

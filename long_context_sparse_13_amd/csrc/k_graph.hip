@@ -23,9 +23,10 @@
 // not exist get an offset past the resource and read as zero, with no branch — and the
 // band loops run only as far as `local` needs.  At D = 64 four workgroups per CU (the
 // LDS allows four); at D = 128 the LDS holds two, so the register cap asks for two
-// wavefronts per SIMD only.  Items are handed to the XCDs in contiguous (block, head)
-// ranges, so the rows a block shares with the blocks just before it are served from that
-// XCD's L2.
+// wavefronts per SIMD only.  Items are (head, block) pairs in head-major order, handed
+// to the XCDs in contiguous ranges: an XCD works through the blocks of one head (or a
+// few) in order, so the rows its far neighbours re-read, up to 2^13 tokens back, are that
+// head's recent rows and stay in the XCD's L2.
 //
 // graph_attn<BF> (any dtype, D % 8 == 0, the general case): one wavefront per (batch,
 // token, group of 64 eight-element chunks of the token's H*D values).  A lane owns one

@@ -157,4 +157,22 @@ __device__ __forceinline__ int64_t xcd_item(int64_t bid, int64_t n) {
 }
 __host__ __device__ inline int64_t xcd_grid(int64_t n) { return ((n + 7) / 8) * 8; }
 
+// The same over `phases` consecutive ranges of ceil(n / phases) items, the last range
+// first: blocks [r * G, (r + 1) * G) (G = xcd_grid of the range size) take range
+// phases - 1 - r, dealt to the XCDs as xcd_item does.  Workgroups start roughly in block
+// order, so the device works through one range of items at a time.
+__device__ __forceinline__ int64_t xcd_item_phased(int64_t bid, int64_t n, int phases) {
+  const int64_t m = (n + phases - 1) / phases;
+  const int64_t g = xcd_grid(m);
+  const int64_t base = (phases - 1 - bid / g) * m;
+  const int64_t mp = n - base < m ? n - base : m;  // items of this range
+  const int64_t bb = bid % g;
+  if (mp <= 0 || bb >= xcd_grid(mp)) return -1;
+  const int64_t it = xcd_item(bb, mp);
+  return it < 0 ? -1 : base + it;
+}
+__host__ __device__ inline int64_t xcd_grid_phased(int64_t n, int phases) {
+  return phases * xcd_grid((n + phases - 1) / phases);
+}
+
 }  // namespace sa

@@ -10,8 +10,8 @@
 // Kernels of one decode step (two launches):
 //  1. decode_block_scores: score_j = (sum_h q_h) . kbar_j for every complete block;
 //     each workgroup hands on the exact top-16 of its blocks as candidates.
-//  2. decode_split_attn: one workgroup of 4 wavefronts per (sequence, KV head, split)
-//     (8 wavefronts when a single split covers everything) selects the top blocks from
+//  2. decode_split_attn: one workgroup of 8 wavefronts per (sequence, KV head, split)
+//     selects the top blocks from
 //     the candidates; each wavefront attends the group's query heads to its sub-slice of
 //     U = selected blocks' tokens before the window followed by the window, through
 //     GroupAttn (MFMA over the grouped heads); the workgroup merges its wavefronts in LDS
@@ -101,8 +101,8 @@ constexpr int kScoreThreads = 256;
 constexpr int kScoreChunk = 256;   // blocks scored per workgroup pass (64 per wavefront)
 constexpr int kCandMax = 64;       // most candidates a scoring workgroup hands on
 constexpr int kMaxScoreWGs = 64;   // scoring workgroups per (sequence, KV head)
-constexpr int kSplitWaves = 4;     // wavefronts per split workgroup (n_splits > 1)
-constexpr int kSplitGrain = kSplitWaves * 64;  // positions of U per split: 2 tiles per wave
+constexpr int kSplitWaves = 8;     // wavefronts per split workgroup (n_splits > 1)
+constexpr int kSplitGrain = kSplitWaves * 32;  // positions of U per split: 1 tile per wave
 constexpr int kWholeWaves = 8;     // wavefronts of the one workgroup per sequence (n_splits == 1)
 
 // Scoring workgroups per (sequence, KV head) and blocks each one covers.
@@ -146,8 +146,10 @@ static int decode_u_max(int Lmax, int block, int top_blocks, int window) {
 }
 
 int decode_auto_splits(int B, int Lmax, int Hkv, int block, int top_blocks, int window) {
-  // two 32-key tiles per wavefront of a 4-wavefront split (the step is latency-bound:
-  // more, thinner splits cost more in the merge than they save), up to ~8 waves per CU
+  // one 32-key tile per wavefront of an 8-wavefront split, so each wavefront waits for
+  // one round of gathers (two tiles per wavefront of 4-wavefront splits: 1 us slower per
+  // step; one tile per wavefront of 4-wavefront splits, twice the splits: 4 us slower,
+  // the merge costs more than it saves), up to ~8 waves per CU
   const int64_t umax = decode_u_max(Lmax, block, top_blocks, window);
   const int64_t steps = imax(1, (umax + kSplitGrain - 1) / kSplitGrain);
   const int64_t cap = imax(1, (2048 / kSplitWaves) / ((int64_t)B * Hkv));

@@ -10,11 +10,15 @@
 //  * sparse_attn_mfma<D, OFS32>: bf16, up to 16 query heads per KV head.  One wavefront
 //    per (batch, token, KV head); keys are streamed 32 at a time through GroupAttn (MFMA
 //    over the grouped heads, online softmax).  Held to 3 wavefronts per SIMD (<= 168
-//    registers).  The kernel is bound by the vector memory pipeline (the texture
-//    addresser is ~80 % busy; with every gathered row an L2 hit it runs ~15 % faster, and
-//    halving its VALU instructions gains nothing), so more resident wavefronts beat a
-//    deeper per-wavefront pipeline, and OFS32 (one KV head's rows of a batch within
-//    4 GB) addresses rows as a uniform base plus a 32-bit offset.  Q and the index row are read
+//    registers).  The kernel is bound by how many gathered rows the memory pipeline keeps
+//    in flight against the L2 / Infinity Cache latency (with every gathered row an L2 hit
+//    it runs ~15 % faster; halving its VALU instructions, or cutting the K loads'
+//    addresser work by staging them through LDS, gains nothing), so more resident
+//    wavefronts beat a deeper per-wavefront pipeline, and OFS32 (one KV head's rows of a
+//    batch within 4 GB) addresses rows as a uniform base plus a 32-bit offset.  Items are
+//    taken in ranges of about 8,192, last rows first, each range dealt to the XCDs in
+//    contiguous pieces (xcd_item_phased): fewer bytes past L2 and ~12 % less time than one
+//    range over the whole sequence.  Q and the index row are read
 //    with non-temporal loads so they do not evict gathered K/V rows (O is written with
 //    ordinary stores, which L2 combines into whole lines).  The listed indices are visited first
 //    (positions inside the window or outside [0, t] are masked out, so each key is

@@ -200,7 +200,9 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ lens, int Lmax, int Hq, int Hkv, int block, int per_wg, int cpw,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters) {
-  __shared__ __attribute__((aligned(16))) uint64_t scomb[kScoreChunk + kCandMax];
+  __shared__ __attribute__((aligned(16))) uint64_t scomb[kScoreChunk];
+  // each wavefront's top cpw of the chunk, then the running candidates
+  __shared__ __attribute__((aligned(16))) uint64_t wsel[(kScoreThreads / 64 + 1) * kCandMax];
   __shared__ uint64_t best[kCandMax];
   __shared__ __attribute__((aligned(16))) uint16_t qrows[16 * D];  // the group's query rows
   // a row (D floats) is read by 8 lanes, C = D/8 consecutive floats each; 8 rows per
@@ -273,11 +275,33 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
       if ((lane & 7) == 0)
         scomb[wv * 64 + gi * 8 + (lane >> 3)] = pack_rank(order_key(part), j < j_end ? j : -1);
     }
+    // each wavefront keeps the top cpw of its own 64 rows (an entry of the chunk's top cpw
+    // has fewer than cpw entries above it in its wavefront too), ranked against its 64
+    // entries only; the workgroup then ranks the 4 cpw survivors
+    constexpr int NW = kScoreThreads / 64;
+    uint64_t* ws = wsel + wv * cpw;
+    if (lane < cpw) ws[lane] = 0ull;
+    wave_lds_sync();  // this wavefront's scores and cleared slots are in place
+    {
+      typedef __attribute__((ext_vector_type(2))) unsigned long long u64x2;
+      const u64x2* c2 = reinterpret_cast<const u64x2*>(scomb + wv * 64);
+      const uint64_t ci = scomb[wv * 64 + lane];
+      int rank = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u64x2 x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = c2[h * 16 + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) rank += (x[u][0] > ci) + (x[u][1] > ci);
+      }
+      if (ci != 0ull && rank < cpw) ws[rank] = ci;
+    }
     // from the second chunk on, the running candidates compete with the new scores
     const bool first = c0 == j_begin;
-    if (!first && tid < cpw) scomb[kScoreChunk + tid] = best[tid];
+    if (!first && tid < cpw) wsel[NW * cpw + tid] = best[tid];
     __syncthreads();
-    rank_select<kScoreThreads>(scomb, kScoreChunk + (first ? 0 : cpw), cpw,
+    rank_select<kScoreThreads>(wsel, NW * cpw + (first ? 0 : cpw), cpw,
                                [&](int rank, uint64_t c) { best[rank] = c; });
     __syncthreads();
   }

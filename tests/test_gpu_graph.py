@@ -39,7 +39,9 @@ def test_degenerate_graphs():
 def test_block_kernel_edges():
     # 64-token blocks: ragged last block, widest band (local = 64), far offsets beyond T,
     # no far offsets at all, and offsets reaching back many blocks
-    _run(507, 2, 1000, 4, 64, "bf16", 1.3, 64, 30)
+    _run(507, 2, 1000, 4, 64, "bf16", 1.3, 64, 14)     # widest band, 7 far offsets, batch 2
+    _run(512, 1, 1000, 4, 64, "bf16", 1.3, 64, 30)     # 23 far offsets: the general kernel
+    _run(513, 1, 200, 2, 64, "bf16", 1.0, 1, 8)        # local 1: 7 far offsets, 2 .. 128
     _run(508, 1, 130, 2, 64, "bf16", 0.5, 64, 6)       # every power of two <= local
     _run(509, 1, 3000, 3, 64, "bf16", 1.0, 32, 14)
     _run(510, 1, 777, 2, 128, "bf16", 2.0, 17, 11)

@@ -325,10 +325,12 @@ size_t sa_cmp_attn_workspace(int B, int T, int Hkv, int D, int block);
  *   score_j = sum_h q[b,t,h,:] . kbar[b,j,g(h),:]   (float32; every query head)
  *
  * over the complete blocks j < (t+1)/block; the top_blocks best (ties to the lower j; all
- * of them when fewer are complete), ascending, are written as their tokens:
- * idx[b, t, i*block + e] = j_i*block + e, -1 padded, so idx [B, T, top_blocks*block] int32
- * feeds sa_sparse_attn_fwd (window 0) as the selected branch.  One selection per query
- * row, shared by all heads, as for the token-level top-k.
+ * of them when fewer are complete), j_0 < j_1 < ..., are written as their tokens, the
+ * blocks interleaved: idx[b, t, e*top_blocks + i] = j_i*block + e (e < block), -1 where
+ * block i does not exist, so idx [B, T, top_blocks*block] int32 feeds sa_sparse_attn_fwd
+ * (window 0) as the selected branch; each 32-entry step of the attention then reads rows
+ * of many blocks instead of one run of consecutive rows.  One selection per query row,
+ * shared by all heads, as for the token-level top-k.
  * q [B, T, Hq, D] bf16 or float32; kbar as for sa_cmp_attn_fwd.
  * workspace: at least sa_block_select_workspace(...) bytes (scores and summed queries).
  * Requires 1 <= top_blocks <= 64, block in {16, 32, 64, 128}, T/block <= 4096.

@@ -529,7 +529,9 @@ def sa_block_select_workspace(B, T, Hkv, D, block, row_begin, row_end) -> int:
 def sa_block_select(q, kbar, block: int, top_blocks: int, row_begin: int = 0,
                     row_end: int | None = None, idx=None, workspace=None):
     """Top blocks per query row by sum_h q_h . kbar_j, written as token lists
-    idx [B, T, top_blocks*block] int32 (rows [row_begin, row_end))."""
+    idx [B, T, top_blocks*block] int32 (rows [row_begin, row_end)), the chosen blocks
+    j_0 < j_1 < ... interleaved: idx[b, t, e*top_blocks + i] = j_i*block + e, -1 where
+    block i does not exist."""
     torch = _torch()
     _dev(q, "q"); _dev(kbar, "kbar", torch.float32)
     _shape(q, "q", None, None, None, None)

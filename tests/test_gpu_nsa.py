@@ -56,6 +56,8 @@ def _check_blocks(gi, want_sel, q, kbar, block, top, rows):
         gb = sorted(set(int(s) // block for s in g if s >= 0))
         wb = sorted(int(j) for j in want_sel[r] if j >= 0)
         toks = orc.block_tokens(np.array(wb + [-1] * (top - len(wb))), block)
+        # the library lists the blocks interleaved: token e of the i-th block at e * top + i
+        toks = toks.reshape(top, block).T.reshape(-1)
         if gb == wb:
             assert np.array_equal(g, toks), t
             continue

@@ -9,10 +9,12 @@
 //
 //  * round_bf16: the float32 block means (sa_block_meanpool of K and of V) rounded once
 //    per call to bf16 rows for the MFMA tiles.
-//  * cmp_attn_tile<D>: the compressed branch.  One workgroup per (batch, 8 tokens, KV
-//    head), one wavefront per token attending to the compressed keys j < (t+1)/block with
-//    GroupAttn's arithmetic; the 32-row K/V tiles are loaded once per workgroup into LDS
-//    and shared by its 8 tokens; token groups are dealt longest first.
+//  * band_attn_tile<D, WIN>: the compressed branch (WIN = false) and sliding-window
+//    attention without listed keys (WIN = true: the window branch, taken by
+//    sa_sparse_attn_fwd when no index list is given).  One workgroup per (batch, 8
+//    tokens, KV head), one wavefront per token with GroupAttn's arithmetic over its key
+//    rows (compressed keys j < (t+1)/block, or tokens [t - W + 1, t]); the 32-row K/V
+//    tiles are loaded once per workgroup into LDS and shared by its 8 tokens.
 //  * head_sum + block_scores: score[t, j] = sum_h q[t,h] . kbar[j, g(h)] in float32 for the
 //    complete blocks of each row (the queries of each KV group summed first); a workgroup
 //    owns 64 rows x 64 blocks with the summed queries and the pooled keys staged in LDS,
@@ -43,19 +45,26 @@ __global__ __launch_bounds__(256) void round_bf16(const float* __restrict__ src,
   st8(dst + 4 * i, u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
 }
 
-// One workgroup of 8 wavefronts per (batch, 8 consecutive tokens, KV head); wavefront w
-// takes token 8 tb + w.  The compressed K and V rows are streamed in 32-row tiles that
-// the whole workgroup loads once into LDS (the next tile's rows in flight in registers
-// while the current one is used), so each row leaves L2 once per 8 tokens instead of
-// once per token.  Per token the arithmetic is GroupAttn's (attn_tile.h): S^T = K . Q^T
-// with the group's heads as the MFMA N dimension, an online softmax in the log2 domain,
-// O^T += V^T . P^T with V^T read from LDS, over the tiles that hold its compressed keys
-// j < (t + 1) / block.  Token groups are dealt longest first.
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void cmp_attn_tile(
+// One workgroup of 8 wavefronts per (batch, 8 consecutive tokens 8 tg .. 8 tg + 7, KV
+// head); wavefront w takes token 8 tg + w.  The K and V rows the 8 tokens attend to are
+// streamed in 32-row tiles that the whole workgroup loads once into LDS (the next tile's
+// rows in flight in registers while the current one is used), so each row leaves L2
+// once per 8 tokens instead of once per token.  Per token the arithmetic is GroupAttn's
+// (attn_tile.h): S^T = K . Q^T with the group's heads as the MFMA N dimension, an online
+// softmax in the log2 domain, O^T += V^T . P^T with V^T read from LDS.  The keys of token t:
+//   WIN = false (NSA's compressed branch): the compressed rows j < (t + 1) / block of the
+//     bf16 block means (nkv = T / block rows per batch); token groups longest first;
+//   WIN = true (a sliding window, the window branch): the token rows [t - window + 1, t]
+//     of the K / V caches (nkv = T).
+// Tiles start at multiples of 32 rows, so a token's keys fall into the same tiles
+// whichever tokens share its workgroup or row range: a row's result does not depend on
+// the range it was computed in.  Tokens outside [r0, r0 + nrows) are skipped.
+template <int D, bool WIN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void band_attn_tile(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
-    const uint16_t* __restrict__ vb, int B, int T, int Hq, int Hkv, int nb, int block,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const uint16_t* __restrict__ vb, int B, int T, int Hq, int Hkv, int nkv, int block,
+    int window, int r0, int nrows, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
   constexpr int KS = D / 32, DT = D / 16, CH = D * 2 / 16;  // 16-byte chunks per row
   constexpr int LROW = D * 2 + 16;                          // padded LDS row of K (bytes)
   constexpr int VP = 72;  // bytes per V^T row (32 keys of one feature, 8 bytes of pad)
@@ -64,15 +73,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void c
   __shared__ __attribute__((aligned(16))) unsigned char vt[D * VP];  // V^T [d][key]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
-  const int ntg = (T + TPG - 1) / TPG;
+  const int tg0 = r0 / TPG;                             // first token group of the range
+  const int ntg = (r0 + nrows + TPG - 1) / TPG - tg0;
   const int64_t items = (int64_t)B * ntg * Hkv;
   if ((int64_t)blockIdx.x >= items) return;
-  const int64_t item = items - 1 - (int64_t)blockIdx.x;  // longest first
+  const int64_t item = items - 1 - (int64_t)blockIdx.x;  // last (longest) token groups first
   const int g = (int)(item % Hkv);
   const int b = (int)((item / Hkv) % B);
-  const int tg = (int)(item / ((int64_t)Hkv * B));
+  const int tg = tg0 + (int)(item / ((int64_t)Hkv * B));
   const int t = tg * TPG + w;
-  const bool tok = t < T;
+  const bool tok = t >= r0 && t < r0 + nrows;
   const int G = Hq / Hkv;
   const int h = g * G + n;
   const bool hv = tok && n < G;
@@ -89,22 +99,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void c
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int nfull_w = tok ? (t + 1) / block : 0;  // this token's compressed keys
-  const int t_last = min(tg * TPG + TPG - 1, T - 1);
-  const int nfull = (t_last + 1) / block;         // the workgroup's
-  const int ntiles = (nfull + 31) / 32;
+  // key rows [lo_w, hi_w] of this token (empty when hi_w < lo_w) and [lo, hi] of the
+  // workgroup's tokens in the range
+  const int t_first = max(tg * TPG, r0), t_last = min(tg * TPG + TPG - 1, r0 + nrows - 1);
+  int lo_w, hi_w, lo, hi;
+  if constexpr (WIN) {
+    lo_w = max(0, t - window + 1);
+    hi_w = tok ? t : -1;
+    lo = max(0, t_first - window + 1);
+    hi = t_last;
+  } else {
+    lo_w = 0;
+    hi_w = tok ? (t + 1) / block - 1 : -1;
+    lo = 0;
+    hi = (t_last + 1) / block - 1;
+  }
+  const int tbase = lo & ~31;  // tiles start at multiples of 32 rows
+  const int ntiles = hi >= lo ? (hi - tbase) / 32 + 1 : 0;
   const int64_t stride = (int64_t)Hkv * D;
-  const uint16_t* kbase = kb + ((int64_t)b * nb * Hkv + g) * D;
-  const uint16_t* vbase = vb + ((int64_t)b * nb * Hkv + g) * D;
+  const uint16_t* kbase = kb + ((int64_t)b * nkv * Hkv + g) * D;
+  const uint16_t* vbase = vb + ((int64_t)b * nkv * Hkv + g) * D;
   // tile loads: thread tid < 32 * CH takes row tid / CH, 16-byte chunk tid % CH
   const bool ldr = tid < 32 * CH;
   const int r_ld = tid / CH, c_ld = tid % CH;
   u32x4 kr = {0u, 0u, 0u, 0u}, vr = kr;
   auto ldtile = [&](int tile) {
-    const int j = tile * 32 + r_ld;
+    const int j = tbase + tile * 32 + r_ld;
     kr = u32x4{0u, 0u, 0u, 0u};
     vr = kr;
-    if (ldr && j < nfull) {
+    if (ldr && j >= lo && j <= hi) {
       kr = ld16(kbase + (int64_t)j * stride + c_ld * 8);
       vr = ld16(vbase + (int64_t)j * stride + c_ld * 8);
     }
@@ -128,9 +151,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void c
     }
     __syncthreads();
     if (tile + 1 < ntiles) ldtile(tile + 1);  // in flight while this tile is used
-    const int valid = nfull_w - tile * 32;     // slots below are this token's keys
-    if (valid > 0) {
-      const uint32_t vm = valid >= 32 ? 0xffffffffu : ((1u << valid) - 1u);
+    // this token's keys in the tile: slots [a, e] (a contiguous run)
+    const int base = tbase + tile * 32;
+    const int a = max(lo_w - base, 0), e = min(hi_w - base, 31);
+    if (a <= e) {
+      const uint32_t vm = (e == 31 ? 0xffffffffu : ((1u << (e + 1)) - 1u)) & ~((1u << a) - 1u);
       // ---- S^T = K . Q^T for the two 16-key halves (K rows from LDS)
       f32x4 s[2];
 #pragma unroll
@@ -596,11 +621,30 @@ hipError_t launch_cmp_attn(const void* q, const float* kbar, const float* vbar, 
   const dim3 grid((unsigned)items);
   const float sl2 = scale * 1.4426950408889634f;
   if (D == 128)
-    hipLaunchKernelGGL(cmp_attn_tile<128>, grid, dim3(512), 0, st, (const uint16_t*)q, kb, vb, B,
-                       T, Hq, Hkv, nb, block, sl2, (uint16_t*)out, lse);
+    hipLaunchKernelGGL((band_attn_tile<128, false>), grid, dim3(512), 0, st, (const uint16_t*)q, kb,
+                       vb, B, T, Hq, Hkv, nb, block, 0, 0, T, sl2, (uint16_t*)out, lse);
   else
-    hipLaunchKernelGGL(cmp_attn_tile<64>, grid, dim3(512), 0, st, (const uint16_t*)q, kb, vb, B,
-                       T, Hq, Hkv, nb, block, sl2, (uint16_t*)out, lse);
+    hipLaunchKernelGGL((band_attn_tile<64, false>), grid, dim3(512), 0, st, (const uint16_t*)q, kb,
+                       vb, B, T, Hq, Hkv, nb, block, 0, 0, T, sl2, (uint16_t*)out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_attn(const void* q, const void* k, const void* v, int B, int T, int Hq,
+                              int Hkv, int D, int window, float scale, void* out, float* lse,
+                              int row_begin, int row_end, hipStream_t st) {
+  const int nrows = row_end - row_begin;
+  if (nrows <= 0) return hipSuccess;
+  const int ntg = (row_end + 7) / 8 - row_begin / 8;
+  const dim3 grid((unsigned)((int64_t)B * ntg * Hkv));
+  const float sl2 = scale * 1.4426950408889634f;
+  if (D == 128)
+    hipLaunchKernelGGL((band_attn_tile<128, true>), grid, dim3(512), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, B, T, Hq, Hkv, T, 1, window,
+                       row_begin, nrows, sl2, (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL((band_attn_tile<64, true>), grid, dim3(512), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, B, T, Hq, Hkv, T, 1, window,
+                       row_begin, nrows, sl2, (uint16_t*)out, lse);
   return hipGetLastError();
 }
 

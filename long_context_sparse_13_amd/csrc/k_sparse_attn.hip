@@ -225,6 +225,10 @@ hipError_t launch_sparse_attn_fwd(const void* q, const void* k, const void* v, c
   const float sl2 = scale * kLog2e;
   const int nrows = row_end - row_begin;
   if (nrows <= 0) return hipSuccess;
+  // no listed keys: a plain sliding window, whose K/V rows neighbouring tokens share
+  if ((!idx || topk == 0) && bf16 && G <= 16 && (D == 64 || D == 128) && window >= 1)
+    return launch_window_attn(q, k, v, B, T, Hq, Hkv, D, window, scale, out, lse, row_begin,
+                              row_end, st);
   const dim3 grid((unsigned)xcd_grid((int64_t)B * nrows * Hkv));
   const dim3 block(64);
   if (bf16 && G <= 16) {

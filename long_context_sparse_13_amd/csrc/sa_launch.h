@@ -87,6 +87,12 @@ hipError_t decode_scratch(void** ptr);
 
 // NSA branches (prefill) and the gated combine.
 size_t cmp_attn_workspace_bytes(int B, int T, int Hkv, int D, int block);
+// Sliding-window attention with no listed keys (bf16, D in {64, 128}, up to 16 query
+// heads per KV head, window >= 1): the 8 tokens of a workgroup share each K/V tile
+// through LDS (band_attn_tile in k_nsa.hip).
+hipError_t launch_window_attn(const void* q, const void* k, const void* v, int B, int T, int Hq,
+                              int Hkv, int D, int window, float scale, void* out, float* lse,
+                              int row_begin, int row_end, hipStream_t st);
 hipError_t launch_cmp_attn(const void* q, const float* kbar, const float* vbar, int B, int T,
                            int Hq, int Hkv, int D, int block, float scale, void* out, float* lse,
                            void* workspace, hipStream_t st);

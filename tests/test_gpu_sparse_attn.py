@@ -49,6 +49,37 @@ def test_mfma_window_only_and_topk_only():
     _run(104, 1, 300, 16, 1, 128, 70, 0, "bf16")
 
 
+def test_window_only_shared_tiles():
+    """No index list: the sliding window through the shared-tile kernel (8 tokens of a
+    workgroup share each K/V tile), against the oracle: long window, GQA with padded head
+    columns and batch 2, a window longer than the sequence, window 1, ragged T."""
+    _run(121, 1, 1000, 16, 1, 128, 0, 512, "bf16")
+    _run(122, 2, 300, 8, 2, 64, 0, 45, "bf16")
+    _run(123, 1, 77, 4, 1, 128, 0, 200, "bf16")
+    _run(124, 1, 130, 16, 1, 64, 0, 1, "bf16")
+    _run(125, 1, 517, 16, 1, 128, 0, 33, "bf16")
+
+
+def test_window_only_row_ranges():
+    """The shared-tile window over row ranges that start and end inside 8-token groups
+    writes what the full call writes, bit for bit (tiles start at multiples of 32 keys
+    whatever the range), and leaves the other rows untouched."""
+    import torch
+    B, T, Hq, Hkv, D, W = 2, 301, 16, 1, 64, 70
+    note(f"window-only rows B={B} T={T} W={W}")
+    x = sa_synth.attn_inputs(126, B, T, Hq, Hkv, D, "bf16")
+    q, k, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+    full, lfull = sa.sa_sparse_attn_fwd(q, k, v, None, W, 0.125, return_lse=True)
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((B, Hq, T), 7.0, dtype=torch.float32, device="cuda")
+    sa.sa_sparse_attn_fwd_rows(q, k, v, None, W, 0.125, 43, 170, out, lse)
+    assert bool((out[:, :43] == 7.0).all()) and bool((out[:, 170:] == 7.0).all())
+    assert torch.equal(out[:, 43:170], full[:, 43:170])
+    for r0, r1 in ((0, 43), (170, 299), (299, 301)):
+        sa.sa_sparse_attn_fwd_rows(q, k, v, None, W, 0.125, r0, r1, out, lse)
+    assert torch.equal(out, full) and torch.equal(lse, lfull)
+
+
 def test_mfma_junk_indices_are_skipped():
     _run(105, 1, 200, 16, 1, 64, 96, 8, "bf16", junk=True)
 

@@ -271,8 +271,9 @@ def main():
     def two_step_indices(timer):
         for r0 in range(0, T, chunk):
             r1 = min(T, r0 + chunk)
-            timer.run("indexer", lambda: sa.sa_indexer_scores(qi, ki, w, r0, r1, scores, ld))
-            timer.run("topk", lambda: sa.sa_topk_select(scores, topk, T, r0, r1, idx, ld))
+            sc = scores[:, : r1 - r0]  # (the last chunk may be shorter; a prefix stays contiguous)
+            timer.run("indexer", lambda: sa.sa_indexer_scores(qi, ki, w, r0, r1, sc, ld))
+            timer.run("topk", lambda: sa.sa_topk_select(sc, topk, T, r0, r1, idx, ld))
 
     def fused_indices(timer):
         for r0 in range(0, T, chunk):

@@ -54,6 +54,21 @@ struct GroupAttn {
     l_run = 0.f;
   }
 
+  // As init, with qrow an in-bounds row for every lane and `valid` false for a padding
+  // head: the loads are issued unconditionally (no branch for the compiler's wait
+  // placement to account for) and the padding heads' rows set to zero.
+  __device__ __forceinline__ void init_masked(const uint16_t* qrow, bool valid, int grp) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 w = ld16_nt(qrow + ks * 32 + grp * 8);
+      qB[ks] = as_bf16x8(valid ? w : u32x4{0u, 0u, 0u, 0u});
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  }
+
   // Registers of one gathered 32-key tile: K rows as MFMA A operands, V rows waiting to
   // be staged in LDS, and the slot mask (bit i set = slot i attended).
   struct Tile {

@@ -214,36 +214,36 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
   const int nb = Lmax / block;
-  const int L = min(max(lens[b], 0), Lmax);  // lengths outside [0, Lmax] are clamped
-  const int nfull = L / block;
-
-  // the merge counter of this (sequence, KV head) starts kernel 2 at zero (same policy as
-  // kernel 2's own accesses to it)
-  if (blockIdx.y == 0 && tid == 0)
-    __hip_atomic_store(&counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int d0 = (lane & 7) * C;
   const int j_begin = blockIdx.y * per_wg;
-  const int j_end = min(j_begin + per_wg, nfull);
-  // the first chunk's key means are requested before the query rows arrive
+  // Issue order: the group's query rows (G x D bf16, one 16-byte piece per thread), the
+  // key means of the workgroup's blocks, then the sequence's length.  The means are read
+  // through a buffer resource over sequence b's rows of KV head g: rows past the cache
+  // read as zero, so no load waits for the length or a branch (rows at or past the
+  // sequence's last complete block are read and then left out of the ranking), and the
+  // query sum below runs while the means are in flight.
+  const int pieces = G * D / 8;
+  const int qp = min(tid, pieces - 1);  // threads past the pieces repeat the last one
+  const u32x4 qv = ld16(q + ((int64_t)b * Hq + g * G) * D + qp * 8);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(kbar) + ((int64_t)b * nb * Hkv + g) * D, 0,
+      (int)(((int64_t)nb * Hkv - g) * D * 4), 0x00020000);
   f32x4 a[8][NL];
   auto load_rows = [&](int c0) {
     const int jw = c0 + wv * 64 + (lane >> 3);  // this lane's row in group 0
 #pragma unroll
     for (int gi = 0; gi < 8; ++gi) {  // all of the wave's rows in flight at once
-      const int j = jw + gi * 8;
-      const float* rp = kbar + (((int64_t)b * nb + (j < j_end ? j : 0)) * Hkv + g) * D + d0;
+      const uint32_t o = ((uint32_t)(jw + gi * 8) * (uint32_t)(Hkv * D) + d0) * 4u;
 #pragma unroll
       for (int l = 0; l < NL; ++l)
-        a[gi][l] = j < j_end ? *reinterpret_cast<const f32x4*>(rp + 4 * l) : f32x4{0.f, 0.f, 0.f, 0.f};
+        a[gi][l] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, o + 16 * l, 0, 0));
     }
   };
-  if (j_begin < j_end) load_rows(j_begin);
-  // the group's query rows (G x D bf16, one 16-byte piece per thread) through LDS
-  {
-    const int pieces = G * D / 8;
-    for (int pc = tid; pc < pieces; pc += kScoreThreads)
-      *reinterpret_cast<u32x4*>(&qrows[pc * 8]) = ld16(q + ((int64_t)b * Hq + g * G) * D + pc * 8);
-  }
+  load_rows(j_begin);
+  const int L = min(max(lens[b], 0), Lmax);  // lengths outside [0, Lmax] are clamped
+  const int nfull = L / block;
+  const int j_end = min(j_begin + per_wg, nfull);  // blocks scored
+  *reinterpret_cast<u32x4*>(&qrows[qp * 8]) = qv;
   __syncthreads();
   float qb[C];
 #pragma unroll
@@ -307,6 +307,10 @@ __global__ __launch_bounds__(kScoreThreads) void decode_block_scores(
   }
   if (tid < cpw)
     reinterpret_cast<uint64_t*>(cand)[((int64_t)bg * gridDim.y + blockIdx.y) * cpw + tid] = best[tid];
+  // the merge counter of this (sequence, KV head) starts kernel 2 at zero (same policy as
+  // kernel 2's own accesses to it)
+  if (blockIdx.y == 0 && tid == 0)
+    __hip_atomic_store(&counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------ kernel 2
@@ -345,21 +349,27 @@ __global__ __launch_bounds__(64 * W) void decode_split_attn(
   const int split = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
+  const bool hv = n < G;
+  // Issue order: this thread's first candidate (n_cand >= 8), the query rows (padding
+  // heads read the group's last row and zero it), then the sequence's length, which is
+  // needed only once the candidates are in LDS; no load waits for another.
+  const uint64_t* cb = reinterpret_cast<const uint64_t*>(cand) + (int64_t)bg * n_cand;
+  const uint64_t c_first = cb[min(tid, n_cand - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+  GA ga;
+  ga.init_masked(q + ((int64_t)b * Hq + g * G + (hv ? n : G - 1)) * D, hv, grp);
+  __builtin_amdgcn_sched_barrier(0);
   const int L = min(max(lens[b], 0), Lmax);
   const int wstart = max(0, L - window);
   const int nfull = L / block;
   const int nsel_blocks = min(top_blocks, nfull);
-  const int h = g * G + n;
-  const bool hv = n < G;
-  GA ga;  // the query rows are requested before the selection work
-  ga.init(hv ? q + ((int64_t)b * Hq + h) * D : nullptr, grp);
 
   // ---- top blocks from the candidates (by score), then ascending by block
   {
     uint64_t* cc = reinterpret_cast<uint64_t*>(&vl[0][0]);
     int* rsel = reinterpret_cast<int*>(cc + n_cand);  // blocks in score order
-    const uint64_t* cb = reinterpret_cast<const uint64_t*>(cand) + (int64_t)bg * n_cand;
-    for (int i = tid; i < n_cand; i += 64 * W) cc[i] = cb[i];
+    cc[min(tid, n_cand - 1)] = c_first;  // (threads past n_cand repeat the last entry)
+    for (int i = tid + 64 * W; i < n_cand; i += 64 * W) cc[i] = cb[i];
     __syncthreads();
     rank_select<64 * W>(cc, n_cand, nsel_blocks,
                                   [&](int rank, uint64_t c) { rsel[rank] = unpack_pos(c); });

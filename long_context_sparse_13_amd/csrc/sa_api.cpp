@@ -530,6 +530,8 @@ static int decode_check_sizes(int B, int Lmax, int Hq, int Hkv, int D, int block
   SUPPORT(D == 64 || D == 128, "head dim D=%d is not supported (64, 128)", D);
   SUPPORT(Hq / Hkv <= 16, "Hq/Hkv=%d is not supported by the decode kernel (<= 16)", Hq / Hkv);
   SUPPORT(Lmax / block <= 262144, "too many blocks per sequence");
+  SUPPORT((int64_t)(Lmax / block) * Hkv * D * 4 < ((int64_t)1 << 31),
+          "the block means of one sequence must span less than 2 GiB");
   return SA_OK;
 }
 

@@ -153,6 +153,13 @@ def test_graph_meanpool_decode_validation(L):
     bad[15] = 0                                                              # f32 decode
     assert d(*bad, P, ws, None) == 2
     assert L.sa_sparse_decode_workspace(2, 1024, 16, 3, 128, 64, 16, 512, 0) == 0
+    # the block means of one sequence must span less than 2 GiB: 2^18 blocks x 16 KV heads
+    # x 128 dims x 4 bytes is 2 GiB exactly (no launch: the size check comes first)
+    big = list(args)
+    big[6], big[7], big[8], big[10] = 16 * 262144, 16, 16, 16
+    assert d(*big, P, ws, None) == 2
+    assert L.sa_sparse_decode_workspace(1, 16 * 262144, 16, 16, 128, 16, 16, 512, 0) == 0
+    assert L.sa_sparse_decode_workspace(1, 16 * 262144, 16, 8, 128, 16, 16, 512, 0) > 0
 
 
 def test_decode_auto_splits(L):

@@ -120,8 +120,9 @@ int sa_topk_select(const float* scores, int64_t ld, int B, int T, int row_begin,
  * qi [B, T, H_I, D_I] and ki [B, T, D_I] bf16 or E4M3 (dtype); w [H_I] float32;
  * idx [B, T, k] int32.
  * workspace: device memory of at least sa_indexer_topk_workspace(...) bytes, no
- * initialisation needed; it holds per-row samples, thresholds and candidate lists
- * (about (row_end / 256) * 2 KB per row), so long rows are best processed in row chunks.
+ * initialisation needed; it holds per-row samples, thresholds and candidate lists (up to
+ * 64 lists of 324 entries of 8 bytes per row: about 162 KB per row once row_end exceeds
+ * 16,384) and up to 256 MB of slots for rows recomputed in full.
  * Once the call has run, the first 4 bytes of the workspace hold, as a uint32, the
  * number of rows that were recomputed in full (a diagnostic; 0 in the usual case).  The
  * kept set is about 1.3-1.6 k entries; beyond k of about 3000 most rows are selected by

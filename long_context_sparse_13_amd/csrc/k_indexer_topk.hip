@@ -16,17 +16,21 @@
 //     so thr is almost always below the k-th largest score.
 //  3. indexer_cand: full MFMA scoring of 32 rows x 64 keys per wavefront step, staged in
 //     LDS; then, row by row, one ballot over the 64 keys finds the scores >= thr, which
-//     go as (score bits, position) to the row's list for that 256-key chunk, in position
-//     order (list length in counts[row, chunk]).  Nothing else is written.
-//  4. cand_topk: one wavefront per row; the chunk lists, concatenated in position order,
-//     are spread over the lanes' registers (up to 4096 entries) and the exact top-k is
-//     taken from them: a radix select whose digits cover only the key range actually
-//     present (so a few hot bins do not serialise the histogram), then output ranks
-//     from two wavefront scans.  Every score >= thr is in the lists, so when they hold
-//     at least k entries they hold the k largest.  Rows with more than 4096 entries are
-//     selected with streaming passes over the lists instead; rows with fewer than k (thr
-//     was above the k-th score) are recomputed in full into their own list area and
-//     selected there with passes over global memory: the answer is exact in every case.
+//     go as (score bits, position) to the row's list for the chunk's group: the 256-key
+//     chunks c with the same c mod 64 are scored by one wavefront, one after the other,
+//     and share a list of at most 256 entries, in position order within each chunk
+//     (counts[row, chunk] = the list's length once that chunk is appended).  Nothing else
+//     is written.
+//  4. cand_topk: one wavefront per row; the chunks' runs of entries, concatenated in
+//     position order, are spread over the lanes' registers (up to 4096 entries) and the
+//     exact top-k is taken from them: a radix select whose digits cover only the key range
+//     actually present (so a few hot bins do not serialise the histogram), then output
+//     ranks from two wavefront scans.  Every score >= thr is in the lists, so when they
+//     hold at least k entries they hold the k largest.  Rows with more than 4096 entries
+//     are selected with streaming passes over the lists instead; rows with fewer than k
+//     (thr was above the k-th score) or a list that ran out of room are listed and
+//  5. fix_rows_k recomputes them in full into a slot of their own and selects there with
+//     passes over global memory: the answer is exact in every case.
 #include "indexer_tile.h"
 #include "sa_launch.h"
 #include "sa_device.h"
@@ -192,6 +196,15 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- 3. candidates
+// A row keeps one candidate list per chunk group (the chunks c with the same c mod
+// kIdxGroups, which one wavefront scores) of at most kGroupCap entries, kListLd apart.  A
+// length of kListFull (recorded once a list was offered more than kGroupCap entries) marks
+// a list that ran out of room; its stores went to the kListLd - kGroupCap spare entries
+// behind it (writes start at most kListFull and a block adds at most 64).
+constexpr int kGroupCap = 256;
+constexpr uint32_t kListFull = kGroupCap + 1;
+constexpr int kListLd = kGroupCap + 1 + 64 + 3;  // 324 entries
+
 template <int H, int DI, bool F8>
 __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ qi,
                                                      const uint8_t* __restrict__ ki,
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
                                                      int row_begin, int row_end, int k,
                                                      const float* __restrict__ thr,
                                                      uint16_t* __restrict__ counts,
-                                                     u32x2* __restrict__ cand, int nch) {
+                                                     u32x2* __restrict__ cand, int nch, int ng) {
   using IW = IdxWave<H, DI, F8>;
   constexpr int SB = 64;        // keys per staged block (4 tiles)
   constexpr int SROW = SB + 4;  // padded LDS row (floats)
@@ -232,14 +245,16 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
   const float thr_v = my_ok ? thr[(int64_t)b * R + (my_t - row_begin)] : INFINITY;
   const int64_t row0 = (int64_t)b * R + (t0 - row_begin);
 
+  // This wavefront's rows keep one list per row for its group (chunks group, group +
+  // kIdxGroups, ...), appended chunk after chunk.  Running lengths (uniform; at most 64
+  // per 64-key block of the group, so below 2^16): rows 2i and 2i + 1 in the low and high
+  // halves of cnt2[i], so the 32 lengths take 16 scalar registers.
+  uint32_t cnt2[IW::ROWS / 2];
+#pragma unroll
+  for (int i = 0; i < IW::ROWS / 2; ++i) cnt2[i] = 0u;
   for (int c = group; c < wave_chunks; c += kIdxGroups) {
     const int s_lo = c * kIdxChunk;
     const int s_hi = min(s_lo + kIdxChunk, t_last + 1);
-    // list lengths of this chunk so far (uniform; <= 256): rows 2i and 2i + 1 in the low and
-    // high halves of cnt2[i], so the 32 counts take 16 scalar registers
-    uint32_t cnt2[IW::ROWS / 2];
-#pragma unroll
-    for (int i = 0; i < IW::ROWS / 2; ++i) cnt2[i] = 0u;
     typename IW::Keys bk;
     IW::load_keys(kib, min(s_lo + n, T - 1), grp, bk);
     for (int j0 = s_lo; j0 < s_hi; j0 += SB) {
@@ -259,14 +274,16 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
       float vals[IW::ROWS];
 #pragma unroll
       for (int rr = 0; rr < IW::ROWS; ++rr) vals[rr] = st[rr * SROW + lane];
-      // the lists of this chunk for the wavefront's 32 rows as one buffer resource: a
-      // lane's store goes to byte offset 8 (rr * rstride + entry); lanes without a
-      // candidate get an offset past the range, and the hardware drops those stores, so
-      // the compaction needs no exec-mask changes or branches.  The base is opaque per
-      // block so the compiler forms it here instead of keeping it live across blocks.
-      int64_t cbo = (row0 * nch + c) * kIdxChunk;
+      // the group lists of the wavefront's 32 rows as one buffer resource: a lane's store
+      // goes to byte offset 8 (rr * rstride + entry); lanes without a candidate get an
+      // offset past the range, and the hardware drops those stores, so the compaction
+      // needs no exec-mask changes or branches.  Entries past kGroupCap (a list that ran
+      // out of room) go to the list's spare entries, the write position held at
+      // kListFull.  The base is opaque per block so the compiler forms it here instead of
+      // keeping it live across blocks.
+      int64_t cbo = (row0 * ng + group) * kListLd;
       asm volatile("" : "+s"(cbo));
-      const uint32_t rstride8 = (uint32_t)nch * kIdxChunk * 8u;  // bytes between rows' lists
+      const uint32_t rstride8 = (uint32_t)ng * kListLd * 8u;  // bytes between rows' lists
       const __amdgpu_buffer_rsrc_t lists = __builtin_amdgcn_make_buffer_rsrc(
           cand + cbo, 0, (int)(rstride8 * IW::ROWS), 0x00020000);
       auto compact = [&](auto diag_tag) {
@@ -276,7 +293,7 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
           const float th = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr_v), rr));
           const bool hit = vals[rr] >= th && (!DIAG || s <= t0 + rr);
           const uint64_t m = ballot(hit);
-          const uint32_t cnt = (cnt2[rr >> 1] >> (16 * (rr & 1))) & 0xffffu;
+          const uint32_t cnt = min((cnt2[rr >> 1] >> (16 * (rr & 1))) & 0xffffu, kListFull);
           const uint32_t at = (uint32_t)rr * rstride8 + (cnt + (uint32_t)lanes_below(m)) * 8u;
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(vals[rr]), (uint32_t)s}, lists,
                                                hit ? at : 0xffffffffu, 0, 0);
@@ -287,11 +304,12 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
       else compact(std::false_type{});
       wave_lds_sync();
     }
-    uint32_t cnt_v = 0u;  // lane rr takes the count of row rr
+    // lane rr: row rr's list length after this chunk (kListFull once past kGroupCap)
+    uint32_t cnt_v = 0u;
 #pragma unroll
     for (int rr = 0; rr < IW::ROWS; ++rr)
       cnt_v = lane == rr ? (cnt2[rr >> 1] >> (16 * (rr & 1))) & 0xffffu : cnt_v;
-    if (my_ok) counts[(row0 + lane) * nch + c] = (uint16_t)cnt_v;
+    if (my_ok) counts[(row0 + lane) * nch + c] = (uint16_t)min(cnt_v, kListFull);
   }
 }
 
@@ -306,7 +324,7 @@ constexpr int kMarkCap = 64 * kCandPerLane;  // entries the mark table covers
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cand_topk(
     int B, int T, int row_begin, int row_end, int k, const float* __restrict__ thr,
-    const uint16_t* __restrict__ counts, const u32x2* __restrict__ cand, int nch,
+    const uint16_t* __restrict__ counts, const u32x2* __restrict__ cand, int nch, int ng,
     int32_t* __restrict__ idx, uint32_t* __restrict__ n_recomputed, int* __restrict__ fix_rows) {
   constexpr int J = kCandPerLane;
   // per wavefront: the list-start marks (during the gather) or the radix histogram
@@ -329,15 +347,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   }
   const int64_t rowi = (int64_t)b * R + r;
   const uint16_t* __restrict__ cr = counts + rowi * nch;
-  const u32x2* __restrict__ cl = cand + rowi * nch * kIdxChunk;
+  const u32x2* __restrict__ cl = cand + rowi * ng * kListLd;
   uint32_t* hist = work_s[wv];
   uint16_t* mark = reinterpret_cast<uint16_t*>(work_s[wv]);
   uint32_t* nz = nz_s[wv];
   uint32_t* sbin = sbin_s[wv];
   const int nc = t / kIdxChunk + 1;  // chunks of this row (<= 1024)
 
-  // ---- list lengths: lane L holds chunks 256 g + 4 L + i (g < 4, i < 4) in registers
-  uint32_t len4[4][2];  // two u16 lengths per word
+  // ---- list lengths.  counts[row, c] is the length of chunk c's group list once chunk c
+  // was appended; lane L holds chunks 256 g + 4 L + i (g < 4, i < 4) in registers, and the
+  // previous chunk of the same group, c - kIdxGroups, is held by lane L - 16 (by lane
+  // L + 48 in the previous g): chunk c's entries are that list's [prev, count).
+  static_assert(kIdxGroups == 64, "the lane mapping of the group lists assumes 64 groups");
+  uint32_t len4[4][2], prv4[4][2];  // two u16 values per word
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int c = 256 * g + 4 * lane;
@@ -346,10 +368,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     len4[g][0] = x[0];
     len4[g][1] = x[1];
   }
+  {
+    uint32_t up[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) up[g][w2] = (uint32_t)shfl_i((int)len4[g][w2], (lane + 48) & 63);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) prv4[g][w2] = lane >= 16 ? up[g][w2] : g > 0 ? up[g - 1][w2] : 0u;
+  }
+  auto half16 = [](uint32_t wd, int i) -> int { return (int)((wd >> (16 * (i & 1))) & 0xffffu); };
   auto len_of = [&](int g, int i) -> int {
     const int c = 256 * g + 4 * lane + i;
-    return c < nc ? (int)((len4[g][i >> 1] >> (16 * (i & 1))) & 0xffffu) : 0;
+    return c < nc ? half16(len4[g][i >> 1], i) - half16(prv4[g][i >> 1], i) : 0;
   };
+  // a list that ran out of room: the row is recomputed in full
+  bool full = false;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      full |= 256 * g + 4 * lane + i < nc && half16(len4[g][i >> 1], i) == (int)kListFull;
+  if (ballot(full) != 0ull) {
+    if (lane == 0) fix_rows[atomicAdd(n_recomputed, 1u)] = (int)rowi;
+    return;
+  }
   int n_hits = 0, n_nz = 0, run[4], zrun[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -387,7 +432,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
       for (int i = 0; i < 4; ++i) {
         const int x = len_of(g, i);
         if (x > 0) {
-          nz[zo] = ((uint32_t)(256 * g + 4 * lane + i) << 16) | (uint32_t)o;
+          // entry e (o <= e < o + x) of the concatenation is cl[nz + e]
+          nz[zo] = (uint32_t)(((4 * lane + i) & (kIdxGroups - 1)) * kListLd +
+                              half16(prv4[g][i >> 1], i) - o);
           mark[o] = (uint16_t)zo;
           atomicAdd(&sbin[o >> 6], 1u);
           ++zo;
@@ -416,8 +463,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
           const int m = max(__builtin_amdgcn_readlane(before_v, j),
                             wave_incl_scan(mr != 0xffff ? mr : INT_MIN, INT_MIN,
                                            [](int x, int y) { return max(x, y); }));
-          const uint32_t info = nz[m];
-          const u32x2 ent = cl[(int)(info >> 16) * kIdxChunk + (e - (int)(info & 0xffffu))];
+          const u32x2 ent = cl[(int)nz[m] + e];
           key[j] = ent[0];
           pos[j] = (int)ent[1];
         }
@@ -491,8 +537,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     // ---- more entries than the registers hold: streaming passes over the lists, lane L
     // taking the chunks L, L + 64, ... (each list read in batches of 16 entries)
     auto each_entry = [&](int c, auto&& f) {
-      const int len = cr[c];
-      const u32x2* src = cl + (int64_t)c * kIdxChunk;
+      const int st = c >= kIdxGroups ? (int)cr[c - kIdxGroups] : 0;
+      const int len = (int)cr[c] - st;
+      const u32x2* src = cl + (c & (kIdxGroups - 1)) * kListLd + st;
       for (int e0 = 0; e0 < len; e0 += 16) {
         u32x2 ev[16];
 #pragma unroll
@@ -549,62 +596,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
 }
 
 // ---------------------------------------------------------------- 5. listed rows
-// fix_score scores each row listed by cand_topk in full into the row's own list area
-// (16-byte aligned, (t/256 + 1) * 2 KB >= 4 (t + 1) bytes), one wavefront per 256-key
-// chunk of a row, spread over the whole grid, with the same MFMA arithmetic as every
-// other indexer kernel; fix_select then runs the two-step path's two-pass radix selection
-// (topk_row) over each listed row.  With no listed row both return at once.
+// fix_rows_k recomputes the rows cand_topk listed: workgroup w takes listed rows w,
+// w + gridDim.x, ... and scores each in full (t + 1 scores, its wavefronts taking the
+// 256-key chunks in turn, with the same MFMA arithmetic as every other indexer kernel)
+// into its own slot of the fix area, then runs the two-step path's two-pass radix
+// selection (topk_row) over that slot.  With no listed row it returns at once.
 template <int H, int DI, bool F8>
-__global__ __launch_bounds__(256) void fix_score(const uint8_t* __restrict__ qi,
-                                                 const uint8_t* __restrict__ ki,
-                                                 const float* __restrict__ wgt, int T,
-                                                 int row_begin, int row_end,
-                                                 u32x2* __restrict__ cand, int nch,
-                                                 const uint32_t* __restrict__ n_fix,
-                                                 const int* __restrict__ fix_rows) {
+__global__ __launch_bounds__(kTkThreads) void fix_rows_k(const uint8_t* __restrict__ qi,
+                                                         const uint8_t* __restrict__ ki,
+                                                         const float* __restrict__ wgt, int T,
+                                                         int row_begin, int row_end, int k,
+                                                         float* __restrict__ area,
+                                                         int64_t area_ld,
+                                                         int32_t* __restrict__ idx,
+                                                         const uint32_t* __restrict__ n_fix,
+                                                         const int* __restrict__ fix_rows) {
   using IW = IdxWave<H, DI, F8>;
+  __shared__ TopkShared sh;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = row_end - row_begin;
-  const int maxch = (row_end - 1) / kIdxChunk + 1;
-  const int64_t items = (int64_t)__builtin_amdgcn_readfirstlane((int)*n_fix) * maxch;
-  for (int64_t it = (int64_t)blockIdx.x * 4 + wv; it < items; it += (int64_t)gridDim.x * 4) {
-    const int i = (int)(it / maxch), c = (int)(it % maxch);
+  const int cnt = __builtin_amdgcn_readfirstlane((int)*n_fix);
+  float* __restrict__ frow = area + (int64_t)blockIdx.x * area_ld;
+  for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
     const int rowi = fix_rows[i];
     const int b = rowi / R, t = row_begin + rowi % R;
-    if (c * kIdxChunk > t) continue;
-    float* frow = reinterpret_cast<float*>(cand + (int64_t)rowi * nch * kIdxChunk);
     IW iw;
     iw.load_single(qi + (int64_t)b * T * H * DI * IW::EB, t, wgt, lane & 15, lane >> 4);
     const uint8_t* kib = ki + (int64_t)b * T * DI * IW::EB;
     constexpr int U = kIdxChunk / 16;  // the chunk's key tiles, all in flight
-    typename IW::Keys bk[U];
+    for (int c = wv; c * kIdxChunk <= t; c += kTkWaves) {
+      typename IW::Keys bk[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      IW::load_keys(kib, min(c * kIdxChunk + u * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
+      for (int u = 0; u < U; ++u)
+        IW::load_keys(kib, min(c * kIdxChunk + u * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float sc = iw.score_single(bk[u]);
-      const int key = c * kIdxChunk + u * 16 + (lane & 15);
-      if (lane < 16 && key <= t) frow[key] = sc;
+      for (int u = 0; u < U; ++u) {
+        const float sc = iw.score_single(bk[u]);
+        const int key = c * kIdxChunk + u * 16 + (lane & 15);
+        if (lane < 16 && key <= t) frow[key] = sc;
+      }
     }
-  }
-}
-
-__global__ __launch_bounds__(kTkThreads) void fix_select(int T, int row_begin, int row_end, int k,
-                                                         const u32x2* __restrict__ cand, int nch,
-                                                         int32_t* __restrict__ idx,
-                                                         const uint32_t* __restrict__ n_fix,
-                                                         const int* __restrict__ fix_rows) {
-  __shared__ TopkShared sh;
-  const int R = row_end - row_begin;
-  const int cnt = (int)*n_fix;
-  for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
-    const int rowi = fix_rows[i];
-    const int b = rowi / R, t = row_begin + rowi % R;
-    const float* frow = reinterpret_cast<const float*>(cand + (int64_t)rowi * nch * kIdxChunk);
+    __syncthreads();  // the row's scores are in its slot
     topk_row(frow, t + 1, k, idx + ((int64_t)b * T + t) * k, sh);
-    __syncthreads();
+    __syncthreads();  // the slot is free for the next row
   }
 }
 
@@ -612,9 +647,9 @@ __global__ __launch_bounds__(kTkThreads) void fix_select(int T, int row_begin, i
 namespace {
 
 struct IdxTopkPlan {
-  int sshift, jrank, nch;
-  int64_t ns_ld;
-  size_t off_stat, off_samp, off_thr, off_cnt, off_fix, off_cand, total;
+  int sshift, jrank, nch, ng, nslots;
+  int64_t ns_ld, fix_ld;
+  size_t off_stat, off_samp, off_thr, off_cnt, off_fix, off_cand, off_area, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -635,9 +670,17 @@ IdxTopkPlan plan_indexer_topk(int B, int row_begin, int row_end, int k) {
   while (sq * sq < kf) ++sq;
   p.sshift = sshift;
   p.jrank = kf + 4 * sq + 4;
-  p.nch = ((row_end - 1) / kIdxChunk + 1 + 3) / 4 * 4;  // multiple of 4: 8-byte count loads
+  const int nchunks = (row_end - 1) / kIdxChunk + 1;
+  p.nch = (nchunks + 3) / 4 * 4;  // multiple of 4: 8-byte count loads
+  p.ng = nchunks < kIdxGroups ? nchunks : kIdxGroups;  // candidate lists per row
   p.ns_ld = ((int64_t)((row_end - 1) >> sshift) + 1 + 3) / 4 * 4;
   const int64_t rows = (int64_t)B * (row_end - row_begin);
+  // the recompute slots: one full row of scores each, as many as fit 256 MB (1 to 256,
+  // and no more than there are rows)
+  p.fix_ld = ((int64_t)row_end + 63) / 64 * 64;
+  const int64_t fit = ((int64_t)256 << 20) / (p.fix_ld * (int64_t)sizeof(float));
+  p.nslots = (int)(fit < 1 ? 1 : fit > 256 ? 256 : fit);
+  if (p.nslots > rows) p.nslots = (int)rows;
   size_t o = 0;
   p.off_stat = o;  // uint32: rows recomputed in full by the last call
   o = align256(o + sizeof(uint32_t));
@@ -649,8 +692,10 @@ IdxTopkPlan plan_indexer_topk(int B, int row_begin, int row_end, int k) {
   o = align256(o + (size_t)rows * p.nch * sizeof(uint16_t));
   p.off_fix = o;  // int32: rows listed for recomputation
   o = align256(o + (size_t)rows * sizeof(int));
-  p.off_cand = o;
-  o = align256(o + (size_t)rows * p.nch * kIdxChunk * sizeof(u32x2));
+  p.off_cand = o;  // per row: ng lists of kListLd (score bits, position) pairs
+  o = align256(o + (size_t)rows * p.ng * kListLd * sizeof(u32x2));
+  p.off_area = o;  // float: the recompute slots
+  o = align256(o + (size_t)p.nslots * p.fix_ld * sizeof(float));
   p.total = o;
   return p;
 }
@@ -672,6 +717,7 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
   u32x2* cand = reinterpret_cast<u32x2*>(ws + p.off_cand);
   uint32_t* stat = reinterpret_cast<uint32_t*>(ws + p.off_stat);
   int* fix = reinterpret_cast<int*>(ws + p.off_fix);
+  float* area = reinterpret_cast<float*>(ws + p.off_area);
   const int R = row_end - row_begin;
 
   // the sample: slot chunks of 64 spread the short sampled rows over more workgroups
@@ -690,17 +736,16 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
     constexpr int HH = decltype(h)::value, DD = decltype(d)::value;
     constexpr bool FF = decltype(f)::value;
     hipLaunchKernelGGL((indexer_cand<HH, DD, FF>), g3, dim3(256), 0, st, (const uint8_t*)qi,
-                       (const uint8_t*)ki, w, T, row_begin, row_end, k, thr, cnt, cand, p.nch);
+                       (const uint8_t*)ki, w, T, row_begin, row_end, k, thr, cnt, cand, p.nch,
+                       p.ng);
     hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL(cand_topk, g4, dim3(256), 0, st, B, T, row_begin, row_end, k, thr, cnt,
-                       cand, p.nch, idx, stat, fix);
+                       cand, p.nch, p.ng, idx, stat, fix);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
-    hipLaunchKernelGGL((fix_score<HH, DD, FF>), dim3(512), dim3(256), 0, st, (const uint8_t*)qi,
-                       (const uint8_t*)ki, w, T, row_begin, row_end, cand, p.nch, stat, fix);
-    if ((e2 = hipGetLastError()) != hipSuccess) return e2;
-    hipLaunchKernelGGL(fix_select, dim3(256), dim3(kTkThreads), 0, st, T, row_begin, row_end, k,
-                       cand, p.nch, idx, stat, fix);
+    hipLaunchKernelGGL((fix_rows_k<HH, DD, FF>), dim3((unsigned)p.nslots), dim3(kTkThreads), 0, st,
+                       (const uint8_t*)qi, (const uint8_t*)ki, w, T, row_begin, row_end, k, area,
+                       p.fix_ld, idx, stat, fix);
     return hipGetLastError();
   });
 }

@@ -120,6 +120,27 @@ def test_list_passes_when_candidates_overflow():
     _case({"qi": qi, "ki": ki, "w": w}, 4000, 8100, 8400, max_recomputed=0)
 
 
+def test_recompute_when_a_group_list_is_full():
+    # the keys of chunks 0, 64 and 128 (positions [0, 256), [16384, 16640), [32768, 33024),
+    # all scored by the same wavefront group and kept in one list of at most 256 entries)
+    # score far above the rest: rows with two or three such chunks behind them have more
+    # candidates in that list than it holds and are recomputed in full (more rows than
+    # recompute slots); rows with only the first such chunk fit and are not
+    g = sa_synth.rng(620)
+    T, H, DI, k = 40000, 4, 32, 600
+    qi = np.ones((1, T, H, DI), np.float32)
+    ki = g.integers(-1, 2, size=(1, T, DI)).astype(np.float32)
+    for c0 in (0, 16384, 32768):
+        ki[0, c0:c0 + 256] = 3.0 + g.integers(0, 3, size=(256, DI))
+    w = np.array([0.5, 0.25, 0.125, 1.0], np.float32)
+    x = {"qi": qi, "ki": ki, "w": w}
+    _, nrec = _case(x, k, 39000, 40000)
+    assert nrec == 1000, nrec
+    _, nrec = _case(x, k, 20000, 20300)
+    assert nrec == 300, nrec
+    _, nrec = _case(x, k, 10000, 10200, max_recomputed=0)
+
+
 def test_64k_rows():
     # the 64K prefill sizes (k = 2048): the last rows of the longest chunk
     x = sa_synth.indexer_inputs(618, 1, 65536, 4, 64, "bf16")

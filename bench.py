@@ -3,9 +3,10 @@
 
 One step = the whole DSA-style prefill hot path on the 64K workload (T = 65,536 tokens,
 16 query heads on 1 KV head of dim 128, bf16; indexer of 4 heads x 64; top-2048 per query
-united with a 128-token window): the fused indexer -> top-k (sa_indexer_topk) over two
-32,768-row chunks, then sa_sparse_attn_fwd (``--indices two-step`` builds the indices with
-sa_indexer_scores + sa_topk_select instead).  Inputs are seeded synthetic tensors
+united with a 128-token window): the fused indexer -> top-k (sa_indexer_topk) in one call
+over all 65,536 rows (``--chunk`` splits it into row chunks), then sa_sparse_attn_fwd
+(``--indices two-step`` builds the indices with sa_indexer_scores + sa_topk_select, in
+chunks of at most 32,768 rows, instead).  Inputs are seeded synthetic tensors
 (sa_synth), resident in HBM before the timed region.  ``value`` is query tokens per second
 of the whole step.
 
@@ -161,7 +162,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--chunk", type=int, default=32768, help="indexer/top-k rows per chunk")
+    ap.add_argument("--chunk", type=int, default=65536, help="indexer/top-k rows per call")
     ap.add_argument("--indices", choices=["fused", "two-step"], default="fused",
                     help="how the step builds the indices: sa_indexer_topk, or "
                          "sa_indexer_scores + sa_topk_select")
@@ -258,9 +259,10 @@ def main():
     qi, ki, w = to_dev(x["qi"], "bf16"), to_dev(x["ki"], "bf16"), to_dev(x["w"], "f32")
     q, k, v = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16")
     chunk = min(args.chunk, T)
+    chunk2 = min(chunk, 32768)  # the two-step path's row chunks (its score buffer: 8.6 GB)
     ld = ((T + 3) // 4) * 4
     fused = args.indices == "fused"
-    scores = torch.empty((1, chunk, ld), dtype=torch.float32, device=dev)
+    scores = torch.empty((1, chunk2, ld), dtype=torch.float32, device=dev)
     # the last row chunk is the longest, so its workspace serves every chunk
     ws = torch.empty(sa.sa_indexer_topk_workspace(1, T, HI, DI, T - chunk, T, topk),
                      dtype=torch.uint8, device=dev)
@@ -269,8 +271,8 @@ def main():
     tm = Timer(torch)
 
     def two_step_indices(timer):
-        for r0 in range(0, T, chunk):
-            r1 = min(T, r0 + chunk)
+        for r0 in range(0, T, chunk2):
+            r1 = min(T, r0 + chunk2)
             sc = scores[:, : r1 - r0]  # (the last chunk may be shorter; a prefix stays contiguous)
             timer.run("indexer", lambda: sa.sa_indexer_scores(qi, ki, w, r0, r1, sc, ld))
             timer.run("topk", lambda: sa.sa_topk_select(sc, topk, T, r0, r1, idx, ld))
@@ -334,8 +336,10 @@ def main():
             prefill_indices(Timer(torch))  # leave the step's own indices in idx
             torch.cuda.synchronize()
     # the same step on two streams: the attention of a row chunk starts as soon as that
-    # chunk's indices exist, beside the next chunk's index build (sa_sparse_attn_fwd_rows)
+    # chunk's indices exist, beside the next chunk's index build (sa_sparse_attn_fwd_rows);
+    # two chunks when the step makes one call
     two_streams = None
+    pchunk = chunk if chunk < T else (T + 1) // 2
     if fused and args.only is None:
         s_idx, s_att = torch.cuda.Stream(), torch.cuda.Stream()
 
@@ -343,8 +347,8 @@ def main():
             cur = torch.cuda.current_stream()
             s_idx.wait_stream(cur)
             s_att.wait_stream(cur)
-            for r0 in range(0, T, chunk):
-                r1 = min(T, r0 + chunk)
+            for r0 in range(0, T, pchunk):
+                r1 = min(T, r0 + pchunk)
                 with torch.cuda.stream(s_idx):
                     sa.sa_indexer_topk(qi, ki, w, topk, r0, r1, idx, ws)
                     ev = torch.cuda.Event()
@@ -367,7 +371,7 @@ def main():
         torch.cuda.synchronize()
         ms_p = e0.elapsed_time(e1) / args.steps
         two_streams = {"ms_per_step": ms_p, "query_tokens_per_s": T / (ms_p * 1e-3),
-                       "vs_sequential_step": ms_step / ms_p,
+                       "vs_sequential_step": ms_step / ms_p, "row_chunk": pchunk,
                        "same_output": bool(torch.equal(out_seq, out))}
         log(f"two streams: {ms_p:.3f} ms/step (sequential {ms_step:.3f})")
         del out_seq

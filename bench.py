@@ -743,8 +743,11 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64, keep
         ws0 = torch.zeros(sa.sa_sparse_decode_workspace(p["B"], p["L"], p["Hq"], p["Hkv"], p["D"],
                                                         p["block"], p["top_blocks"], 0, 0),
                           dtype=torch.uint8, device=dev)
-        # the compressed range (L/64 = 2048 rows) split over 8 workgroups per sequence
-        ns_c = 8
+        # the compressed range (L/64 = 2048 rows) split over 7 workgroups per sequence: with
+        # the window's one, 32 x 8 = 256 workgroups of 8 wavefronts, one per CU (their
+        # registers fill it), so the combined launch runs in one round (8 + 1 splits:
+        # 37 us instead of 29)
+        ns_c = 7
         ws_c = torch.zeros(sa.sa_nsa_decode_branch_workspace(p["B"], p["Hq"], p["Hkv"], p["D"], ns_c),
                            dtype=torch.uint8, device=dev)
         ocd, osd, owd, ond = (torch.empty_like(qd) for _ in range(4))
@@ -761,15 +764,33 @@ def extra_rows(torch, np, sa, sa_synth, to_dev, args, q64, k64, v64, idx64, keep
             "combine": lambda: sa.sa_nsa_combine(ocd[:, None], osd[:, None], owd[:, None], gd,
                                                  out=ond[:, None]),
         }
+        # the step: compressed and window branches in one launch, the selected branch, the
+        # combine; each branch alone and the four separate calls are timed beside
+        ocw, oww = torch.empty_like(qd), torch.empty_like(qd)
+        ws_cw = torch.zeros(max(256, sa.sa_nsa_decode_cmp_win_workspace(p["B"], p["Hq"], p["Hkv"],
+                                                                        p["D"], ns_c, 1)),
+                            dtype=torch.uint8, device=dev)
+        step_fns = [
+            lambda: sa.sa_nsa_decode_cmp_win(qd, kb16, vb16, kc, vc, lens, p["block"], p["window"],
+                                             p["scale"], out_cmp=ocw, out_win=oww,
+                                             n_splits_cmp=ns_c, workspace=ws_cw),
+            dparts["selected"],
+            lambda: sa.sa_nsa_combine(ocw[:, None], osd[:, None], oww[:, None], gd,
+                                      out=ond[:, None]),
+        ]
         dpart_us = {name: timed_cold(fn, 20) * 1e3 for name, fn in dparts.items()}
-        t_nd = timed_cold(lambda: [fn() for fn in dparts.values()], 20)
-        t_nd_warm = timed(lambda: [fn() for fn in dparts.values()], 20)
+        dpart_us["compressed_and_window"] = timed_cold(step_fns[0], 20) * 1e3
+        t_sep = timed_cold(lambda: [fn() for fn in dparts.values()], 20)
+        t_nd = timed_cold(lambda: [fn() for fn in step_fns], 20)
+        t_nd_warm = timed(lambda: [fn() for fn in step_fns], 20)
         rows["nsa_decode_b32_128k"] = {
             "us_per_step": t_nd * 1e3, "warm_us_per_step": t_nd_warm * 1e3, "timing": "cold",
             "tokens_per_s": p["B"] / (t_nd * 1e-3), "parts_us": dpart_us,
+            "separate_branch_calls_us_per_step": t_sep * 1e3,
             "compressed_splits": ns_c,
             "bf16_meanpool_ms_once_per_cache": t_pool16,
         }
+        del ocw, oww, ws_cw
         del kb16, vb16, ws0, ocd, osd, owd, ond, gd
         del qd, kc, vc, kbar, ws, od
         torch.cuda.empty_cache()

@@ -378,6 +378,29 @@ int sa_nsa_decode_branch(const void* q, const void* keys, const void* vals,
 size_t sa_nsa_decode_branch_workspace(int B, int Hq, int Hkv, int D, int n_splits);
 
 /*
+ * NSA decode: the compressed and the window branch of sa_nsa_decode_branch (kinds 1 and 0)
+ * in one launch.  [NSA] "Puntos Clave": the branches are independent; here they share the
+ * launch's fixed costs and run side by side.  Results equal those of the two
+ * sa_nsa_decode_branch calls bit for bit (each branch's workgroups run that call's code).
+ * kbar16, vbar16 [B, Lmax/block, Hkv, D] bf16 (sa_block_meanpool_bf16 of K and of V);
+ * kcache, vcache [B, Lmax, Hkv, D] bf16; q, out_cmp, out_win [B, Hq, D] bf16; lens [B]
+ * int32 on the device (clamped as for sa_nsa_decode_branch); lse_cmp, lse_win [B, Hq]
+ * float32 or NULL.  n_splits_cmp, n_splits_win in 1..64; workspace: at least
+ * sa_nsa_decode_cmp_win_workspace(...) bytes (the compressed side's area, then the window
+ * side's), ZERO-FILLED before its first use and left that way by every call (calls sharing
+ * a workspace must be ordered on one stream); may be NULL when both split counts are 1.
+ * Requires bf16, D in {64, 128}, Hq/Hkv <= 16, block in {16, 32, 64, 128}, Lmax >= block.
+ */
+int sa_nsa_decode_cmp_win(const void* q, const void* kbar16, const void* vbar16,
+                          const void* kcache, const void* vcache, const int32_t* lens, int B,
+                          int Lmax, int Hq, int Hkv, int D, int block, int window, float scale,
+                          int dtype, void* out_cmp, float* lse_cmp, void* out_win, float* lse_win,
+                          int n_splits_cmp, int n_splits_win, void* workspace, size_t ws_bytes,
+                          void* stream);
+size_t sa_nsa_decode_cmp_win_workspace(int B, int Hq, int Hkv, int D, int n_splits_cmp,
+                                       int n_splits_win);
+
+/*
  * NSA gated combine.  [NSA] "Puntos Clave" (three branches) -- the page does not say how
  * they are joined; NSA gates them per head with weights it learns from the query, which
  * are an input here:

@@ -84,6 +84,12 @@ _SIGS = {
                                       _c_int, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_size_t,
                                       _c_void_p]),
     "sa_nsa_decode_branch_workspace": (_c_size_t, [_c_int] * 5),
+    "sa_nsa_decode_cmp_win": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _c_float, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_int, _c_int, _c_void_p, _c_size_t,
+                                       _c_void_p]),
+    "sa_nsa_decode_cmp_win_workspace": (_c_size_t, [_c_int] * 6),
     "sa_nsa_combine": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                 _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "sa_status_str": (ctypes.c_char_p, [_c_int]),
@@ -635,6 +641,64 @@ def sa_nsa_decode_branch(q, keys, vals, lens, kind: int, block: int, window: int
                                     _p(lse), n_splits, _p(workspace), ws_bytes, _stream(q.device))
     _check("sa_nsa_decode_branch", rc)
     return (out, lse) if want_lse else out
+
+
+def sa_nsa_decode_cmp_win_workspace(B, Hq, Hkv, D, n_splits_cmp, n_splits_win) -> int:
+    return int(lib().sa_nsa_decode_cmp_win_workspace(B, Hq, Hkv, D, n_splits_cmp, n_splits_win))
+
+
+def sa_nsa_decode_cmp_win(q, kbar16, vbar16, kcache, vcache, lens, block: int, window: int,
+                          scale: float, out_cmp=None, out_win=None, lse_cmp=None, lse_win=None,
+                          want_lse: bool = False, n_splits_cmp: int = 1, n_splits_win: int = 1,
+                          workspace=None):
+    """The compressed (over the bf16 block means kbar16/vbar16 [B,Lmax/block,Hkv,D]) and the
+    window (over the caches kcache/vcache [B,Lmax,Hkv,D]) branch of sa_nsa_decode_branch in
+    one launch; returns (out_cmp, out_win), plus (lse_cmp, lse_win) with want_lse.  Split
+    counts above 1 need a zero-filled workspace (allocated here, zeroed, when not given)."""
+    torch = _torch()
+    _dev(q, "q")
+    for t, n in ((kbar16, "kbar16"), (vbar16, "vbar16"), (kcache, "kcache"), (vcache, "vcache")):
+        _dev(t, n, q.dtype)
+    _dev(lens, "lens", torch.int32)
+    _shape(q, "q", None, None, None)
+    B, Hq, D = q.shape
+    _shape(kcache, "kcache", B, None, None, D)
+    _, Lmax, Hkv, _ = kcache.shape
+    _shape(vcache, "vcache", B, Lmax, Hkv, D)
+    _shape(kbar16, "kbar16", B, Lmax // block, Hkv, D)
+    _shape(vbar16, "vbar16", B, Lmax // block, Hkv, D)
+    _shape(lens, "lens", B)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    outs = []
+    for o, n in ((out_cmp, "out_cmp"), (out_win, "out_win")):
+        if o is None:
+            o = torch.empty_like(q)
+        _dev(o, n, q.dtype)
+        _shape(o, n, B, Hq, D)
+        outs.append(o)
+    lses = []
+    for l, n in ((lse_cmp, "lse_cmp"), (lse_win, "lse_win")):
+        if want_lse and l is None:
+            l = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        if l is not None:
+            _dev(l, n, torch.float32)
+            _shape(l, n, B, Hq)
+        lses.append(l)
+    need = sa_nsa_decode_cmp_win_workspace(B, Hq, Hkv, D, n_splits_cmp, n_splits_win)
+    ws_bytes = 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().sa_nsa_decode_cmp_win(_p(q), _p(kbar16), _p(vbar16), _p(kcache), _p(vcache),
+                                     _p(lens), B, Lmax, Hq, Hkv, D, block, window, float(scale),
+                                     _dtype_code(q), _p(outs[0]), _p(lses[0]), _p(outs[1]),
+                                     _p(lses[1]), n_splits_cmp, n_splits_win, _p(workspace),
+                                     ws_bytes, _stream(q.device))
+    _check("sa_nsa_decode_cmp_win", rc)
+    return (outs[0], outs[1], lses[0], lses[1]) if want_lse else (outs[0], outs[1])
 
 
 def sa_sparse_attn_bwd_workspace(B, T, Hkv, D, topk, window, rows=0) -> int:

@@ -397,28 +397,52 @@ __global__ __launch_bounds__(256) void block_topk_expand(const float* __restrict
 // ---------------------------------------------------------------- decode: one row range
 // One workgroup of kRangeWaves wavefronts per (sequence, KV head): the wavefronts take
 // consecutive slices of the range (32-row tiles) through GroupAttn, then their partial
-// softmax states are merged by log-sum-exp through LDS.
+// softmax states are merged by log-sum-exp through LDS.  One launch serves one or two
+// branches (sides): split workgroups y < s0.n_splits run side 0, the next s1.n_splits
+// side 1, so the compressed and the window branch of a decode step can share a launch.
 constexpr int kRangeWaves = 8;
+
+struct RangeSide {
+  const uint16_t* keys;
+  const uint16_t* vals;
+  uint16_t* out;
+  float* lse;
+  float* partials;
+  uint32_t* counters;
+  int Lrows, kind, n_splits;
+};
 
 template <int D>
 __global__ __launch_bounds__(64 * kRangeWaves) void nsa_decode_range(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ keys,
-    const uint16_t* __restrict__ vals, const int32_t* __restrict__ lens, int B, int Lrows,
-    int Hq, int Hkv, int kind, int block, int window, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int n_splits,
-    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ lens, int Hq, int Hkv,
+    int block, int window, float scale_log2, RangeSide s0, RangeSide s1) {
   using GA = GroupAttn<D>;
+  const bool second = (int)blockIdx.y >= s0.n_splits;  // uniform
+  const uint16_t* __restrict__ keys = second ? s1.keys : s0.keys;
+  const uint16_t* __restrict__ vals = second ? s1.vals : s0.vals;
+  uint16_t* __restrict__ out = second ? s1.out : s0.out;
+  float* __restrict__ lse = second ? s1.lse : s0.lse;
+  float* __restrict__ partials = second ? s1.partials : s0.partials;
+  uint32_t* __restrict__ counters = second ? s1.counters : s0.counters;
+  const int Lrows = second ? s1.Lrows : s0.Lrows;
+  const int kind = second ? s1.kind : s0.kind;
+  const int n_splits = second ? s1.n_splits : s0.n_splits;
   constexpr int PS = D + 4;  // floats per (split, head) partial: o[D], m, l, 2 pad
   __shared__ __attribute__((aligned(16))) unsigned char vl[kRangeWaves][GA::LDS_BYTES];
   __shared__ int last;
-  __shared__ float pacc[kRangeWaves][16][D];  // unnormalised O per wave and head
-  __shared__ float pm[kRangeWaves][16], pl[kRangeWaves][16];
+  // once the tiles are done, the staging areas hold each wavefront's unnormalised O per
+  // head, then the maxima and sums (so a CU holds two of these workgroups)
+  static_assert(kRangeWaves * 16 * (D + 2) * 4 <= kRangeWaves * GA::LDS_BYTES,
+                "the merge area must fit the staging areas");
+  float(*pacc)[16][D] = reinterpret_cast<float(*)[16][D]>(&vl[0][0]);
+  float(*pm)[16] = reinterpret_cast<float(*)[16]>(&vl[0][0] + kRangeWaves * 16 * D * 4);
+  float(*pl)[16] = pm + kRangeWaves;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, grp = lane >> 4;
   const int bg = (int)blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int split = (int)blockIdx.y;
+  const int split = (int)blockIdx.y - (second ? s0.n_splits : 0);
   const int G = Hq / Hkv;
   const int h = g * G + n;
   const bool hv = n < G;
@@ -450,6 +474,7 @@ __global__ __launch_bounds__(64 * kRangeWaves) void nsa_decode_range(
   ga.run(te - tb, fetch, finish, kbase, vbase, stride, vl[wv], scale_log2, lane);
 
   const float lt = ga.total_l();
+  __syncthreads();  // every wavefront is done with its staging area
   if (grp == 0) {
     pm[wv][n] = ga.m_run;
     pl[wv][n] = lt;
@@ -549,31 +574,56 @@ size_t nsa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int n_splits) {
   return part + ((size_t)B * Hkv * 4 + 255) / 256 * 256;
 }
 
+static RangeSide range_side(const void* keys, const void* vals, int B, int Lrows, int Hq,
+                            int Hkv, int D, int kind, void* out, float* lse, int n_splits,
+                            void* workspace) {
+  RangeSide r{(const uint16_t*)keys, (const uint16_t*)vals, (uint16_t*)out, lse, nullptr,
+              nullptr, Lrows, kind, n_splits};
+  if (n_splits > 1) {
+    const size_t G = (size_t)(Hq / Hkv);
+    const size_t part = ((size_t)B * Hkv * n_splits * G * (D + 4) * 4 + 255) / 256 * 256;
+    r.partials = static_cast<float*>(workspace);
+    r.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + part);
+  }
+  return r;
+}
+
+static hipError_t launch_ranges(const void* q, const int32_t* lens, int B, int Hq, int Hkv,
+                                int D, int block, int window, float scale, const RangeSide& s0,
+                                const RangeSide& s1, hipStream_t st) {
+  const dim3 grid((unsigned)(B * Hkv), (unsigned)(s0.n_splits + s1.n_splits));
+  const float sl2 = scale * 1.4426950408889634f;
+  if (D == 128)
+    hipLaunchKernelGGL(nsa_decode_range<128>, grid, dim3(64 * kRangeWaves), 0, st,
+                       (const uint16_t*)q, lens, Hq, Hkv, block, window, sl2, s0, s1);
+  else
+    hipLaunchKernelGGL(nsa_decode_range<64>, grid, dim3(64 * kRangeWaves), 0, st,
+                       (const uint16_t*)q, lens, Hq, Hkv, block, window, sl2, s0, s1);
+  return hipGetLastError();
+}
+
 hipError_t launch_nsa_decode_range(const void* q, const void* keys, const void* vals,
                                    const int32_t* lens, int B, int Lrows, int Hq, int Hkv, int D,
                                    int kind, int block, int window, float scale, void* out,
                                    float* lse, int n_splits, void* workspace, hipStream_t st) {
-  const dim3 grid((unsigned)(B * Hkv), (unsigned)n_splits);
-  const float sl2 = scale * 1.4426950408889634f;
-  float* partials = nullptr;
-  uint32_t* counters = nullptr;
-  if (n_splits > 1) {
-    const size_t G = (size_t)(Hq / Hkv);
-    const size_t part = ((size_t)B * Hkv * n_splits * G * (D + 4) * 4 + 255) / 256 * 256;
-    partials = static_cast<float*>(workspace);
-    counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + part);
-  }
-  if (D == 128)
-    hipLaunchKernelGGL(nsa_decode_range<128>, grid, dim3(64 * kRangeWaves), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)keys, (const uint16_t*)vals, lens, B,
-                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse, n_splits,
-                       partials, counters);
-  else
-    hipLaunchKernelGGL(nsa_decode_range<64>, grid, dim3(64 * kRangeWaves), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)keys, (const uint16_t*)vals, lens, B,
-                       Lrows, Hq, Hkv, kind, block, window, sl2, (uint16_t*)out, lse, n_splits,
-                       partials, counters);
-  return hipGetLastError();
+  const RangeSide s0 = range_side(keys, vals, B, Lrows, Hq, Hkv, D, kind, out, lse, n_splits,
+                                  workspace);
+  const RangeSide none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+  return launch_ranges(q, lens, B, Hq, Hkv, D, block, window, scale, s0, none, st);
+}
+
+hipError_t launch_nsa_decode_cmp_win(const void* q, const void* kbar16, const void* vbar16,
+                                     const void* kcache, const void* vcache, const int32_t* lens,
+                                     int B, int Lmax, int Hq, int Hkv, int D, int block,
+                                     int window, float scale, void* out_cmp, float* lse_cmp,
+                                     void* out_win, float* lse_win, int ns_cmp, int ns_win,
+                                     void* workspace, hipStream_t st) {
+  const size_t ws_cmp = ns_cmp > 1 ? nsa_decode_workspace_bytes(B, Hq, Hkv, D, ns_cmp) : 0;
+  const RangeSide sc = range_side(kbar16, vbar16, B, Lmax / block, Hq, Hkv, D, 1, out_cmp, lse_cmp,
+                                  ns_cmp, workspace);
+  const RangeSide sw = range_side(kcache, vcache, B, Lmax, Hq, Hkv, D, 0, out_win, lse_win, ns_win,
+                                  static_cast<char*>(workspace) + ws_cmp);
+  return launch_ranges(q, lens, B, Hq, Hkv, D, block, window, scale, sc, sw, st);
 }
 
 __global__ __launch_bounds__(256) void nsa_combine_k(const uint16_t* __restrict__ oc,

@@ -489,6 +489,68 @@ int sa_nsa_decode_branch(const void* q, const void* keys, const void* vals,
   }
 }
 
+static size_t cmp_win_ws(int B, int Hq, int Hkv, int D, int ns_cmp, int ns_win) {
+  return (ns_cmp > 1 ? sa::nsa_decode_workspace_bytes(B, Hq, Hkv, D, ns_cmp) : 0) +
+         (ns_win > 1 ? sa::nsa_decode_workspace_bytes(B, Hq, Hkv, D, ns_win) : 0);
+}
+
+int sa_nsa_decode_cmp_win(const void* q, const void* kbar16, const void* vbar16,
+                          const void* kcache, const void* vcache, const int32_t* lens, int B,
+                          int Lmax, int Hq, int Hkv, int D, int block, int window, float scale,
+                          int dtype, void* out_cmp, float* lse_cmp, void* out_win, float* lse_win,
+                          int n_splits_cmp, int n_splits_win, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  try {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(kbar16);
+    REQUIRE_PTR(vbar16);
+    REQUIRE_PTR(kcache);
+    REQUIRE_PTR(vcache);
+    REQUIRE(lens, "lens is NULL");
+    REQUIRE_PTR(out_cmp);
+    REQUIRE_PTR(out_win);
+    REQUIRE(B >= 1 && Lmax >= 1, "B and Lmax must be >= 1 (B=%d Lmax=%d)", B, Lmax);
+    REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq must be a positive multiple of Hkv (Hq=%d Hkv=%d)", Hq, Hkv);
+    REQUIRE(nsa_block_ok(block), "block must be 16, 32, 64 or 128 (got %d)", block);
+    REQUIRE(Lmax >= block, "Lmax must hold at least one block (Lmax=%d block=%d)", Lmax, block);
+    REQUIRE(window >= 0, "window must be >= 0 (got %d)", window);
+    REQUIRE(std::isfinite(scale), "scale must be finite");
+    REQUIRE((int64_t)B * Hkv <= 0x7fffffff, "too many (sequence, KV head) pairs");
+    REQUIRE(dtype == SA_F32 || dtype == SA_BF16 || dtype == SA_FP8_E4M3, "unknown dtype %d", dtype);
+    REQUIRE((int64_t)B * Lmax * Hkv * D <= kMaxElems, "cache too large");
+    SUPPORT(dtype == SA_BF16, "the decode branches take bf16 tensors (dtype=%d)", dtype);
+    SUPPORT(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+    SUPPORT(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+    REQUIRE(n_splits_cmp >= 1 && n_splits_cmp <= 64 && n_splits_win >= 1 && n_splits_win <= 64,
+            "n_splits_cmp and n_splits_win must be in [1, 64] (got %d, %d)", n_splits_cmp,
+            n_splits_win);
+    const size_t need = cmp_win_ws(B, Hq, Hkv, D, n_splits_cmp, n_splits_win);
+    if (need > 0) {
+      if (!workspace || ws_bytes < need)
+        return fail(SA_ERR_WORKSPACE,
+                    "sa_nsa_decode_cmp_win: workspace of %zu bytes needed for %d + %d splits "
+                    "(got %zu)", need, n_splits_cmp, n_splits_win, workspace ? ws_bytes : (size_t)0);
+      REQUIRE(aligned16(workspace), "workspace is not 16-byte aligned");
+    }
+    return hip_status(sa::launch_nsa_decode_cmp_win(q, kbar16, vbar16, kcache, vcache, lens, B,
+                                                    Lmax, Hq, Hkv, D, block, window, scale,
+                                                    out_cmp, lse_cmp, out_win, lse_win,
+                                                    n_splits_cmp, n_splits_win, workspace,
+                                                    as_stream(stream)),
+                      "sa_nsa_decode_cmp_win launch");
+  } catch (...) {
+    return fail(SA_ERR_INTERNAL, "sa_nsa_decode_cmp_win: unexpected exception");
+  }
+}
+
+size_t sa_nsa_decode_cmp_win_workspace(int B, int Hq, int Hkv, int D, int n_splits_cmp,
+                                       int n_splits_win) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) || n_splits_cmp < 1 ||
+      n_splits_cmp > 64 || n_splits_win < 1 || n_splits_win > 64)
+    return 0;
+  return cmp_win_ws(B, Hq, Hkv, D, n_splits_cmp, n_splits_win);
+}
+
 size_t sa_nsa_decode_branch_workspace(int B, int Hq, int Hkv, int D, int n_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) || n_splits < 1 ||
       n_splits > 64)

@@ -109,6 +109,15 @@ hipError_t launch_nsa_decode_range(const void* q, const void* keys, const void* 
                                    int kind, int block, int window, float scale, void* out,
                                    float* lse, int n_splits, void* workspace, hipStream_t st);
 size_t nsa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int n_splits);
+// The compressed (kind 1, over the pooled bf16 rows) and the window (kind 0) branch in one
+// launch; the workspace holds the compressed side's partials and counters, then the window
+// side's (each nsa_decode_workspace_bytes, present when that side has more than one split).
+hipError_t launch_nsa_decode_cmp_win(const void* q, const void* kbar16, const void* vbar16,
+                                     const void* kcache, const void* vcache, const int32_t* lens,
+                                     int B, int Lmax, int Hq, int Hkv, int D, int block,
+                                     int window, float scale, void* out_cmp, float* lse_cmp,
+                                     void* out_win, float* lse_win, int ns_cmp, int ns_win,
+                                     void* workspace, hipStream_t st);
 hipError_t launch_nsa_combine(const void* oc, const void* os, const void* ow, const float* gates,
                               int B, int T, int Hq, int D, void* out, hipStream_t st);
 

@@ -209,6 +209,24 @@ def test_nsa_validation(L):
     assert wsd > 0 and L.sa_nsa_decode_branch_workspace(2, 16, 1, 96, 4) == 0
     assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, 4, None, 0, None) == 3   # no workspace
     assert d(P, P, P, P, 2, 1024, 16, 1, 128, 0, 64, 512, 0.1, 1, P, None, 4, P, wsd - 1, None) == 3
+    c = L.sa_nsa_decode_cmp_win
+    cw = lambda Lmax=1024, D=128, block=64, window=512, dt=1, ns=(1, 1), ws=None, n=0, lens=P: c(
+        P, P, P, P, P, lens, 2, Lmax, 16, 1, D, block, window, 0.1, dt, P, None, P, None, ns[0],
+        ns[1], ws, n, None)
+    assert cw(block=48) == 1                                                         # block
+    assert cw(Lmax=32) == 1                                                          # no block
+    assert cw(window=-1) == 1
+    assert cw(dt=0) == 2                                                             # f32
+    assert cw(D=96) == 2
+    assert cw(lens=None) == 1
+    assert cw(ns=(0, 1)) == 1 and cw(ns=(1, 65)) == 1                                # splits
+    wcw = L.sa_nsa_decode_cmp_win_workspace(2, 16, 1, 128, 8, 4)
+    assert wcw == wsd + L.sa_nsa_decode_branch_workspace(2, 16, 1, 128, 8)
+    assert L.sa_nsa_decode_cmp_win_workspace(2, 16, 1, 128, 1, 1) == 0
+    assert L.sa_nsa_decode_cmp_win_workspace(2, 16, 1, 96, 8, 4) == 0
+    assert cw(ns=(8, 4)) == 3                                                        # no workspace
+    assert cw(ns=(8, 4), ws=P, n=wcw - 1) == 3
+    assert cw(ns=(8, 4), ws=MIS, n=wcw) == 1                                         # alignment
     mb = L.sa_block_meanpool_bf16
     assert mb(P, P, 1, 1024, 1, 128, 48, 1, P, None) == 1                              # block
     assert mb(P, P, 1, 1024, 1, 128, 64, 2, P, None) == 2                              # E4M3

@@ -225,3 +225,46 @@ def test_nsa_decode_branch_splits(D, Hq, Hkv):
             # the per-(sequence, KV head) counters after the partials are back at zero
             part = (4 * Hkv * ns * (Hq // Hkv) * (D + 4) * 4 + 255) // 256 * 256
             assert not bool(ws[part: part + 4 * Hkv * 4].any())
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,ns_c,ns_w", [(128, 16, 1, 8, 1), (128, 16, 1, 1, 1),
+                                                (64, 8, 2, 3, 5), (128, 4, 2, 64, 2)])
+def test_nsa_decode_cmp_win_equals_branches(D, Hq, Hkv, ns_c, ns_w):
+    """Both range branches in one launch equal the two separate branch calls bit for bit
+    (outputs and lse), on ragged lengths, twice on one workspace (its counters return to
+    zero), and against the oracle."""
+    import torch
+    block, W = 32, 300
+    lens_h = [1500, 999, 64, 1]
+    x = sa_synth.decode_inputs(881 + D, 4, 1500, Hq, Hkv, D, "bf16", lens=lens_h)
+    scale = D ** -0.5
+    q, kc, vc = dev(x["q"], "bf16"), dev(x["kcache"], "bf16"), dev(x["vcache"], "bf16")
+    lens = dev(np.asarray(lens_h, np.int32), "i32")
+    kb16 = sa.sa_block_meanpool_bf16(kc, lens, block)
+    vb16 = sa.sa_block_meanpool_bf16(vc, lens, block)
+    oc, lc = sa.sa_nsa_decode_branch(q, kb16, vb16, lens, 1, block, W, scale, want_lse=True,
+                                     n_splits=ns_c)
+    ow, lw = sa.sa_nsa_decode_branch(q, kc, vc, lens, 0, block, W, scale, want_lse=True,
+                                     n_splits=ns_w)
+    need = sa.sa_nsa_decode_cmp_win_workspace(4, Hq, Hkv, D, ns_c, ns_w)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    gates = np.zeros((4, Hq, 3), np.float32)
+    _, (wc, _, ww), _ = orc.nsa_decode(x["q"], x["kcache"], x["vcache"], np.asarray(lens_h),
+                                       gates, block, 1, W, scale)
+    for rep in range(2):
+        note(f"nsa decode cmp+win, splits {ns_c}/{ns_w}, D={D} Hq={Hq} Hkv={Hkv}, call {rep}")
+        c, w_, lc2, lw2 = sa.sa_nsa_decode_cmp_win(q, kb16, vb16, kc, vc, lens, block, W, scale,
+                                                   want_lse=True, n_splits_cmp=ns_c,
+                                                   n_splits_win=ns_w, workspace=ws)
+        assert torch.equal(c, oc) and torch.equal(w_, ow)
+        assert torch.equal(lc2, lc) and torch.equal(lw2, lw)
+        assert np.abs(host(c) - wc).max() < BF16_TOL
+        assert np.abs(host(w_) - ww).max() < BF16_TOL
+        # each side's per-(sequence, KV head) counters, after its partials, are back at zero
+        a256 = lambda n: (n + 255) // 256 * 256
+        base = 0
+        for ns in (ns_c, ns_w):
+            if ns > 1:
+                part = a256(4 * Hkv * ns * (Hq // Hkv) * (D + 4) * 4)
+                assert not bool(ws[base + part: base + part + 4 * Hkv * 4].any())
+                base += part + a256(4 * Hkv * 4)

@@ -28,7 +28,9 @@
 //    the pooled cache (the compressed branch); per (sequence, KV head) n_splits workgroups
 //    of 8 wavefronts, each taking a share of the range's 32-row tiles, merged by
 //    log-sum-exp in LDS; with several splits each publishes its partial with agent-scope
-//    stores and the last one (a counter) merges them.  The selected branch of decode is sa_sparse_decode with window 0.
+//    stores and the last one (a counter) merges them.  One launch can run both range
+//    branches (the compressed one's workgroups, then the window's).  The selected branch
+//    of decode is sa_sparse_decode with window 0.
 //  * nsa_combine: O = g0 * O_cmp + g1 * O_slc + g2 * O_win, 8 elements per thread.
 #include "attn_tile.h"
 #include "sa_launch.h"

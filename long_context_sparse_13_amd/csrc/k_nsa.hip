@@ -350,49 +350,54 @@ __global__ __launch_bounds__(256) void block_topk_expand(const float* __restrict
   if (take == nfull) {
     mine = lane < nfull ? lane : INT_MAX;
   } else {
-    float v[PER];
+    // order keys (-0 as +0); 0, below every float's key, marks a block that does not exist
+    // or was already chosen
+    uint32_t key[PER];
 #pragma unroll
-    for (int m = 0; m < PER; ++m) v[m] = lane + 64 * m < nfull ? row[lane + 64 * m] : -INFINITY;
+    for (int m = 0; m < PER; ++m)
+      key[m] = lane + 64 * m < nfull ? order_key(row[lane + 64 * m]) : 0u;
     for (int i = 0; i < take; ++i) {
-      float bv = -INFINITY;
+      // this lane's largest key, its lowest block among equal keys (blocks ascend with m)
+      uint32_t bk = 0u;
       int bj = INT_MAX;
 #pragma unroll
-      for (int m = 0; m < PER; ++m) {
-        const int j = lane + 64 * m;
-        if (j < nfull && (v[m] > bv || (v[m] == bv && j < bj))) {
-          bv = v[m];
-          bj = j;
+      for (int m = 0; m < PER; ++m)
+        if (key[m] > bk) {
+          bk = key[m];
+          bj = lane + 64 * m;
         }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {  // the largest score, then the lowest block
-        const float ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (ov > bv || (ov == bv && oj < bj)) {
-          bv = ov;
-          bj = oj;
-        }
-      }
-      if (lane == i) mine = bj;
-      if ((bj & 63) == lane) {  // a chosen block drops out of later rounds
+      // the largest key over the wavefront, then the lowest block holding it (DPP scans,
+      // no LDS round trips)
+      const uint32_t mk = wave_max_u32(bk);
+      const int mj = (int)wave_min_u32(bk == mk ? (uint32_t)bj : 0xffffffffu);
+      if (lane == i) mine = mj;
+      if ((mj & 63) == lane) {  // a chosen block drops out of later rounds
 #pragma unroll
         for (int m = 0; m < PER; ++m)
-          if (m == (bj >> 6)) v[m] = -INFINITY;
+          if (m == (mj >> 6)) key[m] = 0u;
       }
     }
   }
   // ascending: lane i's rank among the chosen blocks, through LDS
   int rank = 0;
-  for (int i = 0; i < take; ++i) rank += __shfl(mine, i) < mine;
+  for (int i = 0; i < take; ++i) rank += __builtin_amdgcn_readlane(mine, i) < mine;
   if (lane < take) sorted_s[wv][rank] = mine;
   wave_lds_sync();
   // interleaved: entry e * nsel + i is token e of the i-th block, so each 32-entry tile of
   // the attention takes two rows from each of 16 blocks instead of 32 consecutive rows of
   // one block (the selected branch at 64K: 3.28 -> 2.73 ms)
-  for (int p = lane; p < nsel * block; p += 64) {
-    const int i = p % nsel, e = p / nsel;
+  if ((nsel & (nsel - 1)) == 0) {  // nsel divides 64: each lane keeps one block i
+    const int sh = __builtin_ctz(nsel);
+    const int i = lane & (nsel - 1);
     const int blk = i < take ? sorted_s[wv][i] : -1;
-    out[p] = blk >= 0 ? blk * block + e : -1;
+    for (int p = lane, e = lane >> sh; p < nsel * block; p += 64, e += 64 >> sh)
+      out[p] = blk >= 0 ? blk * block + e : -1;
+  } else {
+    for (int p = lane; p < nsel * block; p += 64) {
+      const int i = p % nsel, e = p / nsel;
+      const int blk = i < take ? sorted_s[wv][i] : -1;
+      out[p] = blk >= 0 ? blk * block + e : -1;
+    }
   }
 }
 

@@ -74,7 +74,7 @@ def _check_blocks(gi, want_sel, q, kbar, block, top, rows):
 
 
 @pytest.mark.parametrize("T,Hq,Hkv,D,block,top", [(1500, 16, 1, 128, 64, 4), (1200, 4, 2, 64, 16, 16),
-                                                  (700, 8, 1, 64, 32, 64)])
+                                                  (700, 8, 1, 64, 32, 64), (900, 4, 1, 64, 16, 12)])
 def test_block_select_vs_oracle(T, Hq, Hkv, D, block, top):
     x = sa_synth.attn_inputs(811 + T, 1, T, Hq, Hkv, D, "bf16")
     note(f"block_select T={T} Hq={Hq} Hkv={Hkv} D={D} block={block} top={top}")
@@ -85,6 +85,25 @@ def test_block_select_vs_oracle(T, Hq, Hkv, D, block, top):
     want = orc.block_select_rows(x["q"], ok_, block, top, rows)
     ex = _check_blocks(idx[0], want[0], x["q"][0], ok_[0], block, top, rows)
     assert ex <= 3
+
+
+def test_block_select_exact_ties():
+    # every key row the same vector: all complete blocks score exactly alike, so each row
+    # takes its lowest `top` blocks (12 of up to 56, a count that does not divide 64)
+    T, block, top = 900, 16, 12
+    x = sa_synth.attn_inputs(831, 1, T, 4, 1, 64, "bf16")
+    x["k"][:] = x["k"][:, :1]
+    note(f"block_select exact ties T={T} block={block} top={top}")
+    kbar, _, _, _ = _pool(x, T, block)
+    got = host(sa.sa_block_select(dev(x["q"], "bf16"), kbar, block, top))[0]
+    for t in range(0, T, 7):
+        nfull = (t + 1) // block
+        take = min(top, nfull)
+        want = np.full(top * block, -1, np.int64)
+        for e in range(block):
+            for i in range(take):
+                want[e * top + i] = i * block + e
+        assert (got[t] == want).all(), t
 
 
 def test_block_select_row_range():

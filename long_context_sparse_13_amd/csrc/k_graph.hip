@@ -128,6 +128,24 @@ __global__ __launch_bounds__(64) void graph_attn(const void* __restrict__ cq,
 }
 
 
+// Exchanges inside each quad of lanes (the 4 threads of a token) with DPP moves, no LDS
+// round trip: the value of lane l ^ 1, of lane l ^ 2, and of the quad's lane k.
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_bcast(float v, int k) {  // k in 0..3, a constant
+  const int x = __float_as_int(v);
+  switch (k) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x00, 0xF, 0xF, true));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x55, 0xF, 0xF, true));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xAA, 0xF, 0xF, true));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xFF, 0xF, 0xF, true));
+  }
+}
+
 constexpr int kGTB = 64;   // tokens per block
 constexpr int kGBR = 128;  // band rows held (block + local, local <= 64)
 constexpr int kGPR = kGBR + 8;  // LDS row pitch of P (bf16), 16-byte multiple
@@ -293,8 +311,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
                    : -INFINITY;
     mx = fmaxf(mx, lf[u]);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  mx = fmaxf(mx, quad_xor1(mx));
+  mx = fmaxf(mx, quad_xor2(mx));
   float sum = 0.f;   // normaliser of the weights as used (rounded to bf16)
   float sume = 0.f;  // unrounded normaliser, for the log-sum-exp
 #pragma unroll
@@ -316,14 +334,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     sum += pfar[u];
     sume += p;
   }
-  sum += __shfl_xor(sum, 1, 64);
-  sum += __shfl_xor(sum, 2, 64);
-  sume += __shfl_xor(sume, 1, 64);
-  sume += __shfl_xor(sume, 2, 64);
+  sum += quad_xor1(sum);
+  sum += quad_xor2(sum);
+  sume += quad_xor1(sume);
+  sume += quad_xor2(sume);
   // every far weight of the token, from the 4 threads that computed them
   float pall[kGFar];
 #pragma unroll
-  for (int f = 0; f < kGFar; ++f) pall[f] = __shfl(pfar[f >> 2], (lane & ~3) | (f & 3), 64);
+  for (int f = 0; f < kGFar; ++f) pall[f] = quad_bcast(pfar[f >> 2], f & 3);
   __syncthreads();
 
   // ---- band P.V on MFMA: wavefront w takes tokens 16w .. 16w+15, all D columns; band

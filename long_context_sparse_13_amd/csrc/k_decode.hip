@@ -385,12 +385,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_attn(
     if (wv == 0) {
       const int j = lane < nsel_blocks ? blk[lane] : -1;
       const int cnt = j >= 0 ? max(0, min(block, wstart - j * block)) : 0;
-      int x = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
+      const int x = wave_incl_scan(cnt, 0, [](int a, int b2) { return a + b2; });
       if (lane < top_blocks) pre[lane] = x - cnt;
       if (lane == 63) pre[64] = x;
       if (sel_out && split == 0 && lane < top_blocks)

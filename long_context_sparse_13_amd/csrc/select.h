@@ -33,12 +33,7 @@ template <int NT>
 __device__ __forceinline__ int wg_excl_scan(int v, int* wsum) {
   constexpr int W = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v, 0, [](int a, int b) { return a + b; });
   if (lane == 63) wsum[w] = x;
   __syncthreads();
   int base = 0;

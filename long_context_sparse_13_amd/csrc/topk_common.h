@@ -182,21 +182,14 @@ __device__ inline void resolve_emit(TopkShared& sh, int n_hits, uint32_t dstar, 
     for (int r0 = 0; r0 < runs; r0 += 64) {
       const int ri = r0 + lane;
       const int g0 = ri < runs ? sh.run_gt[ri] : 0, e0 = ri < runs ? sh.run_eq[ri] : 0;
-      int gx = g0, ex = e0;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int gy = __shfl_up(gx, o, 64), ey = __shfl_up(ex, o, 64);
-        if (lane >= o) {
-          gx += gy;
-          ex += ey;
-        }
-      }
+      const int gx = wave_incl_scan(g0, 0, [](int a, int b) { return a + b; });
+      const int ex = wave_incl_scan(e0, 0, [](int a, int b) { return a + b; });
       if (ri < runs) {
         sh.run_gt[ri] = gsum + gx - g0;
         sh.run_eq[ri] = esum + ex - e0;
       }
-      gsum += __shfl(gx, 63, 64);
-      esum += __shfl(ex, 63, 64);
+      gsum += __builtin_amdgcn_readlane(gx, 63);
+      esum += __builtin_amdgcn_readlane(ex, 63);
     }
   }
   __syncthreads();

@@ -181,8 +181,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
           x[c2 * 4 + i] = v;
           mt = fmaxf(mt, v);
         }
-      mt = fmaxf(mt, shfl_xor_f(mt, 16));
-      mt = fmaxf(mt, shfl_xor_f(mt, 32));
+      mt = rows4_max(mt);
       const float m_new = fmaxf(m_run, mt);
       const float alpha = exp2_hw(m_run - m_new);
       float psum = 0.f;
@@ -214,9 +213,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
     __syncthreads();  // the tile's LDS rows are rewritten next
   }
 
-  float l = l_run;
-  l += shfl_xor_f(l, 16);
-  l += shfl_xor_f(l, 32);
+  const float l = rows4_sum(l_run);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (hv) {
     uint16_t* orow = out + (((int64_t)b * T + t) * Hq + h) * D;

@@ -90,6 +90,22 @@ __device__ __forceinline__ float sum8_dpp(float v) {
   return v;
 }
 
+// Maximum / sum of v over the lanes l, l ^ 16, l ^ 32 and l ^ 48 (the same position in the
+// four 16-lane rows), in every one of them: gfx950's row-swap permutes exchange rows inside
+// the vector unit, with no LDS round trip.  Every lane of the wavefront must be active.
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 // Inclusive scan over the 64 lanes with DPP moves (no LDS round trips): shifts by 1, 2,

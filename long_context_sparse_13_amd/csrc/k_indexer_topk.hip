@@ -29,8 +29,8 @@
 //     hold at least k entries they hold the k largest.  Rows with more than 4096 entries
 //     are selected with streaming passes over the lists instead; rows with fewer than k
 //     (thr was above the k-th score) or a list that ran out of room are listed and
-//  5. fix_rows_k recomputes them in full into a slot of their own and selects there with
-//     passes over global memory: the answer is exact in every case.
+//  5. fix_score / fix_rows_k recompute them in full into a slot of their own and select
+//     there with passes over global memory: the answer is exact in every case.
 #include "indexer_tile.h"
 #include "sa_launch.h"
 #include "sa_device.h"
@@ -596,11 +596,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
 }
 
 // ---------------------------------------------------------------- 5. listed rows
-// fix_rows_k recomputes the rows cand_topk listed: workgroup w takes listed rows w,
-// w + gridDim.x, ... and scores each in full (t + 1 scores, its wavefronts taking the
-// 256-key chunks in turn, with the same MFMA arithmetic as every other indexer kernel)
-// into its own slot of the fix area, then runs the two-step path's two-pass radix
-// selection (topk_row) over that slot.  With no listed row it returns at once.
+// The rows cand_topk listed are recomputed in full (t + 1 scores, the same MFMA
+// arithmetic as every other indexer kernel) into recompute slots of one row each, then
+// selected there with the two-step path's two-pass radix selection (topk_row).
+// fix_score scores the first nslots listed rows, one wavefront per 256-key chunk of a row,
+// spread over the whole grid; fix_rows_k then has workgroup w select listed row w from
+// slot w and, for listed rows beyond the slots (w + nslots, w + 2 nslots, ...), score each
+// in the workgroup (its wavefronts taking the chunks in turn) and select it in slot w.
+// With no listed row both return at once.
+template <int H, int DI, bool F8>
+__device__ __forceinline__ void fix_score_chunk(const uint8_t* __restrict__ qi,
+                                                const uint8_t* __restrict__ ki,
+                                                const float* __restrict__ wgt, int T, int b,
+                                                int t, int c, float* __restrict__ frow,
+                                                int lane) {
+  using IW = IdxWave<H, DI, F8>;
+  IW iw;
+  iw.load_single(qi + (int64_t)b * T * H * DI * IW::EB, t, wgt, lane & 15, lane >> 4);
+  const uint8_t* kib = ki + (int64_t)b * T * DI * IW::EB;
+  constexpr int U = kIdxChunk / 16;  // the chunk's key tiles, all in flight
+  typename IW::Keys bk[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    IW::load_keys(kib, min(c * kIdxChunk + u * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float sc = iw.score_single(bk[u]);
+    const int key = c * kIdxChunk + u * 16 + (lane & 15);
+    if (lane < 16 && key <= t) frow[key] = sc;
+  }
+}
+
+template <int H, int DI, bool F8>
+__global__ __launch_bounds__(256) void fix_score(const uint8_t* __restrict__ qi,
+                                                 const uint8_t* __restrict__ ki,
+                                                 const float* __restrict__ wgt, int T,
+                                                 int row_begin, int row_end,
+                                                 float* __restrict__ area, int64_t area_ld,
+                                                 int nslots, const uint32_t* __restrict__ n_fix,
+                                                 const int* __restrict__ fix_rows) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = row_end - row_begin;
+  const int maxch = (row_end - 1) / kIdxChunk + 1;
+  const int rows = min(__builtin_amdgcn_readfirstlane((int)*n_fix), nslots);
+  const int64_t items = (int64_t)rows * maxch;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wv; it < items; it += (int64_t)gridDim.x * 4) {
+    const int i = (int)(it / maxch), c = (int)(it % maxch);
+    const int rowi = fix_rows[i];
+    const int b = rowi / R, t = row_begin + rowi % R;
+    if (c * kIdxChunk > t) continue;
+    fix_score_chunk<H, DI, F8>(qi, ki, wgt, T, b, t, c, area + (int64_t)i * area_ld, lane);
+  }
+}
+
 template <int H, int DI, bool F8>
 __global__ __launch_bounds__(kTkThreads) void fix_rows_k(const uint8_t* __restrict__ qi,
                                                          const uint8_t* __restrict__ ki,
@@ -611,7 +660,6 @@ __global__ __launch_bounds__(kTkThreads) void fix_rows_k(const uint8_t* __restri
                                                          int32_t* __restrict__ idx,
                                                          const uint32_t* __restrict__ n_fix,
                                                          const int* __restrict__ fix_rows) {
-  using IW = IdxWave<H, DI, F8>;
   __shared__ TopkShared sh;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -621,23 +669,11 @@ __global__ __launch_bounds__(kTkThreads) void fix_rows_k(const uint8_t* __restri
   for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
     const int rowi = fix_rows[i];
     const int b = rowi / R, t = row_begin + rowi % R;
-    IW iw;
-    iw.load_single(qi + (int64_t)b * T * H * DI * IW::EB, t, wgt, lane & 15, lane >> 4);
-    const uint8_t* kib = ki + (int64_t)b * T * DI * IW::EB;
-    constexpr int U = kIdxChunk / 16;  // the chunk's key tiles, all in flight
-    for (int c = wv; c * kIdxChunk <= t; c += kTkWaves) {
-      typename IW::Keys bk[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        IW::load_keys(kib, min(c * kIdxChunk + u * 16 + (lane & 15), T - 1), lane >> 4, bk[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float sc = iw.score_single(bk[u]);
-        const int key = c * kIdxChunk + u * 16 + (lane & 15);
-        if (lane < 16 && key <= t) frow[key] = sc;
-      }
+    if (i >= (int)gridDim.x) {  // beyond the slots fix_score filled: score it here
+      for (int c = wv; c * kIdxChunk <= t; c += kTkWaves)
+        fix_score_chunk<H, DI, F8>(qi, ki, wgt, T, b, t, c, frow, lane);
+      __syncthreads();  // the row's scores are in the slot
     }
-    __syncthreads();  // the row's scores are in its slot
     topk_row(frow, t + 1, k, idx + ((int64_t)b * T + t) * k, sh);
     __syncthreads();  // the slot is free for the next row
   }
@@ -742,6 +778,10 @@ hipError_t launch_indexer_topk(const void* qi, const void* ki, const float* w, i
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL(cand_topk, g4, dim3(256), 0, st, B, T, row_begin, row_end, k, thr, cnt,
                        cand, p.nch, p.ng, idx, stat, fix);
+    if ((e2 = hipGetLastError()) != hipSuccess) return e2;
+    hipLaunchKernelGGL((fix_score<HH, DD, FF>), dim3(512), dim3(256), 0, st, (const uint8_t*)qi,
+                       (const uint8_t*)ki, w, T, row_begin, row_end, area, p.fix_ld, p.nslots,
+                       stat, fix);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
     hipLaunchKernelGGL((fix_rows_k<HH, DD, FF>), dim3((unsigned)p.nslots), dim3(kTkThreads), 0, st,
                        (const uint8_t*)qi, (const uint8_t*)ki, w, T, row_begin, row_end, k, area,

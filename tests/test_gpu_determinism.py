@@ -92,3 +92,40 @@ def test_nsa_decode_branch_splits():
     note("determinism: sa_nsa_decode_branch window, 8 splits")
     _repeat("sa_nsa_decode_branch kind 0", lambda: list(sa.sa_nsa_decode_branch(
         q, kc, vc, lens, 0, 64, 512, 128 ** -0.5, want_lse=True, n_splits=8, workspace=ws)))
+
+
+def test_nsa_decode_compressed_and_window_one_launch():
+    import torch
+    B, L = 8, 16384
+    dx = sa_synth.decode_inputs(965, B, L, 16, 1, 128, "bf16", lens=[16384, 16000, 9000, 4097,
+                                                                      16384, 700, 12345, 64])
+    q, kc, vc = dev(dx["q"], "bf16"), dev(dx["kcache"], "bf16"), dev(dx["vcache"], "bf16")
+    lens = dev(np.asarray(dx["lens"], np.int32), "i32")
+    kb16 = sa.sa_block_meanpool_bf16(kc, lens, 64)
+    vb16 = sa.sa_block_meanpool_bf16(vc, lens, 64)
+    ws = torch.zeros(sa.sa_nsa_decode_cmp_win_workspace(B, 16, 1, 128, 7, 8), dtype=torch.uint8,
+                     device="cuda")
+    note("determinism: sa_nsa_decode_cmp_win, 7 compressed and 8 window splits")
+    _repeat("sa_nsa_decode_cmp_win", lambda: list(sa.sa_nsa_decode_cmp_win(
+        q, kb16, vb16, kc, vc, lens, 64, 512, 128 ** -0.5, want_lse=True, n_splits_cmp=7,
+        n_splits_win=8, workspace=ws)))
+
+
+def test_nsa_prefill_shared_tile_kernels_and_block_select():
+    """The compressed and window branches share each K/V tile among 8 tokens through LDS;
+    the block selection ranks blocks from an LDS score tile."""
+    import torch
+    T, Hq, D, block = 4096, 16, 128, 64
+    x = sa_synth.attn_inputs(966, 1, T, Hq, 1, D, "bf16")
+    lens = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    q, k, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+    kbar, vbar = sa.sa_block_meanpool(k, lens, block), sa.sa_block_meanpool(v, lens, block)
+    scale = D ** -0.5
+    note(f"determinism: sa_cmp_attn_fwd T={T} block={block}")
+    _repeat("sa_cmp_attn_fwd", lambda: list(sa.sa_cmp_attn_fwd(q, kbar, vbar, block, scale,
+                                                                want_lse=True)))
+    note(f"determinism: window branch (sa_sparse_attn_fwd without a list) T={T} W=512")
+    _repeat("window branch", lambda: list(sa.sa_sparse_attn_fwd(q, k, v, None, 512, scale,
+                                                                 return_lse=True)))
+    note(f"determinism: sa_block_select T={T} top 16")
+    _repeat("sa_block_select", lambda: [sa.sa_block_select(q, kbar, block, 16)])

@@ -38,6 +38,7 @@
 
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 namespace sa {
 
@@ -205,6 +206,20 @@ constexpr int kGroupCap = 256;
 constexpr uint32_t kListFull = kGroupCap + 1;
 constexpr int kListLd = kGroupCap + 1 + 64 + 3;  // 324 entries
 
+// v gets, in lane r, the 16-bit count r of the packed scalar pairs c2 (one v_writelane
+// per row; the lane is an immediate)
+template <int R>
+__device__ __forceinline__ void count_to_lane(int& v, const uint32_t* c2) {
+  asm("v_writelane_b32 %0, %1, %2"
+      : "+v"(v)
+      : "s"((int)((c2[R >> 1] >> (16 * (R & 1))) & 0xffffu)), "i"(R));
+}
+template <int... R>
+__device__ __forceinline__ void counts_to_lanes(int& v, const uint32_t* c2,
+                                                std::integer_sequence<int, R...>) {
+  (count_to_lane<R>(v, c2), ...);
+}
+
 template <int H, int DI, bool F8>
 __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ qi,
                                                      const uint8_t* __restrict__ ki,
@@ -243,6 +258,10 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
   const int my_t = t0 + (lane & 31);
   const bool my_ok = lane < IW::ROWS && my_t < row_end && my_t >= k;
   const float thr_v = my_ok ? thr[(int64_t)b * R + (my_t - row_begin)] : INFINITY;
+  float thr_s[IW::ROWS];  // the same, wave-uniform: compared from scalar registers
+#pragma unroll
+  for (int rr = 0; rr < IW::ROWS; ++rr)
+    thr_s[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr_v), rr));
   const int64_t row0 = (int64_t)b * R + (t0 - row_begin);
 
   // This wavefront's rows keep one list per row for its group (chunks group, group +
@@ -271,32 +290,40 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
       wave_lds_sync();
       // ---- row by row: one lane per key of the block
       const int s = j0 + lane;
+      const int sd = s - t0;  // key s follows row rr when sd > rr (an immediate compare)
       float vals[IW::ROWS];
 #pragma unroll
       for (int rr = 0; rr < IW::ROWS; ++rr) vals[rr] = st[rr * SROW + lane];
       // the group lists of the wavefront's 32 rows as one buffer resource: a lane's store
-      // goes to byte offset 8 (rr * rstride + entry); lanes without a candidate get an
-      // offset past the range, and the hardware drops those stores, so the compaction
-      // needs no exec-mask changes or branches.  Entries past kGroupCap (a list that ran
-      // out of room) go to the list's spare entries, the write position held at
-      // kListFull.  The base is opaque per block so the compiler forms it here instead of
-      // keeping it live across blocks.
+      // goes to byte offset 8 (rr * rstride + entry), the row's part (rr * rstride plus
+      // its current length) in the store's scalar offset and the lane's place among the
+      // row's hits in the vector offset.  Lanes without a candidate get the vector offset
+      // 2^31, past the range (under 2^31 bytes) whether or not the hardware adds the
+      // scalar offset (under 2^31) before its range check, and the hardware drops those
+      // stores, so the compaction needs no exec-mask changes or branches.  Entries past
+      // kGroupCap (a list that ran out of room) go to the list's spare entries, the write
+      // position held at kListFull.  The base and the row pitch are opaque per block so
+      // the compiler forms them (and the 32 row offsets) here instead of holding them in
+      // scalar registers across blocks, which leaves room there for the 32 thresholds.
       int64_t cbo = (row0 * ng + group) * kListLd;
       asm volatile("" : "+s"(cbo));
       const uint32_t rstride8 = (uint32_t)ng * kListLd * 8u;  // bytes between rows' lists
       const __amdgpu_buffer_rsrc_t lists = __builtin_amdgcn_make_buffer_rsrc(
           cand + cbo, 0, (int)(rstride8 * IW::ROWS), 0x00020000);
+      uint32_t rs8 = rstride8;
+      asm volatile("" : "+s"(rs8));
       auto compact = [&](auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
+        uint32_t rowoff = 0u;
 #pragma unroll
         for (int rr = 0; rr < IW::ROWS; ++rr) {
-          const float th = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr_v), rr));
-          const bool hit = vals[rr] >= th && (!DIAG || s <= t0 + rr);
+          const bool hit = vals[rr] >= thr_s[rr] && (!DIAG || sd <= rr);
           const uint64_t m = ballot(hit);
           const uint32_t cnt = min((cnt2[rr >> 1] >> (16 * (rr & 1))) & 0xffffu, kListFull);
-          const uint32_t at = (uint32_t)rr * rstride8 + (cnt + (uint32_t)lanes_below(m)) * 8u;
+          const uint32_t at = (uint32_t)lanes_below(m) * 8u;
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(vals[rr]), (uint32_t)s}, lists,
-                                               hit ? at : 0xffffffffu, 0, 0);
+                                               hit ? at : 0x80000000u, (int)(rowoff + cnt * 8u), 0);
+          rowoff += rs8;
           cnt2[rr >> 1] += (uint32_t)__popcll(m) << (16 * (rr & 1));
         }
       };
@@ -305,11 +332,9 @@ __global__ __launch_bounds__(256) void indexer_cand(const uint8_t* __restrict__ 
       wave_lds_sync();
     }
     // lane rr: row rr's list length after this chunk (kListFull once past kGroupCap)
-    uint32_t cnt_v = 0u;
-#pragma unroll
-    for (int rr = 0; rr < IW::ROWS; ++rr)
-      cnt_v = lane == rr ? (cnt2[rr >> 1] >> (16 * (rr & 1))) & 0xffffu : cnt_v;
-    if (my_ok) counts[(row0 + lane) * nch + c] = (uint16_t)min(cnt_v, kListFull);
+    int cnt_v = 0;
+    counts_to_lanes(cnt_v, cnt2, std::make_integer_sequence<int, IW::ROWS>{});
+    if (my_ok) counts[(row0 + lane) * nch + c] = (uint16_t)min((uint32_t)cnt_v, kListFull);
   }
 }
 

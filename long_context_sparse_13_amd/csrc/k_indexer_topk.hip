@@ -162,21 +162,26 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
     return;
   }
   const int ns = (t >> sshift) + 1;
-  const float* __restrict__ row = samp + item * lds;
+  // the row's samples through a buffer resource over its first ns floats rounded up to a
+  // 16-byte load (within the row: lds is a multiple of 4): loads past it read zero with
+  // no per-lane condition; positions e >= ns take key 0, below every finite score's key
+  // (so below mn, and the radix skips them)
+  const __amdgpu_buffer_rsrc_t rowr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(samp + item * lds), 0, ((ns + 3) & ~3) * 4, 0x00020000);
   uint32_t key[4 * kSampleVec];
   uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int i = 0; i < kSampleVec; ++i) {
     const int e = 256 * i + 4 * lane;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (e < ns) x = *reinterpret_cast<const f32x4*>(row + e);  // (lds is a multiple of 4)
+    if (256 * i < ns)  // (uniform)
+      x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rowr, e * 4, 0, 0));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      key[4 * i + u] = order_key(x[u]);
-      if (e + u < ns) {
-        mn = min(mn, key[4 * i + u]);
-        mx = max(mx, key[4 * i + u]);
-      }
+      const uint32_t kv = e + u < ns ? order_key(x[u]) : 0u;
+      key[4 * i + u] = kv;
+      mn = min(mn, kv != 0u ? kv : 0xffffffffu);
+      mx = max(mx, kv);
     }
   }
   wave_minmax(mn, mx);
@@ -185,11 +190,14 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
   bool whole;
   wave_radix_kth(mn, mx - mn, jrank,
                  [&](auto&& f) {
+                   int nq = ns;
+                   asm volatile("" : "+s"(nq));  // a scalar compare per group, no kept masks
 #pragma unroll
                    for (int i = 0; i < kSampleVec; ++i)
+                     if (256 * i < nq) {
 #pragma unroll
-                     for (int u = 0; u < 4; ++u)
-                       if (256 * i + 4 * lane + u < ns) f(key[4 * i + u]);
+                       for (int u = 0; u < 4; ++u) f(key[4 * i + u]);
+                     }
                  },
                  hist_s[wv], lane, v, take, whole);
   // v is the jrank-th largest sample, or one below the smallest key kept whole
@@ -511,9 +519,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     wave_lds_sync();  // the marks are dead: the histogram takes their place
     wave_radix_kth(lo, mx - lo, k,
                    [&](auto&& f) {
+                     int jq = jn;
+                     asm volatile("" : "+s"(jq));  // a scalar compare per slot, no kept masks
 #pragma unroll
                      for (int j = 0; j < J; ++j)
-                       if (j < jn) f(key[j]);
+                       if (j < jq) f(key[j]);
                    },
                    hist, lane, v, take_eq, whole);
     // ---- output: per slot, the kept entries ranked by a ballot and written through a

@@ -218,10 +218,10 @@ def main():
         print(json.dumps(t))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        print("bench.py: multi-GPU runs are not part of this build (one GPU per box); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py: multi-GPU runs are not implemented (the path is sharded by design "
+              "only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -58,7 +58,7 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1, SA_FP8_E4M3 = 2 } sa_dtype;
 enum {
   SA_OK = 0,
   SA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent shapes */
-  SA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (dtype, D, ...) */
+  SA_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for (dtype, D, ...) */
   SA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace query */
   SA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
   SA_ERR_INTERNAL = 5     /* unexpected internal error */

@@ -5,7 +5,7 @@
 // tokens, a set.  The forward and backward count a listed position s of row t when
 // 0 <= s <= t - window (the window's own positions and anything outside [0, t] are
 // skipped), so a repeated s in that range would be counted twice.  Only this check runs
-// in debug mode; it synchronises the stream to hand its verdict back to the host.
+// in debug mode; it synchronises the stream to hand its result back to the host.
 #include <hip/hip_runtime.h>
 
 #include <climits>

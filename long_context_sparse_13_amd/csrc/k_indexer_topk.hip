@@ -168,20 +168,25 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
   // (so below mn, and the radix skips them)
   const __amdgpu_buffer_rsrc_t rowr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(samp + item * lds), 0, ((ns + 3) & ~3) * 4, 0x00020000);
+  // groups of 256 samples wholly past ns are skipped here and in the radix passes (their
+  // keys are never read)
+  int nq = ns;
+  asm volatile("" : "+s"(nq));  // a scalar compare per group
   uint32_t key[4 * kSampleVec];
   uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int i = 0; i < kSampleVec; ++i) {
-    const int e = 256 * i + 4 * lane;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (256 * i < ns)  // (uniform)
-      x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rowr, e * 4, 0, 0));
+    if (256 * i < nq) {
+      const int e = 256 * i + 4 * lane;
+      const f32x4 x =
+          __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rowr, e * 4, 0, 0));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t kv = e + u < ns ? order_key(x[u]) : 0u;
-      key[4 * i + u] = kv;
-      mn = min(mn, kv != 0u ? kv : 0xffffffffu);
-      mx = max(mx, kv);
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t kv = e + u < ns ? order_key(x[u]) : 0u;
+        key[4 * i + u] = kv;
+        mn = min(mn, kv != 0u ? kv : 0xffffffffu);
+        mx = max(mx, kv);
+      }
     }
   }
   wave_minmax(mn, mx);
@@ -190,11 +195,11 @@ __global__ __launch_bounds__(256) void sample_threshold(const float* __restrict_
   bool whole;
   wave_radix_kth(mn, mx - mn, jrank,
                  [&](auto&& f) {
-                   int nq = ns;
-                   asm volatile("" : "+s"(nq));  // a scalar compare per group, no kept masks
+                   int nq2 = ns;
+                   asm volatile("" : "+s"(nq2));  // a scalar compare per group, no kept masks
 #pragma unroll
                    for (int i = 0; i < kSampleVec; ++i)
-                     if (256 * i < nq) {
+                     if (256 * i < nq2) {
 #pragma unroll
                        for (int u = 0; u < 4; ++u) f(key[4 * i + u]);
                      }

@@ -120,16 +120,11 @@ struct GroupAttn {
     }
   }
 
-  // Online-softmax update with one loaded tile (no-op for an empty mask).  `vl` is this
-  // wave's LDS staging area of LDS_BYTES.
-  __device__ __forceinline__ void compute(const Tile& tl, unsigned char* vl, float scale_log2,
-                                          int lane) {
-    const uint32_t vm = tl.vm;
-    if (vm == 0u) return;
-    const int n = lane & 15, grp = lane >> 4;
-
+  // First half of a tile's update: the scores S^T (returned) and the V rows staged in LDS.
+  // After it the tile's registers are free for the next tile's loads.
+  __device__ __forceinline__ void scores_and_stage(const Tile& tl, unsigned char* vl,
+                                                   f32x4 (&s)[2], int lane) {
     // ---- S^T = K . Q^T for the two 16-key halves
-    f32x4 s[2];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       s[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -146,6 +141,14 @@ struct GroupAttn {
       const int c = lane % CH;
       st16(vl + r * LROW + c * 16, tl.vw[i]);
     }
+  }
+
+  // Second half: online-softmax update with the scores s of a tile with slot mask vm
+  // (not 0) and O^T += V^T P^T from the staged rows.  `vl` is this wave's LDS staging area
+  // of LDS_BYTES.
+  __device__ __forceinline__ void update(const f32x4 (&s)[2], uint32_t vm, unsigned char* vl,
+                                         float scale_log2, int lane) {
+    const int n = lane & 15, grp = lane >> 4;
 
     // ---- online softmax (log2 domain); head n's max over the 4 lane groups
     float x[8];
@@ -196,8 +199,11 @@ struct GroupAttn {
     wave_lds_sync();  // the staging area may be overwritten by the next tile
   }
 
-  // Streams `ntiles` tiles, one loaded and computed at a time (fewer registers, so more
-  // wavefronts per SIMD, which beats a deeper pipeline in each wavefront); empty tiles are
+  // Streams `ntiles` tiles with one tile's registers (fewer registers, so more wavefronts
+  // per SIMD, which beats two tiles of registers in each wavefront): once a tile's K rows
+  // have fed the score MFMAs and its V rows are staged in LDS, the next non-empty tile's
+  // rows are requested into the same registers, so they are in flight during this tile's
+  // softmax and P.V (5.10 -> 5.02 ms on the 64K workload, same bits); empty tiles are
   // skipped.  fetch(i) returns this lane's raw key of tile i (it may issue a load, which
   // is started one tile ahead); finish(i, raw, key, vm) turns it into the slot key and
   // the tile's slot mask.
@@ -210,13 +216,30 @@ struct GroupAttn {
     Tile A;
     int key;
     uint32_t vm;
+    int i = 0;
     int r = fetch(0);
-    for (int i = 0; i < ntiles; ++i) {
-      finish(i, r, key, vm);
-      if (i + 1 < ntiles) r = fetch(i + 1);  // the next raw key is in flight meanwhile
-      if (vm == 0u) continue;
-      load(A, kbase, vbase, stride, key, vm, lane);
-      compute(A, vl, scale_log2, lane);
+    // load the next non-empty tile into A; false when none is left
+    auto advance = [&]() -> bool {
+      while (i < ntiles) {
+        finish(i, r, key, vm);
+        ++i;
+        if (i < ntiles) r = fetch(i);  // the next raw key is in flight meanwhile
+        if (vm != 0u) {
+          load(A, kbase, vbase, stride, key, vm, lane);
+          return true;
+        }
+      }
+      return false;
+    };
+    bool have = advance();
+    while (have) {
+      const uint32_t cur_vm = A.vm;
+      f32x4 s[2];
+      scores_and_stage(A, vl, s, lane);
+      // A's registers are consumed: the next tile's rows are requested now and arrive
+      // while this tile's softmax and P.V run
+      have = advance();
+      update(s, cur_vm, vl, scale_log2, lane);
     }
   }
 

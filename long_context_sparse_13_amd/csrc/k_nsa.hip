@@ -235,30 +235,42 @@ constexpr int kBsDim = 128;    // feature slice staged at a time
 constexpr int kBsPad = kBsDim + 4;
 
 // qs[b, r, g*D + d] = sum over the query heads h of KV group g of q[b, t, h, d] (float32,
-// heads in increasing order), t = row_begin + r; 4 features per thread.
-template <bool BF>
+// heads in increasing order), t = row_begin + r; W (4 or 8, dividing D) features per
+// thread, read 16 bytes at a time when W = 8 and the input is bf16.
+template <bool BF, int W>
 __global__ __launch_bounds__(256) void head_sum(const void* __restrict__ q, int T, int Hq,
                                                 int Hkv, int D, int row_begin, int row_end,
                                                 int B, float* __restrict__ qs) {
   const int E = Hkv * D, G = Hq / Hkv, R = row_end - row_begin;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 features each
-  if (i * 4 >= (int64_t)B * R * E) return;
-  const int64_t f = i * 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // W features each
+  if (i * W >= (int64_t)B * R * E) return;
+  const int64_t f = i * W;
   const int64_t br = f / E;
   const int e = (int)(f % E);
   const int b = (int)(br / R), r = (int)(br % R);
   const int g = e / D, d = e % D;
   const int64_t base = (((int64_t)b * T + row_begin + r) * Hq + g * G) * D + d;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  f32x4 s[W / 4];
+#pragma unroll
+  for (int u = 0; u < W / 4; ++u) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int hh = 0; hh < G; ++hh) {
-    if constexpr (BF) {
+    if constexpr (BF && W == 8) {
+      const u32x4 w = ld16(reinterpret_cast<const uint16_t*>(q) + base + (int64_t)hh * D);
+      s[0] += f32x4{bf16_to_f32((uint16_t)w[0]), bf16_hi(w[0]), bf16_to_f32((uint16_t)w[1]), bf16_hi(w[1])};
+      s[1] += f32x4{bf16_to_f32((uint16_t)w[2]), bf16_hi(w[2]), bf16_to_f32((uint16_t)w[3]), bf16_hi(w[3])};
+    } else if constexpr (BF) {
       const u32x2 w = ld8(reinterpret_cast<const uint16_t*>(q) + base + (int64_t)hh * D);
-      s += f32x4{bf16_to_f32((uint16_t)w[0]), bf16_hi(w[0]), bf16_to_f32((uint16_t)w[1]), bf16_hi(w[1])};
+      s[0] += f32x4{bf16_to_f32((uint16_t)w[0]), bf16_hi(w[0]), bf16_to_f32((uint16_t)w[1]), bf16_hi(w[1])};
     } else {
-      s += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + base + (int64_t)hh * D);
+#pragma unroll
+      for (int u = 0; u < W / 4; ++u)
+        s[u] += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + base +
+                                                (int64_t)hh * D + 4 * u);
     }
   }
-  *reinterpret_cast<f32x4*>(qs + f) = s;
+#pragma unroll
+  for (int u = 0; u < W / 4; ++u) *reinterpret_cast<f32x4*>(qs + f + 4 * u) = s[u];
 }
 
 // sc[b, r, j] = qs[b, r, :] . kbar[b, j, :] (float32) for rows t = row_begin + r and
@@ -732,13 +744,20 @@ hipError_t launch_block_select(const void* q, const float* kbar, int B, int T, i
                                        ((size_t)rows * ld * sizeof(float) + 255) / 256 * 256);
   hipError_t e;
   if (nb > 0) {
-    const unsigned g0 = (unsigned)((rows * E / 4 + 255) / 256);
-    if (bf16)
-      hipLaunchKernelGGL(head_sum<true>, dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D, row_begin,
-                         row_end, B, qs);
+    const bool w8 = D % 8 == 0;  // 8 features per thread (else 4: D is a multiple of 4)
+    const unsigned g0 = (unsigned)((rows * E / (w8 ? 8 : 4) + 255) / 256);
+    if (bf16 && w8)
+      hipLaunchKernelGGL((head_sum<true, 8>), dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D,
+                         row_begin, row_end, B, qs);
+    else if (bf16)
+      hipLaunchKernelGGL((head_sum<true, 4>), dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D,
+                         row_begin, row_end, B, qs);
+    else if (w8)
+      hipLaunchKernelGGL((head_sum<false, 8>), dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D,
+                         row_begin, row_end, B, qs);
     else
-      hipLaunchKernelGGL(head_sum<false>, dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D, row_begin,
-                         row_end, B, qs);
+      hipLaunchKernelGGL((head_sum<false, 4>), dim3(g0), dim3(256), 0, st, q, T, Hq, Hkv, D,
+                         row_begin, row_end, B, qs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 g1((unsigned)((R + kBsRows - 1) / kBsRows), (unsigned)((nb + kBsBlks - 1) / kBsBlks),
                   (unsigned)B);

@@ -13,8 +13,10 @@
 //    registers).  The kernel is bound by how many gathered rows the memory pipeline keeps
 //    in flight against the L2 / Infinity Cache latency (with every gathered row an L2 hit
 //    it runs ~15 % faster; halving its VALU instructions, or cutting the K loads'
-//    addresser work by staging them through LDS, gains nothing), so more resident
-//    wavefronts beat a deeper per-wavefront pipeline, and OFS32 (one KV head's rows of a
+//    addresser work by staging them through LDS or loading them quad-contiguous and
+//    permuting lanes, gains nothing), so more resident wavefronts beat a second tile of
+//    registers per wavefront; within one tile's registers the next tile's rows are
+//    requested as soon as the current tile's K and V have been consumed, and OFS32 (one KV head's rows of a
 //    batch within 4 GB) addresses rows as a uniform base plus a 32-bit offset.  Items are
 //    taken in ranges of about 8,192, last rows first, each range dealt to the XCDs in
 //    contiguous pieces (xcd_item_phased): fewer bytes past L2 and ~12 % less time than one
